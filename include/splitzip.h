@@ -1,0 +1,170 @@
+/*
+ * splitzip.h -- C ABI of the MI355X (gfx950) SplitZip lossless BF16 codec.
+ *
+ * The method (page "splitzip_codec.py -- SplitZip codec adapter for
+ * diffusers-dynamic-offloader", module docstring "Method"): view every BF16
+ * value as 16 bits; keep its sign and 7 low mantissa bits as one byte (sm);
+ * code its 8-bit exponent through a per-tensor table of the 16 most frequent
+ * exponents as a 4-bit code, two codes per byte (pk); send every exponent
+ * outside that table to a sparse escape stream of (int32 chunk id, uint16
+ * position inside a 1024-element chunk, uint8 raw exponent).  Decoding is
+ * bit-exact.
+ *
+ * Wire format (same page, "Payload layout" and function assemble_payload;
+ * page "SplitZip in DDO -- VMM routes", "Invariants common to both routes"
+ * item 1), with A(v) = v rounded up to a multiple of 4, P = ceil(n/2),
+ * e = number of escapes:
+ *   pk        uint8[P]           at off[0] = 0             (even element = high nibble)
+ *   sm        uint8[n]           at off[1] = A(P)
+ *   chunk_id  int32 LE [e]       at off[2] = A(off[1] + n)
+ *   local_pos uint16 LE [e]      at off[3] = off[2] + 4e
+ *   esc_val   uint8[e]           at off[4] = A(off[3] + 2e)
+ *   total size                   comp_bytes = off[4] + e
+ * Padding bytes are zero.  Escapes are in ascending element order.
+ *
+ * Conventions for every entry point:
+ *   - All device work is enqueued asynchronously on `stream` (a hipStream_t,
+ *     NULL = the default stream); no entry point synchronises, allocates or
+ *     frees memory.  Every buffer is owned by the caller.
+ *   - The return value reports argument errors and launch failures only
+ *     (SPLITZIP_OK or an error code, nothing is enqueued on error).  Errors
+ *     found by the device (capacity overflow, corrupt escape stream) are
+ *     written to the status field / word named by the function.
+ *   - Device pointers ("d_") may also be pinned host memory mapped into the
+ *     device address space.
+ *   - Tensor and payload buffers must be 16-byte aligned.
+ *   - n is limited to SPLITZIP_MAX_N elements.
+ */
+#ifndef SPLITZIP_H
+#define SPLITZIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPLITZIP_ABI_VERSION 1
+#define SPLITZIP_CHUNK 1024u
+#define SPLITZIP_MAX_N (1ull << 36)
+
+enum splitzip_status {
+    SPLITZIP_OK = 0,
+    SPLITZIP_ERR_INVALID = 1,   /* null/misaligned pointer, n out of range, bad size */
+    SPLITZIP_ERR_CAPACITY = 2,  /* payload buffer smaller than the payload */
+    SPLITZIP_ERR_CORRUPT = 3,   /* inconsistent payload / metadata */
+    SPLITZIP_ERR_HIP = 4,       /* a HIP runtime call or launch failed */
+    SPLITZIP_ERR_WORKSPACE = 5, /* workspace too small for n */
+    SPLITZIP_ERR_INTERNAL = 6   /* device-side progress guard tripped (must not happen) */
+};
+
+/* Per-tensor codebook (page 1, SplitZipCodebook and calibrate_codebook).
+ * Code c (0..n_codes-1) is the c-th most frequent exponent; equal counts are
+ * ordered by exponent value ascending.  Unused dec_lut slots are 0. */
+typedef struct splitzip_codebook {
+    uint8_t enc_lut[256];        /* exponent -> code, 0 when it has none      */
+    uint8_t enc_lut_marked[256]; /* exponent -> code, 16 when it escapes      */
+    uint8_t dec_lut[16];         /* code -> exponent                          */
+    uint8_t common_lut[256];     /* 1 when the exponent has a code            */
+    uint32_t n_codes;            /* min(16, number of distinct exponents)     */
+    uint32_t reserved;
+    uint64_t covered;            /* elements whose exponent has a code        */
+    uint64_t total;              /* n; coverage = covered / total (1 if n=0)  */
+    uint64_t counts[256];        /* exponent histogram                        */
+} splitzip_codebook;
+
+/* Payload metadata (page 1, PayloadMeta); written by splitzip_encode. */
+typedef struct splitzip_meta {
+    uint64_t n;          /* elements                                          */
+    uint64_t n_pairs;    /* ceil(n/2) = bytes of pk                           */
+    uint64_t chunk_size; /* 1024                                              */
+    uint64_t n_esc;      /* escapes                                           */
+    uint64_t comp_bytes; /* payload size; when status is CAPACITY, the size
+                            that would have been needed                       */
+    uint64_t offsets[5]; /* pk, sm, chunk_id, local_pos, esc_val              */
+    uint64_t covered;    /* copied from the codebook used                     */
+    uint64_t total;
+    int32_t status;      /* SPLITZIP_OK or SPLITZIP_ERR_CAPACITY / _INTERNAL  */
+    uint32_t reserved;
+} splitzip_meta;
+
+/* ABI version of the loaded library (SPLITZIP_ABI_VERSION). */
+int splitzip_abi_version(void);
+
+/* sizeof(splitzip_codebook) and sizeof(splitzip_meta) as compiled into the
+ * library, for bindings that mirror the structs. */
+void splitzip_struct_sizes(size_t *codebook_bytes, size_t *meta_bytes);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *splitzip_status_string(int status);
+
+/* Exact payload size for n elements with n_esc escapes (host function; the
+ * layout rule above).  splitzip_payload_size(n, n) bounds every payload. */
+uint64_t splitzip_payload_size(uint64_t n, uint64_t n_esc);
+
+/* Bytes of device workspace needed by calibrate and encode for tensors of up
+ * to n elements (host function).  A workspace of S bytes serves every n with
+ * splitzip_workspace_size(n) <= S. */
+size_t splitzip_workspace_size(uint64_t n);
+
+/* Prepare a workspace for first use (enqueues a zero-fill kernel).  The
+ * library keeps it consistent afterwards; one workspace must not be used by
+ * two calls that can run at the same time.
+ * Errors: INVALID (null or unaligned d_ws, ws_bytes below the minimum), HIP. */
+int splitzip_workspace_init(void *d_ws, size_t ws_bytes, void *stream);
+
+/* Calibrate the top-16 exponent codebook of one tensor (page 1,
+ * calibrate_codebook): 256-bin exponent histogram, then the 16 most frequent
+ * exponents (count descending, exponent ascending on ties) receive codes
+ * 0..15.
+ *   d_x   n BF16 values as uint16 bit patterns (16-byte aligned, device)
+ *   d_cb  output codebook (device)
+ *   d_ws  initialised workspace of ws_bytes >= splitzip_workspace_size(n)
+ * Errors: INVALID, WORKSPACE, HIP. */
+int splitzip_calibrate(const uint16_t *d_x, uint64_t n, splitzip_codebook *d_cb, void *d_ws,
+                       size_t ws_bytes, void *stream);
+
+/* Encode one tensor with a codebook (page 1, encode_torch and
+ * assemble_payload).  The codebook may come from another tensor: every
+ * exponent without a code becomes an escape.
+ *   d_payload  output buffer of `capacity` bytes (16-byte aligned, device);
+ *              bytes [0, comp_bytes) receive the payload, bytes beyond are
+ *              not touched.
+ *   d_meta     output metadata (device); meta->status = SPLITZIP_ERR_CAPACITY
+ *              when capacity < comp_bytes (then only the dense sections and
+ *              the escapes that fit are written, and comp_bytes holds the
+ *              size needed).
+ * Synchronous errors: INVALID, CAPACITY (capacity below
+ * splitzip_payload_size(n, 0)), WORKSPACE, HIP. */
+int splitzip_encode(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_cb,
+                    uint8_t *d_payload, uint64_t capacity, splitzip_meta *d_meta, void *d_ws,
+                    size_t ws_bytes, void *stream);
+
+/* Decode a payload back to BF16 bit patterns (page 1, decode_torch): dense
+ * 16-entry table lookup plus the escape patch.
+ *   d_payload  payload laid out as d_meta describes (device, 16-byte aligned),
+ *              payload_bytes readable bytes
+ *   d_meta     metadata of the payload (device); meta->n must equal n, the
+ *              offsets must follow the layout rule for (n, meta->n_esc) and
+ *              comp_bytes must not exceed payload_bytes, else nothing is
+ *              decoded and status bit 1 is set
+ *   d_dec_lut  the codebook's 16-entry dec_lut (device)
+ *   d_out      n uint16 outputs (device, 16-byte aligned, must not overlap
+ *              the payload)
+ *   d_status   optional (may be NULL) device int32 that the caller has set to
+ *              0; decode ORs in 1 for inconsistent metadata (see d_meta),
+ *              2 when an escape points outside the tensor,
+ *              4 when a chunk-local position is >= 1024, 8 when escapes are
+ *              not strictly increasing.  Decode never writes outside
+ *              d_out[0..n).
+ * Synchronous errors: INVALID, HIP. */
+int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const splitzip_meta *d_meta,
+                    const uint8_t *d_dec_lut, uint16_t *d_out, uint64_t n, int32_t *d_status,
+                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLITZIP_H */

@@ -1,0 +1,153 @@
+"""ctypes binding of the C ABI in include/splitzip.h.
+
+Argument marshalling only: every step of calibrate / encode / decode runs in
+the HIP kernels of ``_lib/libsplitzip.so``.  The library must have been built
+(``python -m lossless_bf16_tensor_splitzip_amd._build`` or
+``__graft_entry__.build()``); there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from ._build import LIB_PATH
+
+CHUNK = 1024
+MAX_N = 1 << 36
+
+OK = 0
+ERR_INVALID = 1
+ERR_CAPACITY = 2
+ERR_CORRUPT = 3
+ERR_HIP = 4
+ERR_WORKSPACE = 5
+ERR_INTERNAL = 6
+
+# decode status bits
+DEC_BAD_META = 1
+DEC_ESC_OUT_OF_RANGE = 2
+DEC_POS_GE_CHUNK = 4
+DEC_NOT_INCREASING = 8
+
+
+class Codebook(ctypes.Structure):
+    """Mirror of splitzip_codebook."""
+    _fields_ = [
+        ("enc_lut", ctypes.c_uint8 * 256),
+        ("enc_lut_marked", ctypes.c_uint8 * 256),
+        ("dec_lut", ctypes.c_uint8 * 16),
+        ("common_lut", ctypes.c_uint8 * 256),
+        ("n_codes", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+        ("covered", ctypes.c_uint64),
+        ("total", ctypes.c_uint64),
+        ("counts", ctypes.c_uint64 * 256),
+    ]
+
+
+class Meta(ctypes.Structure):
+    """Mirror of splitzip_meta."""
+    _fields_ = [
+        ("n", ctypes.c_uint64),
+        ("n_pairs", ctypes.c_uint64),
+        ("chunk_size", ctypes.c_uint64),
+        ("n_esc", ctypes.c_uint64),
+        ("comp_bytes", ctypes.c_uint64),
+        ("offsets", ctypes.c_uint64 * 5),
+        ("covered", ctypes.c_uint64),
+        ("total", ctypes.c_uint64),
+        ("status", ctypes.c_int32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
+DEC_LUT_OFFSET = Codebook.dec_lut.offset
+
+# name -> (restype, argtypes), exactly the functions of include/splitzip.h
+_P = ctypes.c_void_p
+_U64 = ctypes.c_uint64
+_SZ = ctypes.c_size_t
+SIGNATURES = {
+    "splitzip_abi_version": (ctypes.c_int, []),
+    "splitzip_struct_sizes": (None, [ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
+    "splitzip_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "splitzip_payload_size": (_U64, [_U64, _U64]),
+    "splitzip_workspace_size": (_SZ, [_U64]),
+    "splitzip_workspace_init": (ctypes.c_int, [_P, _SZ, _P]),
+    "splitzip_calibrate": (ctypes.c_int, [_P, _U64, _P, _P, _SZ, _P]),
+    "splitzip_encode": (ctypes.c_int, [_P, _U64, _P, _P, _U64, _P, _P, _SZ, _P]),
+    "splitzip_decode": (ctypes.c_int, [_P, _U64, _P, _P, _P, _U64, _P, _P]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "SplitZip HIP library not built (%s missing): run "
+            "`python -m lossless_bf16_tensor_splitzip_amd._build`" % LIB_PATH)
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    cb_size, meta_size = ctypes.c_size_t(), ctypes.c_size_t()
+    handle.splitzip_struct_sizes(ctypes.byref(cb_size), ctypes.byref(meta_size))
+    if cb_size.value != ctypes.sizeof(Codebook) or meta_size.value != ctypes.sizeof(Meta):
+        raise RuntimeError("struct layout mismatch between the library and the binding")
+    _lib = handle
+    return handle
+
+
+class SplitZipError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (fn, status_string(status), status))
+
+
+def status_string(status: int) -> str:
+    return lib().splitzip_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> int:
+    if status != OK:
+        raise SplitZipError(fn, status)
+    return status
+
+
+# Thin wrappers with the C names (raw pointers / ints in, status out).
+
+def splitzip_abi_version() -> int:
+    return lib().splitzip_abi_version()
+
+
+def splitzip_payload_size(n: int, n_esc: int) -> int:
+    return lib().splitzip_payload_size(n, n_esc)
+
+
+def splitzip_workspace_size(n: int) -> int:
+    return lib().splitzip_workspace_size(n)
+
+
+def splitzip_workspace_init(d_ws: int, ws_bytes: int, stream: int) -> int:
+    return lib().splitzip_workspace_init(d_ws, ws_bytes, stream)
+
+
+def splitzip_calibrate(d_x: int, n: int, d_cb: int, d_ws: int, ws_bytes: int, stream: int) -> int:
+    return lib().splitzip_calibrate(d_x, n, d_cb, d_ws, ws_bytes, stream)
+
+
+def splitzip_encode(d_x: int, n: int, d_cb: int, d_payload: int, capacity: int, d_meta: int,
+                    d_ws: int, ws_bytes: int, stream: int) -> int:
+    return lib().splitzip_encode(d_x, n, d_cb, d_payload, capacity, d_meta, d_ws, ws_bytes, stream)
+
+
+def splitzip_decode(d_payload: int, payload_bytes: int, d_meta: int, d_dec_lut: int, d_out: int,
+                    n: int, d_status: int, stream: int) -> int:
+    return lib().splitzip_decode(d_payload, payload_bytes, d_meta, d_dec_lut, d_out, n, d_status,
+                                 stream)

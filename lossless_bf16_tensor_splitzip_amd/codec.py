@@ -1,0 +1,122 @@
+"""Tensor-level calls of the SplitZip codec: marshalling of torch tensors
+(device memory and streams only) into the C ABI.  No codec arithmetic is done
+here; calibrate, encode and decode run entirely in the HIP kernels."""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _abi
+from ._abi import CHUNK, Codebook, Meta, SplitZipError
+
+CODEBOOK_BYTES = ctypes.sizeof(Codebook)
+META_BYTES = ctypes.sizeof(Meta)
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def _bits(x: torch.Tensor) -> torch.Tensor:
+    if x.dtype is not torch.bfloat16:
+        # page 2: only BF16 is encoded (other formats, e.g. FP8, would expand)
+        raise ValueError("SplitZip expects a bfloat16 tensor, got %s" % x.dtype)
+    if not x.is_cuda:
+        raise ValueError("SplitZip runs on the GPU: move the tensor to a HIP device")
+    if not x.is_contiguous():
+        raise ValueError("SplitZip expects a contiguous tensor")
+    return x.reshape(-1).view(torch.int16)
+
+
+def payload_size(n: int, n_esc: int) -> int:
+    return _abi.splitzip_payload_size(n, n_esc)
+
+
+class Workspace:
+    """Device scratch for calibrate / encode, sized for tensors of up to n_max
+    elements.  One workspace per stream that runs codec calls concurrently."""
+
+    def __init__(self, n_max: int, device=None, stream=None):
+        device = torch.device(device if device is not None else "cuda")
+        self.n_max = n_max
+        self.nbytes = _abi.splitzip_workspace_size(n_max)
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        _abi._check("splitzip_workspace_init",
+                    _abi.splitzip_workspace_init(self.buf.data_ptr(), self.nbytes,
+                                                 _stream(stream, device)))
+
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+
+def new_codebook(device) -> torch.Tensor:
+    return torch.empty(CODEBOOK_BYTES, dtype=torch.uint8, device=device)
+
+
+def new_meta(device) -> torch.Tensor:
+    return torch.empty(META_BYTES, dtype=torch.uint8, device=device)
+
+
+def calibrate(x: torch.Tensor, ws: Workspace, cb: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """Per-tensor top-16 exponent codebook (device bytes of splitzip_codebook)."""
+    xb = _bits(x)
+    if cb is None:
+        cb = new_codebook(x.device)
+    _abi._check("splitzip_calibrate",
+                _abi.splitzip_calibrate(xb.data_ptr(), xb.numel(), cb.data_ptr(), ws.ptr(),
+                                        ws.nbytes, _stream(stream, x.device)))
+    return cb
+
+
+def encode(x: torch.Tensor, cb: torch.Tensor, ws: Workspace, payload: torch.Tensor | None = None,
+           meta: torch.Tensor | None = None, stream=None):
+    """Encode into ``payload`` (allocated for the worst case when None).
+    Returns (payload, meta) as device uint8 tensors; the payload occupies the
+    first meta.comp_bytes bytes."""
+    xb = _bits(x)
+    n = xb.numel()
+    if payload is None:
+        payload = torch.empty(max(payload_size(n, n), 16), dtype=torch.uint8, device=x.device)
+    if meta is None:
+        meta = new_meta(x.device)
+    _abi._check("splitzip_encode",
+                _abi.splitzip_encode(xb.data_ptr(), n, cb.data_ptr(), payload.data_ptr(),
+                                     payload.numel(), meta.data_ptr(), ws.ptr(), ws.nbytes,
+                                     _stream(stream, x.device)))
+    return payload, meta
+
+
+def decode(payload: torch.Tensor, meta: torch.Tensor, cb_or_dec_lut: torch.Tensor, n: int,
+           out: torch.Tensor | None = None, status: torch.Tensor | None = None,
+           stream=None) -> torch.Tensor:
+    """Decode to a flat bfloat16 tensor of n elements (``out`` when given).
+    ``cb_or_dec_lut`` is a device codebook or a 16-byte dec_lut tensor."""
+    dev = payload.device
+    if out is None:
+        out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    if out.dtype is not torch.bfloat16 or not out.is_contiguous() or out.numel() != n:
+        raise ValueError("out must be a contiguous bfloat16 tensor of n elements")
+    lut_ptr = cb_or_dec_lut.data_ptr()
+    if cb_or_dec_lut.numel() == CODEBOOK_BYTES:
+        lut_ptr += _abi.DEC_LUT_OFFSET
+    elif cb_or_dec_lut.numel() != 16:
+        raise ValueError("expected a codebook or a 16-entry dec_lut")
+    st_ptr = 0 if status is None else status.data_ptr()
+    _abi._check("splitzip_decode",
+                _abi.splitzip_decode(payload.data_ptr(), payload.numel(), meta.data_ptr(),
+                                     lut_ptr, out.data_ptr(), n, st_ptr, _stream(stream, dev)))
+    return out
+
+
+def read_codebook(cb: torch.Tensor) -> Codebook:
+    host = cb.detach().to("cpu").numpy().tobytes()
+    return Codebook.from_buffer_copy(host)
+
+
+def read_meta(meta: torch.Tensor) -> Meta:
+    host = meta.detach().to("cpu").numpy().tobytes()
+    return Meta.from_buffer_copy(host)

@@ -1,0 +1,81 @@
+"""The C-ABI library loads on a machine without a GPU, exports every function
+include/splitzip.h declares, agrees with the binding's struct mirrors, and its
+host-side functions (layout size, workspace size, argument checks) behave.
+No device work is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lossless_bf16_tensor_splitzip_amd as S
+from lossless_bf16_tensor_splitzip_amd import _abi
+import oracle_pins as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "splitzip.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(splitzip_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = S.lib()
+    names = declared_functions()
+    assert len(names) == 9, names
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in _abi.SIGNATURES, name
+    assert set(_abi.SIGNATURES) == set(names)
+
+
+def test_struct_layout_matches_header():
+    cb, meta = ctypes.c_size_t(), ctypes.c_size_t()
+    S.lib().splitzip_struct_sizes(ctypes.byref(cb), ctypes.byref(meta))
+    assert cb.value == ctypes.sizeof(_abi.Codebook) == 2856
+    assert meta.value == ctypes.sizeof(_abi.Meta) == 104
+    assert _abi.Codebook.dec_lut.offset == 512
+    assert _abi.Meta.status.offset == 96
+    assert S.lib().splitzip_abi_version() == 1
+
+
+def test_payload_size_matches_golden_layout():
+    path = os.path.join(P.GOLDEN, "layout_sizes.txt")
+    rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    for row in rows:
+        n, e, total = int(row[0]), int(row[1]), int(row[7])
+        assert S.payload_size(n, e) == total
+
+
+def test_workspace_size_monotonic():
+    prev = 0
+    for n in [0, 1, 4095, 4096, 4097, 1 << 20, 33554432, 37748736]:
+        w = _abi.splitzip_workspace_size(n)
+        assert w >= prev
+        prev = w
+        # staging for every element escaping: 3 bytes per element
+        assert w >= 3 * n
+
+
+def test_argument_errors_need_no_device():
+    assert _abi.splitzip_workspace_init(0, 1 << 20, 0) == _abi.ERR_INVALID
+    assert _abi.splitzip_calibrate(0, 5, 0, 0, 0, 0) == _abi.ERR_INVALID
+    assert _abi.splitzip_encode(0, 5, 0, 0, 0, 0, 0, 0, 0) == _abi.ERR_INVALID
+    assert _abi.splitzip_decode(0, 0, 0, 0, 0, 5, 0, 0) == _abi.ERR_INVALID
+    # misaligned tensor pointer
+    assert _abi.splitzip_calibrate(0x1002, 5, 0x2000, 0x3000, 1 << 20, 0) == _abi.ERR_INVALID
+    # n above the limit
+    assert _abi.splitzip_calibrate(0x1000, _abi.MAX_N + 1, 0x2000, 0x3000, 1 << 20, 0) == \
+        _abi.ERR_INVALID
+    for code in range(7):
+        assert _abi.status_string(code)
+    assert _abi.status_string(99) == "unknown status"
+
+
+def test_binding_rejects_non_bf16():
+    import torch
+    with pytest.raises(ValueError):
+        S.codec._bits(torch.zeros(4, dtype=torch.float16))

@@ -1,0 +1,353 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI.
+
+Integer work, tolerance 0: codebook bytes, metadata, payload bytes
+[0, comp_bytes) and decoded bit patterns must equal the oracle's exactly, and
+each side must decode the other's payload.  Small cases span several tiles and
+ragged tails; the large cases are the workloads at full size, in the same
+launch configuration the benchmark times.
+"""
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import lossless_bf16_tensor_splitzip_amd as S
+from lossless_bf16_tensor_splitzip_amd import _abi
+import oracle
+import oracle_pins as P
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    S.lib()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+_WS = {}
+
+
+def workspace(n):
+    """One workspace per size class, reused across tests (as a caller would)."""
+    key = max(n, 1 << 20).bit_length()
+    if key not in _WS:
+        _WS[key] = S.Workspace(1 << key, device=DEV)
+    return _WS[key]
+
+
+def host_bits(x_bf16):
+    return W.bits(x_bf16.cpu()).numpy().view(np.uint16)
+
+
+def gpu_run(x_cpu, cb_source=None, ws=None):
+    """calibrate (on cb_source or x) -> encode -> decode on the GPU."""
+    x = x_cpu.reshape(-1).to(DEV)
+    n = x.numel()
+    ws = ws or workspace(max(n, 0 if cb_source is None else cb_source.numel()))
+    src = x if cb_source is None else cb_source.reshape(-1).to(DEV)
+    cb = S.calibrate(src, ws)
+    payload, meta = S.encode(x, cb, ws)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = S.decode(payload, meta, cb, n, status=status)
+    torch.cuda.synchronize()
+    m = S.read_meta(meta)
+    c = S.read_codebook(cb)
+    pay = payload[: m.comp_bytes].cpu().numpy().tobytes()
+    return dict(cb=c, meta=m, payload=pay, out=host_bits(out), status=int(status.item()),
+                cb_dev=cb, payload_dev=payload, meta_dev=meta)
+
+
+def check_codebook(c, ocb):
+    assert bytes(c.enc_lut) == ocb.enc_lut.tobytes()
+    assert bytes(c.enc_lut_marked) == ocb.enc_lut_marked.tobytes()
+    assert bytes(c.dec_lut) == ocb.dec_lut.tobytes()
+    assert bytes(c.common_lut) == ocb.common_lut.tobytes()
+    assert c.n_codes == ocb.n_codes and c.covered == ocb.covered and c.total == ocb.total
+    assert np.array_equal(np.frombuffer(bytes(c.counts), np.uint64), ocb.counts)
+
+
+def check_meta(m, om, ocb_src):
+    assert m.status == 0
+    assert (m.n, m.n_pairs, m.chunk_size, m.n_esc, m.comp_bytes) == \
+        (om.n, om.n_pairs, om.chunk_size, om.n_esc, om.comp_bytes)
+    assert tuple(m.offsets) == tuple(om.offsets)
+    assert (m.covered, m.total) == (ocb_src.covered, ocb_src.total)
+
+
+def meta_to_device(om) -> torch.Tensor:
+    m = _abi.Meta()
+    m.n, m.n_pairs, m.chunk_size, m.n_esc, m.comp_bytes = (om.n, om.n_pairs, om.chunk_size,
+                                                          om.n_esc, om.comp_bytes)
+    for k in range(5):
+        m.offsets[k] = om.offsets[k]
+    raw = bytes(m)
+    return torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(DEV)
+
+
+def gpu_decode_bytes(payload: bytes, om, dec_lut) -> tuple:
+    pay = torch.frombuffer(bytearray(payload + b"\0" * 16), dtype=torch.uint8).to(DEV)
+    meta = meta_to_device(om)
+    lut = torch.tensor(np.asarray(dec_lut, np.uint8)).to(DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = torch.empty(om.n, dtype=torch.bfloat16, device=DEV)
+    if om.n:
+        S.decode(pay[: len(payload)], meta, lut, om.n, out=out, status=status)
+    torch.cuda.synchronize()
+    return host_bits(out), int(status.item())
+
+
+def full_parity(x_cpu, cb_source=None, name=""):
+    _say("parity case %s n=%d" % (name, x_cpu.numel()))
+    xs = host_bits(x_cpu)
+    g = gpu_run(x_cpu, cb_source)
+    src = xs if cb_source is None else host_bits(cb_source)
+    ocb = oracle.calibrate(src)
+    check_codebook(g["cb"], ocb)
+    opay, om = oracle.encode(xs, ocb)
+    check_meta(g["meta"], om, ocb)
+    if g["payload"] != opay:
+        a = np.frombuffer(g["payload"], np.uint8)
+        b = np.frombuffer(opay, np.uint8)
+        bad = np.nonzero(a != b)[0]
+        raise AssertionError("payload differs at %d bytes, first at %d (sections %s)"
+                             % (bad.size, bad[0], om.offsets))
+    assert g["status"] == 0
+    assert np.array_equal(g["out"], xs)
+    # cross-decoding: oracle decodes the GPU payload, the GPU decodes the oracle's
+    assert np.array_equal(oracle.decode(g["payload"], om, ocb.dec_lut), xs)
+    out2, st2 = gpu_decode_bytes(opay, om, ocb.dec_lut)
+    assert st2 == 0 and np.array_equal(out2, xs)
+    return g, om
+
+
+SIZES = [0, 1, 2, 3, 5, 7, 8, 9, 15, 16, 17, 31, 33, 1023, 1024, 1025, 2047, 4095, 4096, 4097,
+         8191, 8192, 8193, 12289, 65536, 100_003]
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_sizes_gaussian(n):
+    full_parity(W.gaussian_weight(n, seed=11), name="gauss")
+
+
+@pytest.mark.parametrize("n", [1, 7, 4097, 8193, 100_003, 300_001])
+def test_sizes_escape_heavy(n):
+    full_parity(W.log_uniform_stress(n, seed=12), name="loguniform")
+
+
+@pytest.mark.parametrize("n", [3, 4096, 77_777])
+def test_random_bits(n):
+    g = torch.Generator().manual_seed(n)
+    x = torch.randint(-32768, 32768, (n,), dtype=torch.int32, generator=g).to(torch.int16)
+    full_parity(x.view(torch.bfloat16), name="randbits")
+
+
+def test_subnormal_only():
+    full_parity(W.subnormal_gaussian(70_001, seed=3, stream=1), name="subnormal")
+
+
+def test_constant_tensor():
+    full_parity(torch.full((50_001,), -3.5, dtype=torch.bfloat16), name="constant")
+
+
+def test_exhaustive_patterns():
+    x = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    g, om = full_parity(x, name="exhaustive")
+    assert om.n_esc == 61440 and om.comp_bytes == 528384
+
+
+def test_foreign_codebook_all_escape():
+    x = W.gaussian_weight(50_003, seed=13)
+    src = W.subnormal_gaussian(1000, seed=3, stream=1)   # only exponent 0 has a code
+    g, om = full_parity(x, cb_source=src, name="all-escape")
+    assert om.n_esc > 49_000
+
+
+def test_golden_examples():
+    for ex in P.load_examples():
+        x = torch.from_numpy(P.example_input(ex).astype(np.int16)).view(torch.bfloat16)
+        src = None
+        if ex["codebook_from"] != "self":
+            src = torch.from_numpy(P._u16(ex["codebook_from"]["x"]).astype(np.int16)).view(
+                torch.bfloat16)
+        if x.numel() == 0:
+            continue
+        g = gpu_run(x, src)
+        assert g["payload"] == P.example_payload(ex), ex["name"]
+        assert np.array_equal(g["out"], P.example_input(ex))
+
+
+def test_escapes_at_chunk_and_tile_edges():
+    n = 3 * 4096 + 5
+    x = torch.full((n,), 1.0, dtype=torch.bfloat16)
+    edges = [0, 1, 1023, 1024, 2047, 2048, 4095, 4096, 4097, 8191, 8192, 12287, 12288, n - 1]
+    x[edges] = 2.0
+    src = torch.ones(8, dtype=torch.bfloat16)
+    g, om = full_parity(x, cb_source=src, name="edges")
+    assert om.n_esc == len(edges)
+
+
+def test_determinism_and_workspace_reuse():
+    big = W.log_uniform_stress(1 << 20, seed=14)
+    small = W.gaussian_weight(5_001, seed=15)
+    ws = workspace(1 << 20)
+    runs = [gpu_run(big, ws=ws), gpu_run(small, ws=ws), gpu_run(big, ws=ws), gpu_run(big, ws=ws)]
+    assert runs[0]["payload"] == runs[2]["payload"] == runs[3]["payload"]
+    xs = host_bits(small)
+    opay, _ = oracle.encode(xs, oracle.calibrate(xs))
+    assert runs[1]["payload"] == opay
+
+
+def test_capacity_overflow():
+    x = W.log_uniform_stress(20_001, seed=16).to(DEV)
+    ws = workspace(20_001)
+    cb = S.calibrate(x, ws)
+    xs = host_bits(x)
+    _, om = oracle.encode(xs, oracle.calibrate(xs))
+    cap = om.offsets[2] + 4 * (om.n_esc // 2)   # room for half of the chunk ids only
+    guard = 64
+    buf = torch.full((cap + guard,), 0xA5, dtype=torch.uint8, device=DEV)
+    meta = torch.zeros(S.codec.META_BYTES, dtype=torch.uint8, device=DEV)
+    rc = _abi.splitzip_encode(x.view(torch.int16).data_ptr(), x.numel(), cb.data_ptr(),
+                              buf.data_ptr(), cap, meta.data_ptr(), ws.ptr(), ws.nbytes,
+                              torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    m = S.read_meta(meta)
+    assert m.status == _abi.ERR_CAPACITY and m.comp_bytes == om.comp_bytes
+    assert bool((buf[cap:] == 0xA5).all())          # nothing written past capacity
+    # synchronous check: below the dense size
+    rc = _abi.splitzip_encode(x.view(torch.int16).data_ptr(), x.numel(), cb.data_ptr(),
+                              buf.data_ptr(), om.offsets[2] - 1, meta.data_ptr(), ws.ptr(),
+                              ws.nbytes, torch.cuda.current_stream().cuda_stream)
+    assert rc == _abi.ERR_CAPACITY
+
+
+def test_decode_flags_corrupt_streams():
+    n = 3000
+    x = torch.full((n,), 1.0, dtype=torch.bfloat16)
+    x[[5, 1500, 2999]] = 2.0
+    xs = host_bits(x)
+    ocb = oracle.calibrate(np.array([0x3F80], np.uint16))
+    opay, om = oracle.encode(xs, ocb)
+    cid_at, pos_at = om.offsets[2], om.offsets[3]
+
+    def patched(edits):
+        b = bytearray(opay)
+        for at, val, width in edits:
+            b[at: at + width] = val.to_bytes(width, "little", signed=val < 0)
+        return bytes(b)
+
+    cases = {
+        _abi.DEC_POS_GE_CHUNK: [(pos_at, 1024, 2)],
+        _abi.DEC_ESC_OUT_OF_RANGE: [(cid_at + 8, 9, 4)],
+        _abi.DEC_NOT_INCREASING: [(pos_at, 1000, 2), (cid_at + 4, 0, 4)],
+    }
+    for bit, edits in cases.items():
+        _, st = gpu_decode_bytes(patched(edits), om, ocb.dec_lut)
+        assert st & bit, (bit, st)
+    bad = oracle.Meta(om.n, om.n_pairs, om.chunk_size, om.n_esc, om.comp_bytes,
+                      (0, om.offsets[1] + 4) + tuple(om.offsets[2:]))
+    _, st = gpu_decode_bytes(opay, bad, ocb.dec_lut)
+    assert st & _abi.DEC_BAD_META
+    _, st = gpu_decode_bytes(opay, om, ocb.dec_lut)
+    assert st == 0
+
+
+def test_argument_errors():
+    x = torch.zeros(64, dtype=torch.bfloat16, device=DEV)
+    ws = workspace(64)
+    cbt = torch.empty(S.codec.CODEBOOK_BYTES, dtype=torch.uint8, device=DEV)
+    s = torch.cuda.current_stream().cuda_stream
+    xp = x.view(torch.int16).data_ptr()
+    assert _abi.splitzip_calibrate(xp + 2, 63, cbt.data_ptr(), ws.ptr(), ws.nbytes, s) == \
+        _abi.ERR_INVALID
+    assert _abi.splitzip_calibrate(0, 64, cbt.data_ptr(), ws.ptr(), ws.nbytes, s) == \
+        _abi.ERR_INVALID
+    assert _abi.splitzip_calibrate(xp, 64, cbt.data_ptr(), ws.ptr(), 100, s) == \
+        _abi.ERR_WORKSPACE
+    assert _abi.splitzip_calibrate(xp, 64, cbt.data_ptr(), ws.ptr(), ws.nbytes, s) == _abi.OK
+    with pytest.raises(ValueError):
+        S.calibrate(torch.zeros(8, dtype=torch.float16, device=DEV), ws)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size
+# ---------------------------------------------------------------------------
+
+def test_workload_weight_1m_odd():
+    g, om = full_parity(W.gaussian_weight(1_000_003, seed=0), name="weight_1m_odd")
+    assert 0.749 < om.comp_bytes / (2 * 1_000_003) < 0.752
+
+
+@pytest.mark.parametrize("kv", [0, 1])
+def test_workload_kv_layer(kv):
+    full_parity(W.kv_layer(seed=2, stream=kv), name="kv_layer_%d" % kv)
+
+
+def test_workload_stress_log_uniform():
+    g, om = full_parity(W.log_uniform_stress(1 << 24, seed=3, stream=0), name="stress_loguniform")
+    assert om.n_esc > (1 << 23)
+
+
+def test_workload_stress_subnormal():
+    g, om = full_parity(W.subnormal_gaussian(1 << 24, seed=3, stream=1), name="stress_subnormal")
+    assert om.n_esc == 0
+
+
+def test_workload_linear_weight_decode_100x():
+    x_cpu = W.weight_with_outliers(seed=4)
+    _say("parity case linear_weight n=%d" % x_cpu.numel())
+    g, om = full_parity(x_cpu, name="linear_weight")
+    n = x_cpu.numel()
+    arena = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for _ in range(100):
+        S.decode(g["payload_dev"], g["meta_dev"], g["cb_dev"], n, out=arena, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(host_bits(arena), host_bits(x_cpu))
+
+
+def test_workload_kv_stream_4gib():
+    """32 layers x (K, V) [1, 8, 32768, 128], one codebook each.  Every tensor
+    is round-tripped on the GPU and checked against the closed-form size and
+    the escape-count identity; three of them are compared byte for byte with
+    the oracle."""
+    n = 8 * 32768 * 128
+    ws = workspace(n)
+    payload = torch.empty(S.payload_size(n, n), dtype=torch.uint8, device=DEV)
+    out = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    full = {(0, 0), (17, 1), (31, 1)}
+    for layer in range(32):
+        for kv in range(2):
+            x = W.kv_cache_tensor(layer, kv, device=DEV)
+            cb = S.calibrate(x, ws)
+            _, meta = S.encode(x, cb, ws, payload=payload)
+            S.decode(payload, meta, cb, n, out=out, status=status)
+            assert torch.equal(out.view(torch.int16), x.reshape(-1).view(torch.int16))
+            m = S.read_meta(meta)
+            c = S.read_codebook(cb)
+            assert m.status == 0 and m.n_esc == n - c.covered
+            assert m.comp_bytes == P.closed_form_total(n, m.n_esc)
+            if (layer, kv) in full:
+                _say("parity case kv_stream layer=%d kv=%d" % (layer, kv))
+                xs = host_bits(x)
+                ocb = oracle.calibrate(xs)
+                check_codebook(c, ocb)
+                opay, om = oracle.encode(xs, ocb)
+                check_meta(m, om, ocb)
+                assert payload[: m.comp_bytes].cpu().numpy().tobytes() == opay
+    assert int(status.item()) == 0
