@@ -1,0 +1,225 @@
+"""Benchmark of the SplitZip codec on one MI355X.
+
+Workload: a streaming KV cache of 32 layers x (K, V) tensors [1, 8, 32768, 128]
+bf16 (64 tensors, 2^31 elements, 4 GiB), N(0, 0.02) values (seed 5, stream
+2*layer + kv), one codebook per tensor.  A step is one pass of the whole hot
+path: calibrate all 64 tensors, encode all 64, decode all 64 (inputs already
+resident in HBM).  The per-phase times come from HIP events on the stream the
+kernels are launched on.
+
+Prints ONE JSON line.  ``value`` is the end-to-end raw-BF16 throughput of the
+step (4 GiB / step time); the line also carries per-phase throughput, the
+compression ratio, the roofline of the dominant call and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "encode/decode GB/s of raw BF16 + % HBM roofline; compression ratio"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
+LAYERS, HEADS, SEQ, HEAD_DIM = 32, 8, 32768, 128
+N = HEADS * SEQ * HEAD_DIM       # elements per tensor
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU oracle budget for the cpu_baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this codec build runs on exactly one GPU; --gpus %d is not supported "
+              "(the multi-GPU sharding is described in DESIGN.md)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import lossless_bf16_tensor_splitzip_amd as S
+    from lossless_bf16_tensor_splitzip_amd import _abi
+    import workloads as W
+
+    lib = S.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = int(stream.cuda_stream)
+    T = 2 * LAYERS
+
+    # inputs, generated on the GPU, resident in HBM
+    x_all = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    for layer in range(LAYERS):
+        for kv in range(2):
+            x_all[2 * layer + kv] = W.kv_cache_tensor(layer, kv, device=dev).reshape(-1)
+    cap = S.payload_size(N, N)          # worst case: any data fits
+    pay_all = torch.empty(T, cap, dtype=torch.uint8, device=dev)
+    out_all = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    cbs = torch.empty(T, S.codec.CODEBOOK_BYTES, dtype=torch.uint8, device=dev)
+    metas = torch.zeros(T, S.codec.META_BYTES, dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = S.Workspace(N, device=dev)
+    torch.cuda.synchronize()
+
+    xp = [x_all[i].data_ptr() for i in range(T)]
+    pp = [pay_all[i].data_ptr() for i in range(T)]
+    op = [out_all[i].data_ptr() for i in range(T)]
+    cp = [cbs[i].data_ptr() for i in range(T)]
+    mp = [metas[i].data_ptr() for i in range(T)]
+    wsp, wsb, stp = ws.ptr(), ws.nbytes, status.data_ptr()
+    lut_off = _abi.DEC_LUT_OFFSET
+    cal, enc, dec = lib.splitzip_calibrate, lib.splitzip_encode, lib.splitzip_decode
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        for i in range(T):
+            rc = cal(xp[i], N, cp[i], wsp, wsb, sh)
+            if rc:
+                raise _abi.SplitZipError("splitzip_calibrate", rc)
+        if evs:
+            evs[1].record(stream)
+        for i in range(T):
+            rc = enc(xp[i], N, cp[i], pp[i], cap, mp[i], wsp, wsb, sh)
+            if rc:
+                raise _abi.SplitZipError("splitzip_encode", rc)
+        if evs:
+            evs[2].record(stream)
+        for i in range(T):
+            rc = dec(pp[i], cap, mp[i], cp[i] + lut_off, op[i], N, 0, sh)
+            if rc:
+                raise _abi.SplitZipError("splitzip_decode", rc)
+        if evs:
+            evs[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    phase_ms = {"calibrate": 0.0, "encode": 0.0, "decode": 0.0}
+    for e in evs:
+        phase_ms["calibrate"] += e[0].elapsed_time(e[1])
+        phase_ms["encode"] += e[1].elapsed_time(e[2])
+        phase_ms["decode"] += e[2].elapsed_time(e[3])
+    for k in phase_ms:
+        phase_ms[k] /= args.steps
+    step_ms = sum(phase_ms.values())
+
+    # correctness of the timed work: every tensor round-trips bit for bit
+    assert int(status.item()) == 0, "decode reported status %d" % int(status.item())
+    assert torch.equal(out_all.view(torch.int16), x_all.view(torch.int16)), "round trip failed"
+    metas_h = [S.read_meta(metas[i]) for i in range(T)]
+    assert all(m.status == 0 for m in metas_h)
+    comp_total = sum(m.comp_bytes for m in metas_h)
+    esc_total = sum(m.n_esc for m in metas_h)
+    covered = sum(m.covered for m in metas_h)
+    raw_bytes = 2 * N * T
+
+    def gbps(nbytes, ms):
+        return nbytes / (ms * 1e-3) / 1e9
+
+    # algorithmic bytes (what the method must move) per phase
+    alg = {"calibrate": raw_bytes, "encode": raw_bytes + comp_total, "decode": comp_total + raw_bytes}
+    phases = {}
+    for k, ms in phase_ms.items():
+        phases[k] = {"ms": round(ms, 4), "ms_per_call": round(ms / T, 5),
+                     "raw_GBps": round(gbps(raw_bytes, ms), 1),
+                     "alg_bytes_per_call": alg[k] // T,
+                     "alg_GBps": round(gbps(alg[k], ms), 1),
+                     "hbm_frac": round(gbps(alg[k], ms) / HBM_PEAK_GBPS, 4)}
+    dom = max(phase_ms, key=phase_ms.get)
+    kernel_of = {"calibrate": "k_calibrate", "encode": "k_encode+k_encode_tail",
+                 "decode": "k_decode_dense+k_decode_patch"}
+    achieved = gbps(alg[dom], phase_ms[dom])
+    roofline = {"bound": "hbm", "kernel": kernel_of[dom], "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x_all, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbps(raw_bytes, step_ms), 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": "kv_stream_32x2x8x32768x128", "tensors": T,
+                   "elements_per_tensor": N, "raw_bytes": raw_bytes,
+                   "values": "N(0,0.02) bf16, seed 5, stream 2*layer+kv",
+                   "codebook": "one per tensor", "step": "calibrate all, encode all, decode all"},
+        "encode_GBps": phases["encode"]["raw_GBps"],
+        "decode_GBps": phases["decode"]["raw_GBps"],
+        "calibrate_GBps": phases["calibrate"]["raw_GBps"],
+        "payload_over_raw": round(comp_total / raw_bytes, 6),
+        "raw_over_payload": round(raw_bytes / comp_total, 4),
+        "n_esc_total": esc_total,
+        "coverage": round(covered / (N * T), 6),
+        "phases": phases,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "context_h200": {"encode_GBps": 613, "decode_GBps": 2182,
+                         "note": "pages' figures on LLM KV activations, other hardware"},
+    }
+    print(json.dumps(line))
+
+
+def cpu_baseline(x_all, budget_s):
+    """The oracle as it stands (plain single-threaded C), on whole tensors of
+    the same workload until the time budget is spent."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    o = oracle.default()
+    done, t_cpu = 0, 0.0
+    while done < x_all.shape[0] and (t_cpu < budget_s or done == 0):
+        xs = x_all[done].view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        cb = o.calibrate(xs)
+        payload, meta = o.encode(xs, cb)
+        out = o.decode(payload, meta, cb.dec_lut)
+        t_cpu += time.perf_counter() - t0
+        if not np.array_equal(out, xs):
+            raise AssertionError("oracle round trip failed on tensor %d" % done)
+        done += 1
+    raw = 2 * N * done
+    return {"value": round(raw / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d of 64 tensors (calibrate+encode+decode each), %.1f s" % (done, t_cpu)}
+
+
+if __name__ == "__main__":
+    main()

@@ -8,28 +8,36 @@
 // to both routes", item 1).  Ties among equally frequent exponents are broken
 // by ascending exponent value.
 //
-// Kernels (all integer work, HBM-bandwidth bound, no matrix cores):
-//   k_calibrate      exponent histogram in LDS (one private copy per lane of
-//                    a wave, so equal exponents never collide on a bank), one
-//                    device atomic per non-empty bin per workgroup, and a
-//                    top-16 select by the last workgroup to finish.
-//   k_encode         persistent tile loop: 16-byte loads, LDS code table,
-//                    nibble packing, sign+mantissa bytes, wave ballots to
-//                    rank escapes, decoupled look-back across tiles (tickets
-//                    handed out in start order, so every awaited tile is
-//                    running or done) giving each escape its global rank in
-//                    ascending element order.
-//   k_encode_tail    moves the staged positions / raw exponents behind the
-//                    chunk ids once the escape count is known, writes the
-//                    metadata and leaves the workspace clean for the next call.
-//   k_decode_dense   pk + sm -> bf16 through a 256-entry pair table in LDS.
-//   k_decode_patch   one lane per escape: rebuild the element from its raw
-//                    exponent and its own sign/mantissa byte.
+// All work is integer and streams through HBM; nothing is a contraction, so
+// no matrix cores.  Device-scope atomics on one address serialise (about
+// 12 ns each on this part), so no kernel takes a global ticket or bumps a
+// shared counter per workgroup:
+//   k_calibrate   exponent histogram in LDS (64 lane-private copies, so equal
+//                 exponents in a wave never hit one bank), per-workgroup
+//                 partials written with plain stores, merged by the last
+//                 arriver of each group of 16 workgroups and then by the last
+//                 group (counters on separate cache lines), which also runs
+//                 the top-16 select.
+//   k_encode      one 4096-element tile per workgroup: 16-byte loads, code
+//                 table in LDS, nibble packing, sign/mantissa bytes, wave
+//                 ballots to rank escapes, decoupled look-back over tiles in
+//                 launch order.  A tile whose predecessor has published
+//                 nothing after a short wait counts that predecessor's escapes
+//                 itself, so progress never depends on the dispatch order.
+//   k_encode_tail moves staged positions / raw exponents behind the chunk ids
+//                 once the escape count is known, writes the metadata and
+//                 leaves the workspace clean for the next call.
+//   k_decode      one 8192-element tile per workgroup: pk + sm -> bf16 through
+//                 a 256-entry pair table in LDS, with the tile's escapes found
+//                 by a wave-wide search of the sorted chunk ids and patched
+//                 before (few) or after (many) the 16-byte stores.
+//   k_decode_check  (only when a status word is requested) validates every
+//                 escape and re-applies it by scatter, which also makes the
+//                 decode correct for escape streams that are not sorted.
 
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
-#include <string.h>
 
 #include "splitzip.h"
 
@@ -43,21 +51,22 @@ constexpr int kEncTile = kThreads * kUnit * kEncUnits;   // 4096 elements
 constexpr int kDecUnits = 4;
 constexpr int kDecTile = kThreads * kUnit * kDecUnits;   // 8192 elements
 constexpr int kCalThreads = 1024;
+constexpr int kCalMaxGrid = 512;              // two 1024-thread workgroups per CU
+constexpr int kCalGroup = 16;                 // arrivals per first-level counter
+constexpr int kCalCopies = 16;                // global histogram copies
+constexpr int kRegisterPatchMax = 16;         // escapes per decode tile patched in registers
+constexpr int kTailTiles = 256;               // encode tiles placed per tail workgroup
 
-// Workspace layout (bytes).  The tile-status region and the staging areas
-// depend only on the workspace size, so one workspace serves any n that fits.
-constexpr size_t kWsTicket = 0;      // uint32 encode tile ticket
-constexpr size_t kWsCalDone = 4;     // uint32 calibrate workgroups finished
-constexpr size_t kWsGuard = 8;       // uint32 progress guard tripped
-constexpr size_t kWsTotalEsc = 16;   // uint64 escape count of the last encode
-constexpr size_t kWsHist = 256;      // uint64[256] global histogram
-constexpr size_t kWsStatus = 256 + 2048;  // uint64[t_max] look-back words
+// Workspace layout (bytes).  Counters sit on separate cache lines; all of them
+// and the global histogram copies return to zero at the end of every call.
+// The tile counts and the staging area depend only on the workspace size, so
+// one workspace serves any n that fits.
+constexpr size_t kWsCalTop = 0;                                          // uint32
+constexpr size_t kWsCalLvl1 = 256;                                       // uint32, 64 B apart
+constexpr size_t kWsCalHist = kWsCalLvl1 + 64 * (kCalMaxGrid / kCalGroup);   // uint64[16][256]
+constexpr size_t kWsTiles = kWsCalHist + 8 * 256 * kCalCopies;            // uint32[t_max], then stage
 constexpr size_t kWsSlack = 64;
-
-constexpr uint64_t kFlagAgg = 1ull << 62;
-constexpr uint64_t kFlagPrefix = 2ull << 62;
-constexpr uint64_t kValueMask = (1ull << 62) - 1;
-constexpr uint32_t kSpinLimit = 1u << 20;
+static_assert(kWsTiles % 256 == 0, "alignment");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -70,6 +79,7 @@ struct Layout {
     uint64_t n_pairs, off_sm, off_cid, off_lpos, off_ev, total;
 };
 
+// Page 1, assemble_payload: section offsets for n elements and e escapes.
 __host__ __device__ inline Layout layout_of(uint64_t n, uint64_t e) {
     Layout L;
     L.n_pairs = (n + 1) / 2;
@@ -81,19 +91,19 @@ __host__ __device__ inline Layout layout_of(uint64_t n, uint64_t e) {
     return L;
 }
 
-// Staging areas and look-back capacity of a workspace of ws_bytes.
+// Tile capacity and staging area of a workspace of ws_bytes.
 struct WsPlan {
-    uint64_t t_max;       // tiles the status region holds
-    uint64_t off_lpos;    // uint16[t_max * kEncTile]
-    uint64_t off_ev;      // uint8[t_max * kEncTile]
+    uint64_t t_max;       // tiles the workspace holds
+    uint64_t off_count;   // uint32[t_max] escapes per tile
+    uint64_t off_stage;   // uint32[t_max * kEncTile] staged escapes
 };
 
 __host__ inline WsPlan ws_plan(size_t ws_bytes) {
     WsPlan P{0, 0, 0};
-    if (ws_bytes < kWsStatus + kWsSlack) return P;
-    P.t_max = (ws_bytes - kWsStatus - kWsSlack) / (8 + 3 * (uint64_t)kEncTile);
-    P.off_lpos = align16(kWsStatus + 8 * P.t_max);
-    P.off_ev = align16(P.off_lpos + 2 * P.t_max * kEncTile);
+    if (ws_bytes < kWsTiles + kWsSlack) return P;
+    P.t_max = (ws_bytes - kWsTiles - kWsSlack) / (4 + 4 * (uint64_t)kEncTile);
+    P.off_count = kWsTiles;
+    P.off_stage = align16(kWsTiles + 4 * P.t_max);
     return P;
 }
 
@@ -125,9 +135,18 @@ __device__ inline uint32_t join16(uint32_t sm, uint32_t ex) {
     return ((sm & 0x80u) << 8) | (ex << 7) | (sm & 0x7Fu);
 }
 
+// Word k of a 4-word vector without dynamic register indexing.
+__device__ inline uint32_t word_of(const u32x4 q, int k) {
+    return k == 0 ? q.x : (k == 1 ? q.y : (k == 2 ? q.z : q.w));
+}
+
 // ---------------------------------------------------------------------------
 // Calibrate (page 1, calibrate_codebook)
 // ---------------------------------------------------------------------------
+
+// Wait until every vector memory operation this wave issued has completed
+// (for atomics: performed at the device coherence point).
+__device__ inline void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
 __global__ __launch_bounds__(kCalThreads) void k_calibrate(const uint16_t *__restrict__ x,
                                                            uint64_t n,
@@ -135,9 +154,9 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(const uint16_t *__res
                                                            uint8_t *__restrict__ ws) {
     __shared__ uint32_t hist[256 * 64];   // [exponent][lane]
     __shared__ uint32_t part[4 * 256];
-    __shared__ uint64_t cnt[256];
+    __shared__ uint64_t key[256];
     __shared__ uint64_t covered;
-    __shared__ uint32_t is_last;
+    __shared__ uint32_t proceed;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -184,38 +203,70 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(const uint16_t *__res
         part[tid] = s;
     }
     __syncthreads();
+    // Merge into one of kCalCopies global histograms (few workgroups per
+    // address, so the device atomics do not queue up behind each other).
+    uint64_t *ghist = reinterpret_cast<uint64_t *>(ws + kWsCalHist);
     if (tid < 256) {
-        uint32_t s = part[tid] + part[256 + tid] + part[512 + tid] + part[768 + tid];
-        if (s) atomicAdd(reinterpret_cast<unsigned long long *>(ws + kWsHist) + tid,
-                         (unsigned long long)s);
+        const uint32_t s = part[tid] + part[256 + tid] + part[512 + tid] + part[768 + tid];
+        if (s)
+            atomicAdd(reinterpret_cast<unsigned long long *>(
+                          ghist + (blockIdx.x % kCalCopies) * 256 + tid),
+                      (unsigned long long)s);
     }
-    __threadfence();
+    wait_vector_memory();
     __syncthreads();
+
+    // Arrival: the last workgroup of each group of 16 reports to the top
+    // counter; the last group merges the copies and selects the codes.
+    const uint32_t g = blockIdx.x / kCalGroup;
+    const uint32_t gsize = min((uint32_t)kCalGroup, gridDim.x - g * kCalGroup);
+    const uint32_t ngroups = (gridDim.x + kCalGroup - 1) / kCalGroup;
     if (tid == 0) {
-        uint32_t prev = __hip_atomic_fetch_add(reinterpret_cast<uint32_t *>(ws + kWsCalDone), 1u,
-                                               __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = (prev == gridDim.x - 1) ? 1u : 0u;
+        uint32_t *ctr = reinterpret_cast<uint32_t *>(ws + kWsCalLvl1 + 64 * g);
+        const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t go = 0;
+        if (prev == gsize - 1) {
+            __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t *top = reinterpret_cast<uint32_t *>(ws + kWsCalTop);
+            const uint32_t p2 = __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+            if (p2 == ngroups - 1) {
+                __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                go = 1;
+            }
+        }
+        proceed = go;
         covered = 0;
     }
     __syncthreads();
-    if (!is_last) return;
-    __threadfence();
+    if (!proceed) return;
 
-    // Last workgroup: every histogram atomic of this call is visible.  Rank of
-    // exponent v = number of exponents with a larger count, or an equal count
-    // and a smaller value; ranks 0..15 of occurring exponents become codes.
-    uint64_t *ghist = reinterpret_cast<uint64_t *>(ws + kWsHist);
-    if (tid < 256) cnt[tid] = ld_agent(ghist + tid);
-    __syncthreads();
-    uint32_t code = 16;
     uint64_t c = 0;
     if (tid < 256) {
-        c = cnt[tid];
-        uint32_t rank = 0;
-        for (int u = 0; u < 256; ++u) {
-            uint64_t cu = cnt[u];
-            rank += (cu > c || (cu == c && u < tid)) ? 1u : 0u;
+        uint64_t copy[kCalCopies];
+#pragma unroll
+        for (int k = 0; k < kCalCopies; ++k) copy[k] = ld_agent(ghist + k * 256 + tid);
+#pragma unroll
+        for (int k = 0; k < kCalCopies; ++k) {
+            c += copy[k];
+            st_agent(ghist + k * 256 + tid, 0);   // clean for the next call
         }
+        // unique sort key: count first, then the smaller exponent value
+        key[tid] = c ? ((c << 8) | (uint64_t)(255 - tid)) : 0;
+    }
+    __syncthreads();
+    {   // rank = number of larger keys; 4 threads per exponent, 64 keys each
+        const int bin = tid & 255, quarter = tid >> 8;
+        const uint64_t mine = key[bin];
+        uint32_t r = 0;
+        for (int u = quarter * 64; u < quarter * 64 + 64; ++u) r += key[u] > mine ? 1u : 0u;
+        part[tid] = r;
+    }
+    __syncthreads();
+    uint32_t code = 16;
+    if (tid < 256) {
+        const uint32_t rank = part[tid] + part[256 + tid] + part[512 + tid] + part[768 + tid];
         code = (c > 0 && rank < 16) ? rank : 16u;
         cb->enc_lut[tid] = (uint8_t)(code < 16 ? code : 0);
         cb->enc_lut_marked[tid] = (uint8_t)code;
@@ -225,7 +276,6 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(const uint16_t *__res
             cb->dec_lut[code] = (uint8_t)tid;
             atomicAdd(reinterpret_cast<unsigned long long *>(&covered), (unsigned long long)c);
         }
-        st_agent(ghist + tid, 0);   // leave the histogram clean for the next call
     }
     const int distinct = __syncthreads_count(tid < 256 && c > 0);
     const uint32_t n_codes = distinct < 16 ? (uint32_t)distinct : 16u;
@@ -235,7 +285,6 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(const uint16_t *__res
         cb->reserved = 0;
         cb->covered = covered;
         cb->total = n;
-        *reinterpret_cast<uint32_t *>(ws + kWsCalDone) = 0;
     }
 }
 
@@ -249,17 +298,10 @@ struct EncArgs {
     uint64_t ntiles;
     const splitzip_codebook *cb;
     uint8_t *payload;
-    uint64_t capacity;
     uint64_t n_pairs, off_sm, off_cid;
-    uint8_t *ws;
-    uint16_t *stage_lpos;
-    uint8_t *stage_ev;
+    uint32_t *tile_count;   // escapes per tile
+    uint32_t *stage;        // per tile: (position in tile << 8) | raw exponent, in order
 };
-
-// Word k of a 4-word vector without dynamic register indexing.
-__device__ inline uint32_t word_of(const u32x4 q, int k) {
-    return k == 0 ? q.x : (k == 1 ? q.y : (k == 2 ? q.z : q.w));
-}
 
 // One 8-element unit: codes -> 4 pk bytes, sign/mantissa -> 8 sm bytes,
 // escape mask (bit j = element j escapes).
@@ -272,7 +314,8 @@ __device__ inline void encode_unit(const u32x4 q, const uint8_t *lut, uint32_t &
         const uint32_t w = q[k];
         const uint32_t m_even = lut[exp_lo(w)];
         const uint32_t m_odd = lut[exp_hi(w)];
-        // marked code: 0..15, or 16 for an escape, whose nibble is 16 & 15 = 0
+        // marked code: 0..15, or 16 for an escape, whose nibble is 16 & 15 = 0;
+        // the even element takes the high nibble
         const uint32_t byte = ((m_even & 15u) << 4) | (m_odd & 15u);
         pk |= byte << (8 * k);
         flags |= ((m_even >> 4) | ((m_odd >> 4) << 1)) << (2 * k);
@@ -283,184 +326,129 @@ __device__ inline void encode_unit(const u32x4 q, const uint8_t *lut, uint32_t &
           (sm_of16(q[3] >> 16) << 24);
 }
 
+// Dense sections of one tile plus the tile's escapes, staged in element
+// order; no communication between tiles.
 __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
     __shared__ uint8_t lut[256];
     __shared__ uint32_t wtot[kEncUnits][4];
-    __shared__ uint32_t tile_slot[2];
-    __shared__ uint64_t excl_slot;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    uint32_t *ticket = reinterpret_cast<uint32_t *>(a.ws + kWsTicket);
-    uint64_t *status = reinterpret_cast<uint64_t *>(a.ws + kWsStatus);
+    const uint64_t t = blockIdx.x;
+    const uint64_t base = t * kEncTile;
+    const bool full = base + kEncTile <= a.n;
 
+    u32x4 q[kEncUnits];
+    if (full) {
+#pragma unroll
+        for (int u = 0; u < kEncUnits; ++u) {
+            const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+            q[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.x + i0));
+        }
+    }
     lut[tid] = a.cb->enc_lut_marked[tid];
-    if (tid == 0) tile_slot[0] = atomicAdd(ticket, 1u);
     __syncthreads();
 
-    uint32_t it = 0;
-    uint64_t t = tile_slot[0];
-    while (t < a.ntiles) {
-        if (tid == 0) tile_slot[(it + 1) & 1] = atomicAdd(ticket, 1u);
-        const uint64_t base = t * kEncTile;
-        const bool full = base + kEncTile <= a.n;
-
-        u32x4 q[kEncUnits];
-        uint32_t flags[kEncUnits];
-        if (full) {
-#pragma unroll
-            for (int u = 0; u < kEncUnits; ++u) {
-                const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
-                q[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.x + i0));
-            }
-#pragma unroll
-            for (int u = 0; u < kEncUnits; ++u) {
-                const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
-                uint32_t pk, sm0, sm1;
-                encode_unit(q[u], lut, pk, sm0, sm1, flags[u]);
-                *reinterpret_cast<uint32_t *>(a.payload + i0 / 2) = pk;
-                u32x2 smv = {sm0, sm1};
-                *reinterpret_cast<u32x2_a4 *>(a.payload + a.off_sm + i0) = smv;
-            }
-        } else {
-            // last, partial tile: element-wise with bounds checks
-#pragma unroll
-            for (int u = 0; u < kEncUnits; ++u) {
-                const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
-                uint32_t codes[kUnit];
-                uint32_t f = 0;
-                uint32_t wv[4] = {0, 0, 0, 0};
-#pragma unroll
-                for (int j = 0; j < kUnit; ++j) {
-                    const uint64_t i = i0 + j;
-                    uint32_t b = 0;
-                    codes[j] = 0;
-                    if (i < a.n) {
-                        b = a.x[i];
-                        const uint32_t m = lut[exp_lo(b)];
-                        codes[j] = m & 15u;
-                        f |= (m >> 4) << j;
-                        a.payload[a.off_sm + i] = (uint8_t)sm_of16(b);
-                    }
-                    wv[j >> 1] |= b << (16 * (j & 1));
-                }
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint64_t i = i0 + 2 * k;
-                    if (i < a.n) {
-                        const uint32_t lo = (i + 1 < a.n) ? codes[2 * k + 1] : 0u;
-                        a.payload[i / 2] = (uint8_t)((codes[2 * k] << 4) | lo);
-                    }
-                }
-                q[u] = u32x4{wv[0], wv[1], wv[2], wv[3]};
-                flags[u] = f;
-            }
-        }
-        if (t == a.ntiles - 1 && tid == 0) {
-            // zero padding between the dense sections (page 1: the payload is
-            // assembled in a zero-filled buffer)
-            for (uint64_t b = a.n_pairs; b < a.off_sm; ++b) a.payload[b] = 0;
-            for (uint64_t b = a.off_sm + a.n; b < a.off_cid; ++b) a.payload[b] = 0;
-        }
-
-        // Escape ranks inside the tile, in element order (unit, thread, j).
-        uint32_t pre[kEncUnits];
+    uint32_t flags[kEncUnits];
+    if (full) {
 #pragma unroll
         for (int u = 0; u < kEncUnits; ++u) {
-            const uint32_t c = __builtin_popcount(flags[u]);
-            const uint64_t any = __ballot(c != 0);
-            uint32_t p = 0, tot = 0;
-            if (any) {
-#pragma unroll
-                for (int bit = 0; bit < 4; ++bit) {
-                    const uint64_t m = __ballot((c >> bit) & 1u);
-                    p += lanes_below(m) << bit;
-                    tot += (uint32_t)__popcll(m) << bit;
-                }
-            }
-            pre[u] = p;
-            if (lane == 0) wtot[u][wave] = tot;
+            const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+            uint32_t pk, sm0, sm1;
+            encode_unit(q[u], lut, pk, sm0, sm1, flags[u]);
+            __builtin_nontemporal_store(pk, reinterpret_cast<uint32_t *>(a.payload + i0 / 2));
+            u32x2 smv = {sm0, sm1};
+            __builtin_nontemporal_store(smv, reinterpret_cast<u32x2_a4 *>(a.payload + a.off_sm + i0));
         }
-        __syncthreads();
-
-        uint32_t tile_total = 0;
-        uint32_t ubase[kEncUnits];
+    } else {
+        // last, partial tile: element-wise with bounds checks
 #pragma unroll
         for (int u = 0; u < kEncUnits; ++u) {
-            ubase[u] = tile_total;
+            const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+            uint32_t codes[kUnit];
+            uint32_t f = 0;
+            uint32_t wv[4] = {0, 0, 0, 0};
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                ubase[u] += (w < wave) ? wtot[u][w] : 0u;
-                tile_total += wtot[u][w];
-            }
-        }
-
-        // Decoupled look-back (wave 0): publish this tile's count, then add
-        // the counts of earlier tiles until one with a published prefix.
-        if (wave == 0) {
-            uint64_t excl = 0;
-            if (t == 0) {
-                if (lane == 0) st_agent(status, kFlagPrefix | tile_total);
-            } else {
-                if (lane == 0) st_agent(status + t, kFlagAgg | tile_total);
-                int64_t j = (int64_t)t - 1;
-                uint32_t spins = 0;
-                while (true) {
-                    const int64_t idx = j - lane;
-                    const uint64_t v = idx >= 0 ? ld_agent(status + idx) : kFlagPrefix;
-                    const uint32_t flag = (uint32_t)(v >> 62);
-                    const uint64_t pm = __ballot(flag == 2);
-                    const uint64_t im = __ballot(flag == 0);
-                    const int fp = pm ? (__ffsll((unsigned long long)pm) - 1) : 64;
-                    const uint64_t before = fp == 64 ? ~0ull : ((1ull << fp) - 1);
-                    if (im & before) {
-                        if (++spins > kSpinLimit) {
-                            if (lane == 0)
-                                atomicOr(reinterpret_cast<uint32_t *>(a.ws + kWsGuard), 1u);
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                        continue;
-                    }
-                    excl += wave_sum_u64(lane <= fp ? (v & kValueMask) : 0);
-                    if (fp < 64) break;
-                    j -= 64;
+            for (int j = 0; j < kUnit; ++j) {
+                const uint64_t i = i0 + j;
+                uint32_t b = 0;
+                codes[j] = 0;
+                if (i < a.n) {
+                    b = a.x[i];
+                    const uint32_t m = lut[exp_lo(b)];
+                    codes[j] = m & 15u;
+                    f |= (m >> 4) << j;
+                    a.payload[a.off_sm + i] = (uint8_t)sm_of16(b);
                 }
-                if (lane == 0) st_agent(status + t, kFlagPrefix | (excl + tile_total));
+                wv[j >> 1] |= b << (16 * (j & 1));
             }
-            if (lane == 0) {
-                excl_slot = excl;
-                if (t == a.ntiles - 1)
-                    st_agent(reinterpret_cast<uint64_t *>(a.ws + kWsTotalEsc), excl + tile_total);
-            }
-        }
-        __syncthreads();
-
-        if (tile_total) {
-            const uint64_t excl = excl_slot;
 #pragma unroll
-            for (int u = 0; u < kEncUnits; ++u) {
-                uint32_t f = flags[u];
-                uint64_t r = excl + ubase[u] + pre[u];
-                const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
-                while (f) {
-                    const int j = __builtin_ctz(f);
-                    f &= f - 1;
-                    const uint64_t i = i0 + j;
-                    const uint32_t w = word_of(q[u], j >> 1);
-                    const uint32_t ex = (j & 1) ? exp_hi(w) : exp_lo(w);
-                    const uint64_t at = a.off_cid + 4 * r;
-                    if (at + 4 <= a.capacity)
-                        *reinterpret_cast<uint32_t *>(a.payload + at) = (uint32_t)(i / kChunk);
-                    a.stage_lpos[r] = (uint16_t)(i % kChunk);
-                    a.stage_ev[r] = (uint8_t)ex;
-                    ++r;
+            for (int k = 0; k < 4; ++k) {
+                const uint64_t i = i0 + 2 * k;
+                if (i < a.n) {
+                    const uint32_t lo = (i + 1 < a.n) ? codes[2 * k + 1] : 0u;
+                    a.payload[i / 2] = (uint8_t)((codes[2 * k] << 4) | lo);
                 }
             }
+            q[u] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+            flags[u] = f;
         }
-        ++it;
-        t = tile_slot[it & 1];
+    }
+    if (t == a.ntiles - 1 && tid == 0) {
+        // zero padding between the dense sections (page 1: the payload is
+        // assembled in a zero-filled buffer)
+        for (uint64_t b = a.n_pairs; b < a.off_sm; ++b) a.payload[b] = 0;
+        for (uint64_t b = a.off_sm + a.n; b < a.off_cid; ++b) a.payload[b] = 0;
+    }
+
+    // Escape ranks inside the tile, in element order (unit, thread, j).
+    uint32_t pre[kEncUnits];
+#pragma unroll
+    for (int u = 0; u < kEncUnits; ++u) {
+        const uint32_t c = __builtin_popcount(flags[u]);
+        const uint64_t any = __ballot(c != 0);
+        uint32_t p = 0, tot = 0;
+        if (any) {
+#pragma unroll
+            for (int bit = 0; bit < 4; ++bit) {
+                const uint64_t m = __ballot((c >> bit) & 1u);
+                p += lanes_below(m) << bit;
+                tot += (uint32_t)__popcll(m) << bit;
+            }
+        }
+        pre[u] = p;
+        if (lane == 0) wtot[u][wave] = tot;
+    }
+    __syncthreads();
+
+    uint32_t tile_total = 0;
+    uint32_t ubase[kEncUnits];
+#pragma unroll
+    for (int u = 0; u < kEncUnits; ++u) {
+        ubase[u] = tile_total;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            ubase[u] += (w < wave) ? wtot[u][w] : 0u;
+            tile_total += wtot[u][w];
+        }
+    }
+    if (tid == 0) a.tile_count[t] = tile_total;
+    if (tile_total) {
+        uint32_t *stage = a.stage + t * kEncTile;
+#pragma unroll
+        for (int u = 0; u < kEncUnits; ++u) {
+            uint32_t f = flags[u];
+            uint32_t r = ubase[u] + pre[u];
+            const uint32_t l0 = (uint32_t)u * (kThreads * kUnit) + tid * kUnit;
+            while (f) {
+                const int j = __builtin_ctz(f);
+                f &= f - 1;
+                const uint32_t w = word_of(q[u], j >> 1);
+                const uint32_t ex = (j & 1) ? exp_hi(w) : exp_lo(w);
+                stage[r++] = ((l0 + j) << 8) | ex;
+            }
+        }
     }
 }
 
@@ -471,41 +459,109 @@ struct TailArgs {
     uint8_t *payload;
     uint64_t capacity;
     splitzip_meta *meta;
-    uint8_t *ws;
-    const uint16_t *stage_lpos;
-    const uint8_t *stage_ev;
+    const uint32_t *tile_count;
+    const uint32_t *stage;
 };
 
+// Inclusive scan of one value per thread across a 256-thread workgroup.
+__device__ inline uint32_t block_scan_incl(uint32_t v, uint32_t *lds_waves) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(v, off, 64);
+        if (lane >= off) v += y;
+    }
+    if (lane == 63) lds_waves[wave] = v;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) v += lds_waves[w];
+    return v;
+}
+
+// Escape placement: every workgroup sums the tile counts before its range
+// (its first escape's rank) and over all tiles (the escape count, hence the
+// offsets of local_pos and esc_val), then writes its tiles' escapes at their
+// final ranks.  Workgroup 0 writes the padding and the metadata.
 __global__ __launch_bounds__(kThreads) void k_encode_tail(TailArgs a) {
-    const uint64_t e =
-        a.ntiles ? ld_agent(reinterpret_cast<const uint64_t *>(a.ws + kWsTotalEsc)) : 0;
-    const Layout L = layout_of(a.n, e);
-    const bool fits = L.total <= a.capacity;
-    const uint64_t g = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-    const uint64_t gs = (uint64_t)gridDim.x * kThreads;
-    if (fits && e) {
-        // local_pos: e uint16 from the staging area to off_lpos (4-aligned)
-        uint32_t *lp_dst = reinterpret_cast<uint32_t *>(a.payload + L.off_lpos);
-        const uint32_t *lp_src = reinterpret_cast<const uint32_t *>(a.stage_lpos);
-        for (uint64_t k = g; k < e / 2; k += gs) lp_dst[k] = lp_src[k];
-        uint32_t *ev_dst = reinterpret_cast<uint32_t *>(a.payload + L.off_ev);
-        const uint32_t *ev_src = reinterpret_cast<const uint32_t *>(a.stage_ev);
-        for (uint64_t k = g; k < e / 4; k += gs) ev_dst[k] = ev_src[k];
-        if (g == 0) {
-            if (e & 1) {
-                *reinterpret_cast<uint16_t *>(a.payload + L.off_lpos + 2 * (e - 1)) =
-                    a.stage_lpos[e - 1];
-                a.payload[L.off_lpos + 2 * e] = 0;       // alignment padding
-                a.payload[L.off_lpos + 2 * e + 1] = 0;
+    __shared__ uint64_t red[2][kThreads / 64];
+    __shared__ uint32_t waves[kThreads / 64];
+    __shared__ uint32_t scan[kTailTiles + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t t0 = (uint64_t)blockIdx.x * kTailTiles;
+    const uint64_t t1 = t0 + kTailTiles < a.ntiles ? t0 + kTailTiles : a.ntiles;
+
+    // counts of all tiles, 4 per load, 8 loads in flight per thread
+    uint64_t before = 0, all = 0;
+    const uint64_t nvec = a.ntiles / 4;
+    const u32x4 *cv = reinterpret_cast<const u32x4 *>(a.tile_count);
+    for (uint64_t v0 = 0; v0 < nvec; v0 += 8 * kThreads) {
+        u32x4 c4[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint64_t v = v0 + j * kThreads + tid;
+            c4[j] = v < nvec ? cv[v] : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint64_t t = 4 * (v0 + j * kThreads + tid);
+            const uint64_t s4 = (uint64_t)c4[j].x + c4[j].y + c4[j].z + c4[j].w;
+            all += s4;
+            if (t + 4 <= t0) before += s4;
+            else if (t < t0) {
+                before += c4[j].x;
+                if (t + 1 < t0) before += c4[j].y;
+                if (t + 2 < t0) before += c4[j].z;
             }
-            for (uint64_t k = e & ~uint64_t(3); k < e; ++k) a.payload[L.off_ev + k] = a.stage_ev[k];
         }
     }
-    // leave the look-back words clear for the next call
-    uint64_t *status = reinterpret_cast<uint64_t *>(a.ws + kWsStatus);
-    for (uint64_t k = g; k < a.ntiles; k += gs) status[k] = 0;
-    if (g == 0) {
-        uint32_t *guard = reinterpret_cast<uint32_t *>(a.ws + kWsGuard);
+    for (uint64_t t = 4 * nvec + tid; t < a.ntiles; t += kThreads) {
+        const uint32_t c = a.tile_count[t];
+        all += c;
+        if (t < t0) before += c;
+    }
+    before = wave_sum_u64(before);
+    all = wave_sum_u64(all);
+    if (lane == 0) {
+        red[0][wave] = before;
+        red[1][wave] = all;
+    }
+    // exclusive scan of this block's tile counts
+    const uint64_t mine_t = t0 + tid;
+    const uint32_t mine_c = mine_t < t1 ? a.tile_count[mine_t] : 0u;
+    const uint32_t incl = block_scan_incl(mine_c, waves);
+    scan[tid + 1] = incl;
+    if (tid == 0) scan[0] = 0;
+    __syncthreads();
+    uint64_t P = 0, e = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+        P += red[0][w];
+        e += red[1][w];
+    }
+    const Layout L = layout_of(a.n, e);
+    const bool fits = L.total <= a.capacity;
+    const uint32_t mine_total = scan[t1 - t0];
+
+    for (uint32_t k = tid; k < mine_total; k += kThreads) {
+        // tile j of this block holding the k-th escape: last j with scan[j] <= k
+        uint32_t lo = 0, hi = (uint32_t)(t1 - t0);
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (scan[mid] <= k) lo = mid; else hi = mid;
+        }
+        const uint64_t tile = t0 + lo;
+        const uint32_t word = a.stage[tile * kEncTile + (k - scan[lo])];
+        const uint64_t i = tile * kEncTile + (word >> 8);
+        const uint64_t r = P + k;
+        if (L.off_cid + 4 * r + 4 <= a.capacity)
+            *reinterpret_cast<uint32_t *>(a.payload + L.off_cid + 4 * r) = (uint32_t)(i / kChunk);
+        if (fits) {
+            *reinterpret_cast<uint16_t *>(a.payload + L.off_lpos + 2 * r) = (uint16_t)(i % kChunk);
+            a.payload[L.off_ev + r] = (uint8_t)(word & 0xFFu);
+        }
+    }
+    if (blockIdx.x == 0 && tid == 0) {
+        if (fits)
+            for (uint64_t b = L.off_lpos + 2 * e; b < L.off_ev; ++b) a.payload[b] = 0;
         splitzip_meta *m = a.meta;
         m->n = a.n;
         m->n_pairs = L.n_pairs;
@@ -519,11 +575,8 @@ __global__ __launch_bounds__(kThreads) void k_encode_tail(TailArgs a) {
         m->offsets[4] = L.off_ev;
         m->covered = a.cb->covered;
         m->total = a.cb->total;
-        m->status = *guard ? SPLITZIP_ERR_INTERNAL : (fits ? SPLITZIP_OK : SPLITZIP_ERR_CAPACITY);
+        m->status = fits ? SPLITZIP_OK : SPLITZIP_ERR_CAPACITY;
         m->reserved = 0;
-        *guard = 0;
-        *reinterpret_cast<uint32_t *>(a.ws + kWsTicket) = 0;
-        *reinterpret_cast<uint64_t *>(a.ws + kWsTotalEsc) = 0;
     }
 }
 
@@ -551,29 +604,140 @@ __device__ inline bool meta_ok(const DecArgs &a, Layout &L) {
            m->offsets[4] == L.off_ev && m->comp_bytes == L.total && L.total <= a.payload_bytes;
 }
 
-__global__ __launch_bounds__(kThreads) void k_decode_dense(DecArgs a) {
-    __shared__ uint32_t pair_lut[256];   // pk byte -> (even exponent, odd exponent)
+// First r in [lo, hi) with cid[r] >= key (hi when none), for chunk ids sorted
+// on [lo, hi); one wave.  A 64-entry window at the interpolated guess settles
+// most searches with one load; otherwise a 64-ary search narrows the range.
+__device__ inline uint64_t lower_bound_wave(const int32_t *cid, uint64_t lo, uint64_t hi,
+                                            int64_t key, uint64_t guess, int lane) {
+    if (hi > lo + 64) {
+        uint64_t wlo = guess > 32 ? guess - 32 : 0;
+        if (wlo < lo) wlo = lo;
+        if (wlo > hi - 64) wlo = hi - 64;
+        const int64_t v = cid[wlo + lane];
+        const uint64_t below = __ballot(v < key);
+        const uint32_t k = __popcll(below);
+        const bool left_ok = (wlo == lo) || (below & 1ull);
+        if (left_ok && k < 64) return wlo + k;
+        if (!left_ok) hi = wlo;              // answer in [lo, wlo]
+        else lo = wlo + 64;                  // whole window below the key
+    }
+    while (hi > lo + 63) {
+        const uint64_t span = hi - lo;
+        const uint64_t s = lo + (span * (uint64_t)(lane + 1)) / 65;
+        const int64_t v = cid[s];
+        const uint32_t k = __popcll(__ballot(v < key));
+        const uint64_t s_lo = __shfl(s, k > 0 ? (int)k - 1 : 0, 64);
+        const uint64_t s_hi = __shfl(s, k < 64 ? (int)k : 63, 64);
+        const uint64_t nlo = k > 0 ? s_lo + 1 : lo;
+        const uint64_t nhi = k < 64 ? s_hi : hi;
+        lo = nlo;
+        hi = nhi;
+    }
+    const uint64_t p = lo + lane;
+    const int64_t v = p < hi ? (int64_t)cid[p] : INT64_MAX;
+    return lo + __popcll(__ballot(v < key));
+}
+
+__global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
+    __shared__ uint32_t pair_lut[256];      // pk byte -> (even exponent, odd exponent << 16)
+    __shared__ uint32_t esc_list[kRegisterPatchMax];
+    __shared__ uint64_t range[2];
     Layout L;
     if (!meta_ok(a, L)) {
         if (blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
         return;
     }
     const int tid = threadIdx.x;
-    pair_lut[tid] = (uint32_t)a.dec_lut[tid >> 4] | ((uint32_t)a.dec_lut[tid & 15] << 16);
-    __syncthreads();
-
+    const int lane = tid & 63;
+    const uint64_t e = a.meta->n_esc;
     const uint64_t base = (uint64_t)blockIdx.x * kDecTile;
+    const bool full = base + kDecTile <= a.n;
     const uint8_t *pk = a.payload;
     const uint8_t *sm = a.payload + L.off_sm;
-    if (base + kDecTile <= a.n) {
-        uint32_t pkw[kDecUnits];
-        u32x2 smw[kDecUnits];
+    const int32_t *cid = reinterpret_cast<const int32_t *>(a.payload + L.off_cid);
+    const uint16_t *lpos = reinterpret_cast<const uint16_t *>(a.payload + L.off_lpos);
+    const uint8_t *ev = a.payload + L.off_ev;
+
+    uint32_t pkw[kDecUnits];
+    u32x2 smw[kDecUnits];
+    if (full) {
 #pragma unroll
         for (int u = 0; u < kDecUnits; ++u) {
             const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
             pkw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(pk + i0 / 2));
             smw[u] = *reinterpret_cast<const u32x2_a4 *>(sm + i0);
         }
+    }
+    pair_lut[tid] = (uint32_t)a.dec_lut[tid >> 4] | ((uint32_t)a.dec_lut[tid & 15] << 16);
+    if (tid < 64) {
+        // escapes of chunks [c0, c1): the tile's range of the sorted stream
+        uint64_t r0 = 0, r1 = 0;
+        if (e) {
+            const uint64_t nchunks = (a.n + kChunk - 1) / kChunk;
+            const uint64_t c0 = base / kChunk, c1 = c0 + kDecTile / kChunk;
+            r0 = lower_bound_wave(cid, 0, e, (int64_t)c0, (e * c0) / nchunks, lane);
+            r1 = lower_bound_wave(cid, r0, e, (int64_t)c1, r0 + (e * (c1 - c0)) / nchunks, lane);
+        }
+        if (lane == 0) {
+            range[0] = r0;
+            range[1] = r1;
+        }
+    }
+    __syncthreads();
+    const uint64_t r0 = range[0], r1 = range[1];
+    const uint64_t c = r1 - r0;
+
+    if (full && c <= kRegisterPatchMax) {
+        if (tid < c) {
+            // local index in the tile, or all ones when the entry is unusable
+            const uint64_t r = r0 + tid;
+            const int64_t idx = (int64_t)cid[r] * kChunk + lpos[r];
+            const bool inside = idx >= (int64_t)base && idx < (int64_t)(base + kDecTile);
+            esc_list[tid] = inside ? ((uint32_t)(idx - base) | ((uint32_t)ev[r] << 16)) : ~0u;
+        }
+        __syncthreads();
+        u32x4 o[kDecUnits];
+#pragma unroll
+        for (int u = 0; u < kDecUnits; ++u) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t ee = pair_lut[(pkw[u] >> (8 * k)) & 0xFFu];
+                const uint32_t s = smw[u][k >> 1] >> (16 * (k & 1));
+                o[u][k] = join16(s & 0xFFu, ee & 0xFFu) | (join16((s >> 8) & 0xFFu, ee >> 16) << 16);
+            }
+        }
+        for (uint32_t k = 0; k < c; ++k) {
+            const uint32_t entry = esc_list[k];
+            if (entry == ~0u) continue;
+            const uint32_t loc = entry & 0xFFFFu;
+            if (((loc >> 3) & (kThreads - 1)) != (uint32_t)tid) continue;
+            const uint32_t j = loc & 7u;
+            const uint32_t ex = entry >> 16;
+#pragma unroll
+            for (int u = 0; u < kDecUnits; ++u) {
+                if ((loc >> 11) != (uint32_t)u) continue;
+                const uint32_t sw = (j < 4) ? smw[u][0] : smw[u][1];
+                const uint32_t s = (sw >> (8 * (j & 3))) & 0xFFu;
+                const uint32_t val = join16(s, ex);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    if ((uint32_t)w != (j >> 1)) continue;
+                    o[u][w] = (j & 1) ? ((o[u][w] & 0xFFFFu) | (val << 16))
+                                      : ((o[u][w] & 0xFFFF0000u) | val);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kDecUnits; ++u) {
+            const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+            __builtin_nontemporal_store(o[u], reinterpret_cast<u32x4 *>(a.out + i0));
+        }
+        return;
+    }
+
+    // Many escapes, or the last partial tile: dense stores, then a scatter of
+    // the tile's escapes after the workgroup barrier.
+    if (full) {
 #pragma unroll
         for (int u = 0; u < kDecUnits; ++u) {
             const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
@@ -584,36 +748,43 @@ __global__ __launch_bounds__(kThreads) void k_decode_dense(DecArgs a) {
                 const uint32_t s = smw[u][k >> 1] >> (16 * (k & 1));
                 o[k] = join16(s & 0xFFu, ee & 0xFFu) | (join16((s >> 8) & 0xFFu, ee >> 16) << 16);
             }
-            __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(a.out + i0));
+            *reinterpret_cast<u32x4 *>(a.out + i0) = o;
         }
     } else {
-        for (uint64_t i = base + tid; i < a.n && i < base + kDecTile; i += kThreads) {
+        for (uint64_t i = base + tid; i < a.n; i += kThreads) {
             const uint32_t byte = pk[i / 2];
             const uint32_t code = (i & 1) ? (byte & 15u) : (byte >> 4);
             a.out[i] = (uint16_t)join16(sm[i], a.dec_lut[code]);
         }
     }
+    __syncthreads();
+    for (uint64_t r = r0 + tid; r < r1; r += kThreads) {
+        const int64_t idx = (int64_t)cid[r] * kChunk + lpos[r];
+        if (idx >= (int64_t)base && idx < (int64_t)(base + kDecTile) && idx < (int64_t)a.n)
+            a.out[idx] = (uint16_t)join16(sm[idx], ev[r]);
+    }
 }
 
-__global__ __launch_bounds__(kThreads) void k_decode_patch(DecArgs a) {
+// Validation (and order-independent re-application) of every escape.
+__global__ __launch_bounds__(kThreads) void k_decode_check(DecArgs a) {
     Layout L;
-    if (!meta_ok(a, L)) return;   // reported by k_decode_dense
+    if (!meta_ok(a, L)) return;   // reported by k_decode
     const uint64_t e = a.meta->n_esc;
     const uint8_t *sm = a.payload + L.off_sm;
-    const uint8_t *cid_b = a.payload + L.off_cid;
+    const int32_t *cid = reinterpret_cast<const int32_t *>(a.payload + L.off_cid);
     const uint16_t *lpos = reinterpret_cast<const uint16_t *>(a.payload + L.off_lpos);
     const uint8_t *ev = a.payload + L.off_ev;
     const uint64_t gs = (uint64_t)gridDim.x * kThreads;
     int32_t bad = 0;
     for (uint64_t r = (uint64_t)blockIdx.x * kThreads + threadIdx.x; r < e; r += gs) {
-        const int32_t cid = *reinterpret_cast<const int32_t *>(cid_b + 4 * r);
+        const int32_t c = cid[r];
         const uint32_t pos = lpos[r];
-        if (cid < 0) { bad |= 2; continue; }
+        if (c < 0) { bad |= 2; continue; }
         if (pos >= kChunk) bad |= 4;
-        const uint64_t idx = (uint64_t)cid * kChunk + pos;
+        const uint64_t idx = (uint64_t)c * kChunk + pos;
         if (idx >= a.n) { bad |= 2; continue; }
         if (r > 0) {
-            const int32_t pc = *reinterpret_cast<const int32_t *>(cid_b + 4 * (r - 1));
+            const int32_t pc = cid[r - 1];
             const uint64_t prev = (uint64_t)(uint32_t)pc * kChunk + lpos[r - 1];
             if (pc < 0 || prev >= idx) bad |= 8;
         }
@@ -634,23 +805,17 @@ __global__ void k_fill_zero(uint32_t *p, uint64_t words) {
 
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices];
-int g_enc_blocks_per_cu[kMaxDevices];
 
-bool device_info(int &cus, int &enc_occ) {
+bool cu_count(int &cus) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
     if (g_cu_count[dev] == 0) {
-        int c = 0, occ = 0;
+        int c = 0;
         if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return false;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_encode, kThreads, 0) !=
-            hipSuccess)
-            return false;
-        g_enc_blocks_per_cu[dev] = occ > 0 ? occ : 1;
         g_cu_count[dev] = c > 0 ? c : 1;
     }
     cus = g_cu_count[dev];
-    enc_occ = g_enc_blocks_per_cu[dev];
     return true;
 }
 
@@ -681,7 +846,7 @@ const char *splitzip_status_string(int status) {
         case SPLITZIP_ERR_CORRUPT: return "corrupt payload or metadata";
         case SPLITZIP_ERR_HIP: return "HIP runtime error";
         case SPLITZIP_ERR_WORKSPACE: return "workspace too small";
-        case SPLITZIP_ERR_INTERNAL: return "device progress guard tripped";
+        case SPLITZIP_ERR_INTERNAL: return "internal error";
         default: return "unknown status";
     }
 }
@@ -692,16 +857,14 @@ size_t splitzip_workspace_size(uint64_t n) {
     uint64_t t = enc_tiles(n);
     if (t == 0) t = 1;
     // smallest size whose plan holds t tiles
-    return (size_t)(kWsStatus + kWsSlack + t * (8 + 3 * (uint64_t)kEncTile));
+    return (size_t)(kWsTiles + kWsSlack + t * (4 + 4 * (uint64_t)kEncTile));
 }
 
 int splitzip_workspace_init(void *d_ws, size_t ws_bytes, void *stream) {
     if (!d_ws || !aligned(d_ws, 16) || ws_bytes < splitzip_workspace_size(0))
         return SPLITZIP_ERR_INVALID;
-    const WsPlan P = ws_plan(ws_bytes);
-    const uint64_t words = (kWsStatus + 8 * P.t_max) / 4;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    k_fill_zero<<<256, 256, 0, s>>>(reinterpret_cast<uint32_t *>(d_ws), words);
+    k_fill_zero<<<64, 256, 0, s>>>(reinterpret_cast<uint32_t *>(d_ws), kWsTiles / 4);
     return launched();
 }
 
@@ -711,11 +874,12 @@ int splitzip_calibrate(const uint16_t *d_x, uint64_t n, splitzip_codebook *d_cb,
         !d_ws || !aligned(d_ws, 16))
         return SPLITZIP_ERR_INVALID;
     if (ws_bytes < splitzip_workspace_size(0)) return SPLITZIP_ERR_WORKSPACE;
-    int cus = 0, occ = 0;
-    if (!device_info(cus, occ)) return SPLITZIP_ERR_HIP;
+    int cus = 0;
+    if (!cu_count(cus)) return SPLITZIP_ERR_HIP;
     const uint64_t nvec = n >> 3;
     uint64_t grid = (nvec + 4 * kCalThreads - 1) / (4 * kCalThreads);
-    const uint64_t cap = 2 * (uint64_t)cus;
+    uint64_t cap = 2 * (uint64_t)cus;
+    if (cap > kCalMaxGrid) cap = kCalMaxGrid;
     if (grid > cap) grid = cap;
     if (grid == 0) grid = 1;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -736,24 +900,18 @@ int splitzip_encode(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_
     const uint64_t ntiles = enc_tiles(n);
     const WsPlan P = ws_plan(ws_bytes);
     if (ws_bytes < splitzip_workspace_size(n) || P.t_max < ntiles) return SPLITZIP_ERR_WORKSPACE;
-    int cus = 0, occ = 0;
-    if (!device_info(cus, occ)) return SPLITZIP_ERR_HIP;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     uint8_t *ws = reinterpret_cast<uint8_t *>(d_ws);
-    uint16_t *stage_lpos = reinterpret_cast<uint16_t *>(ws + P.off_lpos);
-    uint8_t *stage_ev = ws + P.off_ev;
+    uint32_t *counts = reinterpret_cast<uint32_t *>(ws + P.off_count);
+    uint32_t *stage = reinterpret_cast<uint32_t *>(ws + P.off_stage);
     if (ntiles) {
-        EncArgs a{d_x,      n,        ntiles,    d_cb, d_payload, capacity, L0.n_pairs,
-                  L0.off_sm, L0.off_cid, ws,      stage_lpos, stage_ev};
-        uint64_t grid = (uint64_t)cus * occ;
-        if (grid > ntiles) grid = ntiles;
-        k_encode<<<(unsigned)grid, kThreads, 0, s>>>(a);
+        EncArgs a{d_x, n, ntiles, d_cb, d_payload, L0.n_pairs, L0.off_sm, L0.off_cid, counts, stage};
+        k_encode<<<(unsigned)ntiles, kThreads, 0, s>>>(a);
         if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     }
-    TailArgs t{n, ntiles, d_cb, d_payload, capacity, d_meta, ws, stage_lpos, stage_ev};
-    uint64_t tgrid = (ntiles + 7) / 8;
-    if (tgrid > 512) tgrid = 512;
+    uint64_t tgrid = (ntiles + kTailTiles - 1) / kTailTiles;
     if (tgrid == 0) tgrid = 1;
+    TailArgs t{n, ntiles, d_cb, d_payload, capacity, d_meta, counts, stage};
     k_encode_tail<<<(unsigned)tgrid, kThreads, 0, s>>>(t);
     return launched();
 }
@@ -769,11 +927,13 @@ int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const spli
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     DecArgs a{d_payload, payload_bytes, d_meta, d_dec_lut, d_out, n, d_status};
     const uint64_t grid = (n + kDecTile - 1) / kDecTile;
-    k_decode_dense<<<(unsigned)grid, kThreads, 0, s>>>(a);
+    k_decode<<<(unsigned)grid, kThreads, 0, s>>>(a);
     if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
-    uint64_t pgrid = (n + 16 * kThreads - 1) / (16 * kThreads);
-    if (pgrid > 1024) pgrid = 1024;
-    k_decode_patch<<<(unsigned)pgrid, kThreads, 0, s>>>(a);
+    if (d_status) {
+        uint64_t cgrid = (n + 16 * kThreads - 1) / (16 * kThreads);
+        if (cgrid > 1024) cgrid = 1024;
+        k_decode_check<<<(unsigned)cgrid, kThreads, 0, s>>>(a);
+    }
     return launched();
 }
 

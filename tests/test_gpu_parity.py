@@ -58,14 +58,16 @@ def gpu_run(x_cpu, cb_source=None, ws=None):
     src = x if cb_source is None else cb_source.reshape(-1).to(DEV)
     cb = S.calibrate(src, ws)
     payload, meta = S.encode(x, cb, ws)
+    # decode twice: the plain fused path (no status word) and the validating one
+    out_fast = S.decode(payload, meta, cb, n)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
     out = S.decode(payload, meta, cb, n, status=status)
     torch.cuda.synchronize()
     m = S.read_meta(meta)
     c = S.read_codebook(cb)
     pay = payload[: m.comp_bytes].cpu().numpy().tobytes()
-    return dict(cb=c, meta=m, payload=pay, out=host_bits(out), status=int(status.item()),
-                cb_dev=cb, payload_dev=payload, meta_dev=meta)
+    return dict(cb=c, meta=m, payload=pay, out=host_bits(out), out_fast=host_bits(out_fast),
+                status=int(status.item()), cb_dev=cb, payload_dev=payload, meta_dev=meta)
 
 
 def check_codebook(c, ocb):
@@ -95,16 +97,16 @@ def meta_to_device(om) -> torch.Tensor:
     return torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(DEV)
 
 
-def gpu_decode_bytes(payload: bytes, om, dec_lut) -> tuple:
+def gpu_decode_bytes(payload: bytes, om, dec_lut, validate=True) -> tuple:
     pay = torch.frombuffer(bytearray(payload + b"\0" * 16), dtype=torch.uint8).to(DEV)
     meta = meta_to_device(om)
     lut = torch.tensor(np.asarray(dec_lut, np.uint8)).to(DEV)
-    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV) if validate else None
     out = torch.empty(om.n, dtype=torch.bfloat16, device=DEV)
     if om.n:
         S.decode(pay[: len(payload)], meta, lut, om.n, out=out, status=status)
     torch.cuda.synchronize()
-    return host_bits(out), int(status.item())
+    return host_bits(out), (int(status.item()) if validate else 0)
 
 
 def full_parity(x_cpu, cb_source=None, name=""):
@@ -124,10 +126,13 @@ def full_parity(x_cpu, cb_source=None, name=""):
                              % (bad.size, bad[0], om.offsets))
     assert g["status"] == 0
     assert np.array_equal(g["out"], xs)
+    assert np.array_equal(g["out_fast"], xs)
     # cross-decoding: oracle decodes the GPU payload, the GPU decodes the oracle's
     assert np.array_equal(oracle.decode(g["payload"], om, ocb.dec_lut), xs)
     out2, st2 = gpu_decode_bytes(opay, om, ocb.dec_lut)
     assert st2 == 0 and np.array_equal(out2, xs)
+    out3, _ = gpu_decode_bytes(opay, om, ocb.dec_lut, validate=False)
+    assert np.array_equal(out3, xs)
     return g, om
 
 
@@ -262,6 +267,45 @@ def test_decode_flags_corrupt_streams():
     assert st & _abi.DEC_BAD_META
     _, st = gpu_decode_bytes(opay, om, ocb.dec_lut)
     assert st == 0
+
+
+def test_unsorted_escape_stream_with_validation():
+    """A stream whose escapes are not in ascending order is flagged, and the
+    validating decode (which re-applies every escape by scatter) still
+    reproduces the tensor."""
+    n = 3 * 8192 + 77
+    x = torch.full((n,), 1.0, dtype=torch.bfloat16)
+    pos = [3, 900, 5000, 8191, 8192, 9000, 17000, 24000, n - 1]
+    x[pos] = torch.tensor([2.0, -4.0, 8.0, 0.5, 16.0, -0.25, 3.0, 64.0, -2.0],
+                          dtype=torch.bfloat16)
+    xs = host_bits(x)
+    ocb = oracle.calibrate(np.array([0x3F80], np.uint16))
+    opay, om = oracle.encode(xs, ocb)
+    e = om.n_esc
+    assert e == len(pos)
+    buf = bytearray(opay)
+    order = list(range(e))[::-1]          # reverse the escape stream
+    for sec, width in ((2, 4), (3, 2), (4, 1)):
+        at = om.offsets[sec]
+        items = [bytes(buf[at + width * r: at + width * (r + 1)]) for r in range(e)]
+        for k, r in enumerate(order):
+            buf[at + width * k: at + width * (k + 1)] = items[r]
+    out, st = gpu_decode_bytes(bytes(buf), om, ocb.dec_lut)
+    assert st & _abi.DEC_NOT_INCREASING
+    assert np.array_equal(out, xs)
+
+
+@pytest.mark.parametrize("tiles", [255, 256, 257, 513])
+def test_escape_placement_across_tail_blocks(tiles):
+    """Escapes spread over more tiles than one placement block handles."""
+    n = tiles * 4096 - 5
+    full_parity(W.log_uniform_stress(n, seed=30 + tiles), name="tail blocks %d" % tiles)
+
+
+@pytest.mark.parametrize("n", [300 * 4096 * 8 - 3, 8 * 4096 * 1024 - 8, 17 * 4096 * 8 + 5])
+def test_calibrate_grid_edges(n):
+    """Calibrate grids of a full 512 workgroups with an uneven last group."""
+    full_parity(W.gaussian_weight(n, seed=40), name="calibrate grid")
 
 
 def test_argument_errors():
