@@ -9,28 +9,31 @@
 // by ascending exponent value.
 //
 // All work is integer and streams through HBM; nothing is a contraction, so
-// no matrix cores.  Device-scope atomics on one address serialise (about
-// 12 ns each on this part), so no kernel takes a global ticket or bumps a
-// shared counter per workgroup:
+// no matrix cores.  Two measured properties of this part shape the kernels:
+// device-scope atomics on one address serialise (about 12 ns each), and an
+// agent-scope fence (L2 write-back + invalidate) issued by every workgroup
+// costs tens of microseconds.  So no kernel takes a global ticket, keeps a
+// per-workgroup counter on one address or issues a device fence:
 //   k_calibrate   exponent histogram in LDS (64 lane-private copies, so equal
-//                 exponents in a wave never hit one bank), per-workgroup
-//                 partials written with plain stores, merged by the last
-//                 arriver of each group of 16 workgroups and then by the last
-//                 group (counters on separate cache lines), which also runs
-//                 the top-16 select.
-//   k_encode      one 4096-element tile per workgroup: 16-byte loads, code
+//                 exponents in a wave never hit one bank), merged with device
+//                 atomics into 16 spread copies; the last arriver of each group
+//                 of 16 workgroups reports to a top counter and the last group
+//                 folds the copies and runs the top-16 select.
+//   k_encode      one 8192-element tile per workgroup: 16-byte loads, code
 //                 table in LDS, nibble packing, sign/mantissa bytes, wave
-//                 ballots to rank escapes, decoupled look-back over tiles in
-//                 launch order.  A tile whose predecessor has published
-//                 nothing after a short wait counts that predecessor's escapes
-//                 itself, so progress never depends on the dispatch order.
-//   k_encode_tail moves staged positions / raw exponents behind the chunk ids
-//                 once the escape count is known, writes the metadata and
-//                 leaves the workspace clean for the next call.
-//   k_decode      one 8192-element tile per workgroup: pk + sm -> bf16 through
-//                 a 256-entry pair table in LDS, with the tile's escapes found
-//                 by a wave-wide search of the sorted chunk ids and patched
-//                 before (few) or after (many) the 16-byte stores.
+//                 ballots to rank the tile's escapes, which are staged in the
+//                 workspace with the tile's escape count.  Tiles never talk
+//                 to each other.
+//   k_encode_tail scans the tile counts (every workgroup sums the counts it
+//                 needs) and writes chunk id, chunk-local position and raw
+//                 exponent of every escape at its final rank, then the padding
+//                 and the metadata.
+//   k_decode      one tile of 8192, 16384 or 32768 elements per workgroup (the
+//                 widest that still gives each CU four workgroups): pk + sm ->
+//                 bf16 through a 256-entry pair table in LDS, with the tile's
+//                 escapes found by a wave-wide search of the sorted chunk ids
+//                 and patched in registers (few) or by scatter after the
+//                 16-byte stores (many).
 //   k_decode_check  (only when a status word is requested) validates every
 //                 escape and re-applies it by scatter, which also makes the
 //                 decode correct for escape streams that are not sorted.
@@ -46,10 +49,12 @@ namespace {
 constexpr uint32_t kChunk = SPLITZIP_CHUNK;
 constexpr int kThreads = 256;                 // encode / decode workgroup
 constexpr int kUnit = 8;                      // elements per 16-byte load
-constexpr int kEncUnits = 2;                  // units per thread per tile
-constexpr int kEncTile = kThreads * kUnit * kEncUnits;   // 4096 elements
-constexpr int kDecUnits = 4;
-constexpr int kDecTile = kThreads * kUnit * kDecUnits;   // 8192 elements
+#ifndef SPLITZIP_ENC_UNITS
+#define SPLITZIP_ENC_UNITS 4
+#endif
+constexpr int kEncUnits = SPLITZIP_ENC_UNITS; // units per thread per tile
+constexpr int kEncTile = kThreads * kUnit * kEncUnits;   // 8192 elements
+// decode tiles of 2048 * U elements, U in {4, 8, 16} chosen from n (below)
 constexpr int kCalThreads = 1024;
 constexpr int kCalMaxGrid = 512;              // two 1024-thread workgroups per CU
 constexpr int kCalGroup = 16;                 // arrivals per first-level counter
@@ -489,6 +494,9 @@ __global__ __launch_bounds__(kThreads) void k_encode_tail(TailArgs a) {
     const uint64_t t0 = (uint64_t)blockIdx.x * kTailTiles;
     const uint64_t t1 = t0 + kTailTiles < a.ntiles ? t0 + kTailTiles : a.ntiles;
 
+    // this block's own tile counts (issued first, used after the sweep)
+    const uint64_t mine_t = t0 + tid;
+    const uint32_t mine_c = mine_t < t1 ? a.tile_count[mine_t] : 0u;
     // counts of all tiles, 4 per load, 8 loads in flight per thread
     uint64_t before = 0, all = 0;
     const uint64_t nvec = a.ntiles / 4;
@@ -525,8 +533,6 @@ __global__ __launch_bounds__(kThreads) void k_encode_tail(TailArgs a) {
         red[1][wave] = all;
     }
     // exclusive scan of this block's tile counts
-    const uint64_t mine_t = t0 + tid;
-    const uint32_t mine_c = mine_t < t1 ? a.tile_count[mine_t] : 0u;
     const uint32_t incl = block_scan_incl(mine_c, waves);
     scan[tid + 1] = incl;
     if (tid == 0) scan[0] = 0;
@@ -638,7 +644,9 @@ __device__ inline uint64_t lower_bound_wave(const int32_t *cid, uint64_t lo, uin
     return lo + __popcll(__ballot(v < key));
 }
 
+template <int kDecUnits>
 __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
+    constexpr int kDecTile = kThreads * kUnit * kDecUnits;
     __shared__ uint32_t pair_lut[256];      // pk byte -> (even exponent, odd exponent << 16)
     __shared__ uint32_t esc_list[kRegisterPatchMax];
     __shared__ uint64_t range[2];
@@ -665,7 +673,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
         for (int u = 0; u < kDecUnits; ++u) {
             const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
             pkw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(pk + i0 / 2));
-            smw[u] = *reinterpret_cast<const u32x2_a4 *>(sm + i0);
+            smw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4 *>(sm + i0));
         }
     }
     pair_lut[tid] = (uint32_t)a.dec_lut[tid >> 4] | ((uint32_t)a.dec_lut[tid & 15] << 16);
@@ -730,7 +738,8 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
 #pragma unroll
         for (int u = 0; u < kDecUnits; ++u) {
             const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
-            __builtin_nontemporal_store(o[u], reinterpret_cast<u32x4 *>(a.out + i0));
+            // plain stores: measured faster than non-temporal ones for this stream
+            *reinterpret_cast<u32x4 *>(a.out + i0) = o[u];
         }
         return;
     }
@@ -926,8 +935,18 @@ int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const spli
     if (n == 0) return SPLITZIP_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     DecArgs a{d_payload, payload_bytes, d_meta, d_dec_lut, d_out, n, d_status};
-    const uint64_t grid = (n + kDecTile - 1) / kDecTile;
-    k_decode<<<(unsigned)grid, kThreads, 0, s>>>(a);
+    // Wider tiles keep more bytes in flight per wave; use the widest that
+    // still gives every CU four workgroups.
+    int cus = 0;
+    if (!cu_count(cus)) return SPLITZIP_ERR_HIP;
+    const uint64_t want = 4 * (uint64_t)cus;
+    const uint64_t t16 = (n + 16 * 2048 - 1) / (16 * 2048), t8 = (n + 8 * 2048 - 1) / (8 * 2048);
+    if (t16 >= want)
+        k_decode<16><<<(unsigned)t16, kThreads, 0, s>>>(a);
+    else if (t8 >= want)
+        k_decode<8><<<(unsigned)t8, kThreads, 0, s>>>(a);
+    else
+        k_decode<4><<<(unsigned)((n + 4 * 2048 - 1) / (4 * 2048)), kThreads, 0, s>>>(a);
     if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     if (d_status) {
         uint64_t cgrid = (n + 16 * kThreads - 1) / (16 * kThreads);
