@@ -89,6 +89,22 @@ typedef struct splitzip_meta {
     uint32_t reserved;
 } splitzip_meta;
 
+/* One tensor of a batched call.  The array of items lives in host memory;
+ * the pointers in it are device pointers.  Each batched call reads only the
+ * fields it needs:
+ *   calibrate  x, n -> cb
+ *   encode     x, n, cb, payload, capacity -> payload, meta
+ *   decode     payload, capacity (readable bytes), meta, cb (its dec_lut), n -> out */
+typedef struct splitzip_item {
+    const uint16_t *x;     /* n BF16 values as uint16 bit patterns (16-byte aligned) */
+    uint64_t n;            /* elements                                               */
+    splitzip_codebook *cb; /* codebook of this tensor                                */
+    uint8_t *payload;      /* payload buffer (16-byte aligned)                       */
+    uint64_t capacity;     /* bytes of the payload buffer                            */
+    splitzip_meta *meta;   /* metadata of the payload                                */
+    uint16_t *out;         /* decoded output (16-byte aligned)                       */
+} splitzip_item;
+
 /* ABI version of the loaded library (SPLITZIP_ABI_VERSION). */
 int splitzip_abi_version(void);
 
@@ -107,6 +123,11 @@ uint64_t splitzip_payload_size(uint64_t n, uint64_t n_esc);
  * to n elements (host function).  A workspace of S bytes serves every n with
  * splitzip_workspace_size(n) <= S. */
 size_t splitzip_workspace_size(uint64_t n);
+
+/* Bytes of workspace needed by the batched calls on `count` tensors of the
+ * given element counts (host array); also enough for any single call on one
+ * of them. */
+size_t splitzip_workspace_size_batch(const uint64_t *n, uint32_t count);
 
 /* Prepare a workspace for first use (enqueues a zero-fill kernel).  The
  * library keeps it consistent afterwards; one workspace must not be used by
@@ -162,6 +183,22 @@ int splitzip_encode(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_
 int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const splitzip_meta *d_meta,
                     const uint8_t *d_dec_lut, uint16_t *d_out, uint64_t n, int32_t *d_status,
                     void *stream);
+
+/* Batched forms of calibrate / encode / decode for many tensors with one
+ * codebook each (the per-tensor granularity of page 1, SplitZipCodebook):
+ * the same computation as calling the single-tensor function on every item
+ * in order, with the tensors of up to 32 consecutive items sharing each
+ * kernel launch.  `items` is a host array of `count` entries, read before the
+ * call returns.  Error codes as for the single-tensor calls; on an argument
+ * error nothing is enqueued.  Encode needs a workspace of at least
+ * splitzip_workspace_size_batch(n, count) bytes.  For decode, d_status (may
+ * be NULL) collects the status bits of all items. */
+int splitzip_calibrate_batch(const splitzip_item *items, uint32_t count, void *d_ws,
+                             size_t ws_bytes, void *stream);
+int splitzip_encode_batch(const splitzip_item *items, uint32_t count, void *d_ws,
+                          size_t ws_bytes, void *stream);
+int splitzip_decode_batch(const splitzip_item *items, uint32_t count, int32_t *d_status,
+                          void *stream);
 
 #ifdef __cplusplus
 }

@@ -10,8 +10,8 @@ The method: page "splitzip_codec.py -- SplitZip codec adapter for
 diffusers-dynamic-offloader" and page "SplitZip in DDO -- VMM routes".
 """
 from ._abi import CHUNK, Codebook, Meta, SplitZipError, lib  # noqa: F401
-from .codec import (Workspace, calibrate, decode, encode, payload_size,  # noqa: F401
+from .codec import (Batch, Workspace, calibrate, decode, encode, payload_size,  # noqa: F401
                     read_codebook, read_meta)
 
-__all__ = ["CHUNK", "Codebook", "Meta", "SplitZipError", "Workspace", "calibrate", "encode",
+__all__ = ["CHUNK", "Batch", "Codebook", "Meta", "SplitZipError", "Workspace", "calibrate", "encode",
            "decode", "payload_size", "read_codebook", "read_meta", "lib"]

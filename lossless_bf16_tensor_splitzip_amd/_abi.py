@@ -61,6 +61,19 @@ class Meta(ctypes.Structure):
     ]
 
 
+class Item(ctypes.Structure):
+    """Mirror of splitzip_item (one tensor of a batched call; device pointers)."""
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("n", ctypes.c_uint64),
+        ("cb", ctypes.c_void_p),
+        ("payload", ctypes.c_void_p),
+        ("capacity", ctypes.c_uint64),
+        ("meta", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+    ]
+
+
 DEC_LUT_OFFSET = Codebook.dec_lut.offset
 
 # name -> (restype, argtypes), exactly the functions of include/splitzip.h
@@ -77,6 +90,10 @@ SIGNATURES = {
     "splitzip_calibrate": (ctypes.c_int, [_P, _U64, _P, _P, _SZ, _P]),
     "splitzip_encode": (ctypes.c_int, [_P, _U64, _P, _P, _U64, _P, _P, _SZ, _P]),
     "splitzip_decode": (ctypes.c_int, [_P, _U64, _P, _P, _P, _U64, _P, _P]),
+    "splitzip_workspace_size_batch": (_SZ, [ctypes.POINTER(ctypes.c_uint64), ctypes.c_uint32]),
+    "splitzip_calibrate_batch": (ctypes.c_int, [_P, ctypes.c_uint32, _P, _SZ, _P]),
+    "splitzip_encode_batch": (ctypes.c_int, [_P, ctypes.c_uint32, _P, _SZ, _P]),
+    "splitzip_decode_batch": (ctypes.c_int, [_P, ctypes.c_uint32, _P, _P]),
 }
 
 _lib = None
@@ -151,3 +168,24 @@ def splitzip_decode(d_payload: int, payload_bytes: int, d_meta: int, d_dec_lut: 
                     n: int, d_status: int, stream: int) -> int:
     return lib().splitzip_decode(d_payload, payload_bytes, d_meta, d_dec_lut, d_out, n, d_status,
                                  stream)
+
+
+def splitzip_workspace_size_batch(ns) -> int:
+    arr = (ctypes.c_uint64 * max(len(ns), 1))(*ns)
+    return lib().splitzip_workspace_size_batch(arr, len(ns))
+
+
+def _items_ptr(items):
+    return ctypes.cast(items, ctypes.c_void_p) if items is not None else None
+
+
+def splitzip_calibrate_batch(items, count: int, d_ws: int, ws_bytes: int, stream: int) -> int:
+    return lib().splitzip_calibrate_batch(_items_ptr(items), count, d_ws, ws_bytes, stream)
+
+
+def splitzip_encode_batch(items, count: int, d_ws: int, ws_bytes: int, stream: int) -> int:
+    return lib().splitzip_encode_batch(_items_ptr(items), count, d_ws, ws_bytes, stream)
+
+
+def splitzip_decode_batch(items, count: int, d_status: int, stream: int) -> int:
+    return lib().splitzip_decode_batch(_items_ptr(items), count, d_status, stream)

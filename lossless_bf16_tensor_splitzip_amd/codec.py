@@ -8,7 +8,7 @@ import ctypes
 import torch
 
 from . import _abi
-from ._abi import CHUNK, Codebook, Meta, SplitZipError
+from ._abi import CHUNK, Codebook, Item, Meta, SplitZipError
 
 CODEBOOK_BYTES = ctypes.sizeof(Codebook)
 META_BYTES = ctypes.sizeof(Meta)
@@ -37,12 +37,15 @@ def payload_size(n: int, n_esc: int) -> int:
 
 class Workspace:
     """Device scratch for calibrate / encode, sized for tensors of up to n_max
-    elements.  One workspace per stream that runs codec calls concurrently."""
+    elements (or, with ``batch_ns``, for batched calls on tensors of those
+    sizes).  One workspace per stream that runs codec calls concurrently."""
 
-    def __init__(self, n_max: int, device=None, stream=None):
+    def __init__(self, n_max: int = 0, device=None, stream=None, batch_ns=None):
         device = torch.device(device if device is not None else "cuda")
         self.n_max = n_max
         self.nbytes = _abi.splitzip_workspace_size(n_max)
+        if batch_ns is not None:
+            self.nbytes = max(self.nbytes, _abi.splitzip_workspace_size_batch(list(batch_ns)))
         self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
         _abi._check("splitzip_workspace_init",
                     _abi.splitzip_workspace_init(self.buf.data_ptr(), self.nbytes,
@@ -120,3 +123,43 @@ def read_codebook(cb: torch.Tensor) -> Codebook:
 def read_meta(meta: torch.Tensor) -> Meta:
     host = meta.detach().to("cpu").numpy().tobytes()
     return Meta.from_buffer_copy(host)
+
+
+class Batch:
+    """Per-tensor buffers of a batched call: codebook, payload, metadata and
+    output for each tensor of ``xs`` (device tensors of bfloat16).  The item
+    array is built once, so repeated calls only cross the C ABI."""
+
+    def __init__(self, xs, device=None, capacities=None):
+        self.xs = [_bits(x) for x in xs]
+        device = self.xs[0].device if self.xs else torch.device(device or "cuda")
+        self.ns = [x.numel() for x in self.xs]
+        caps = capacities or [max(payload_size(n, n), 16) for n in self.ns]
+        self.cbs = [new_codebook(device) for _ in self.xs]
+        self.payloads = [torch.empty(c, dtype=torch.uint8, device=device) for c in caps]
+        self.metas = [torch.zeros(META_BYTES, dtype=torch.uint8, device=device) for _ in self.xs]
+        self.outs = [torch.empty(n, dtype=torch.bfloat16, device=device) for n in self.ns]
+        self.items = (Item * max(len(self.xs), 1))()
+        for k, x in enumerate(self.xs):
+            it = self.items[k]
+            it.x, it.n, it.cb = x.data_ptr(), self.ns[k], self.cbs[k].data_ptr()
+            it.payload, it.capacity = self.payloads[k].data_ptr(), self.payloads[k].numel()
+            it.meta, it.out = self.metas[k].data_ptr(), self.outs[k].data_ptr()
+        self.count = len(self.xs)
+        self.device = device
+
+    def calibrate(self, ws: Workspace, stream=None):
+        _abi._check("splitzip_calibrate_batch",
+                    _abi.splitzip_calibrate_batch(self.items, self.count, ws.ptr(), ws.nbytes,
+                                                  _stream(stream, self.device)))
+
+    def encode(self, ws: Workspace, stream=None):
+        _abi._check("splitzip_encode_batch",
+                    _abi.splitzip_encode_batch(self.items, self.count, ws.ptr(), ws.nbytes,
+                                               _stream(stream, self.device)))
+
+    def decode(self, status: torch.Tensor | None = None, stream=None):
+        st_ptr = 0 if status is None else status.data_ptr()
+        _abi._check("splitzip_decode_batch",
+                    _abi.splitzip_decode_batch(self.items, self.count, st_ptr,
+                                               _stream(stream, self.device)))

@@ -13,21 +13,27 @@
 // device-scope atomics on one address serialise (about 12 ns each), and an
 // agent-scope fence (L2 write-back + invalidate) issued by every workgroup
 // costs tens of microseconds.  So no kernel takes a global ticket, keeps a
-// per-workgroup counter on one address or issues a device fence:
+// per-workgroup counter on one address or issues a device fence.
+//
+// Every kernel works on a batch of up to kMaxBatch tensors whose descriptors
+// travel by value in the kernel arguments; a single-tensor call is a batch of
+// one.  Workgroups find their tensor by a binary search over the batch's
+// prefix of workgroups (or tiles) per tensor.
 //   k_calibrate   exponent histogram in LDS (64 lane-private copies, so equal
 //                 exponents in a wave never hit one bank), merged with device
-//                 atomics into 16 spread copies; the last arriver of each group
-//                 of 16 workgroups reports to a top counter and the last group
-//                 folds the copies and runs the top-16 select.
+//                 atomics into 16 spread copies per tensor; the last arriver
+//                 of each group of 16 workgroups reports to the tensor's top
+//                 counter and the tensor's last group folds the copies and
+//                 runs the top-16 select.
 //   k_encode      one 8192-element tile per workgroup: 16-byte loads, code
 //                 table in LDS, nibble packing, sign/mantissa bytes, wave
 //                 ballots to rank the tile's escapes, which are staged in the
 //                 workspace with the tile's escape count.  Tiles never talk
 //                 to each other.
-//   k_encode_tail scans the tile counts (every workgroup sums the counts it
-//                 needs) and writes chunk id, chunk-local position and raw
-//                 exponent of every escape at its final rank, then the padding
-//                 and the metadata.
+//   k_encode_tail scans the tile counts of a tensor (every workgroup sums the
+//                 counts it needs) and writes chunk id, chunk-local position
+//                 and raw exponent of every escape at its final rank, then the
+//                 padding and the metadata.
 //   k_decode      one tile of 8192, 16384 or 32768 elements per workgroup (the
 //                 widest that still gives each CU four workgroups): pk + sm ->
 //                 bf16 through a 256-entry pair table in LDS, with the tile's
@@ -40,6 +46,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include "splitzip.h"
@@ -47,6 +54,7 @@
 namespace {
 
 constexpr uint32_t kChunk = SPLITZIP_CHUNK;
+constexpr int kMaxBatch = 32;                 // tensors per launch
 constexpr int kThreads = 256;                 // encode / decode workgroup
 constexpr int kUnit = 8;                      // elements per 16-byte load
 #ifndef SPLITZIP_ENC_UNITS
@@ -54,22 +62,23 @@ constexpr int kUnit = 8;                      // elements per 16-byte load
 #endif
 constexpr int kEncUnits = SPLITZIP_ENC_UNITS; // units per thread per tile
 constexpr int kEncTile = kThreads * kUnit * kEncUnits;   // 8192 elements
-// decode tiles of 2048 * U elements, U in {4, 8, 16} chosen from n (below)
 constexpr int kCalThreads = 1024;
-constexpr int kCalMaxGrid = 512;              // two 1024-thread workgroups per CU
+constexpr int kCalMaxGrid = 512;              // workgroups per tensor, at most
+constexpr int kCalTarget = 2;                 // resident 1024-thread workgroups per CU
 constexpr int kCalGroup = 16;                 // arrivals per first-level counter
-constexpr int kCalCopies = 16;                // global histogram copies
+constexpr int kCalCopies = 16;                // global histogram copies per tensor
 constexpr int kRegisterPatchMax = 16;         // escapes per decode tile patched in registers
 constexpr int kTailTiles = 256;               // encode tiles placed per tail workgroup
 
-// Workspace layout (bytes).  Counters sit on separate cache lines; all of them
-// and the global histogram copies return to zero at the end of every call.
-// The tile counts and the staging area depend only on the workspace size, so
-// one workspace serves any n that fits.
-constexpr size_t kWsCalTop = 0;                                          // uint32
-constexpr size_t kWsCalLvl1 = 256;                                       // uint32, 64 B apart
-constexpr size_t kWsCalHist = kWsCalLvl1 + 64 * (kCalMaxGrid / kCalGroup);   // uint64[16][256]
-constexpr size_t kWsTiles = kWsCalHist + 8 * 256 * kCalCopies;            // uint32[t_max], then stage
+// Workspace layout (bytes).  kMaxBatch calibrate slots, each with its
+// counters on separate cache lines and its histogram copies (all of which
+// return to zero at the end of every call), then the encode tile counts and
+// staging area, whose size depends only on the workspace size.
+constexpr size_t kSlotTop = 0;                                           // uint32
+constexpr size_t kSlotLvl1 = 64;                                         // uint32, 64 B apart
+constexpr size_t kSlotHist = kSlotLvl1 + 64 * (kCalMaxGrid / kCalGroup); // uint64[16][256]
+constexpr size_t kCalSlot = (kSlotHist + 8 * 256 * kCalCopies + 255) & ~size_t(255);
+constexpr size_t kWsTiles = kCalSlot * kMaxBatch;                        // uint32[t_max], stage
 constexpr size_t kWsSlack = 64;
 static_assert(kWsTiles % 256 == 0, "alignment");
 
@@ -98,7 +107,7 @@ __host__ __device__ inline Layout layout_of(uint64_t n, uint64_t e) {
 
 // Tile capacity and staging area of a workspace of ws_bytes.
 struct WsPlan {
-    uint64_t t_max;       // tiles the workspace holds
+    uint64_t t_max;       // encode tiles the workspace holds
     uint64_t off_count;   // uint32[t_max] escapes per tile
     uint64_t off_stage;   // uint32[t_max * kEncTile] staged escapes
 };
@@ -130,6 +139,21 @@ __device__ inline uint64_t wave_sum_u64(uint64_t v) {
     return v;
 }
 
+// Wait until every vector memory operation this wave issued has completed
+// (for atomics: performed at the device coherence point).
+__device__ inline void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Last k in [0, count) with start[k] <= g, for start[0] = 0 <= g < start[count].
+template <typename T>
+__device__ inline uint32_t find_item(const T *start, uint32_t count, uint64_t g) {
+    uint32_t lo = 0, hi = count;
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if ((uint64_t)start[mid] <= g) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
 // Page 1, docstring "Method": the exponent is bits 7..14 of the 16-bit view;
 // the stored byte keeps bit 15 (sign) as its bit 7 and the 7 low mantissa bits.
 __device__ inline uint32_t exp_lo(uint32_t w) { return (w >> 7) & 0xFFu; }
@@ -149,19 +173,31 @@ __device__ inline uint32_t word_of(const u32x4 q, int k) {
 // Calibrate (page 1, calibrate_codebook)
 // ---------------------------------------------------------------------------
 
-// Wait until every vector memory operation this wave issued has completed
-// (for atomics: performed at the device coherence point).
-__device__ inline void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0); }
+struct CalItem {
+    const uint16_t *x;
+    uint64_t n;
+    splitzip_codebook *cb;
+};
 
-__global__ __launch_bounds__(kCalThreads) void k_calibrate(const uint16_t *__restrict__ x,
-                                                           uint64_t n,
-                                                           splitzip_codebook *__restrict__ cb,
-                                                           uint8_t *__restrict__ ws) {
+struct CalArgs {
+    uint32_t count;
+    uint32_t wg_start[kMaxBatch + 1];   // first workgroup of each tensor
+    CalItem it[kMaxBatch];
+    uint8_t *ws;                        // calibrate slots
+};
+
+__global__ __launch_bounds__(kCalThreads) void k_calibrate(CalArgs a) {
     __shared__ uint32_t hist[256 * 64];   // [exponent][lane]
     __shared__ uint32_t part[4 * 256];
     __shared__ uint64_t key[256];
     __shared__ uint64_t covered;
     __shared__ uint32_t proceed;
+
+    const uint32_t item = find_item(a.wg_start, a.count, blockIdx.x);
+    const CalItem I = a.it[item];
+    const uint32_t wg = blockIdx.x - a.wg_start[item];
+    const uint32_t nwg = a.wg_start[item + 1] - a.wg_start[item];
+    uint8_t *slot = a.ws + (size_t)item * kCalSlot;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -169,10 +205,10 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(const uint16_t *__res
     __syncthreads();
 
     uint32_t *hl = hist + lane;
-    const uint64_t nvec = n >> 3;
-    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
-    const uint64_t stride = (uint64_t)gridDim.x * kCalThreads;
-    uint64_t v = (uint64_t)blockIdx.x * kCalThreads + tid;
+    const uint64_t nvec = I.n >> 3;
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(I.x);
+    const uint64_t stride = (uint64_t)nwg * kCalThreads;
+    uint64_t v = (uint64_t)wg * kCalThreads + tid;
     for (; v + 3 * stride < nvec; v += 4 * stride) {
         u32x4 q[4];
 #pragma unroll
@@ -194,8 +230,8 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(const uint16_t *__res
             atomicAdd(hl + exp_hi(q[w]) * 64, 1u);
         }
     }
-    if (blockIdx.x == 0 && (uint64_t)tid < (n & 7)) {
-        uint32_t b = x[(nvec << 3) + tid];
+    if (wg == 0 && (uint64_t)tid < (I.n & 7)) {
+        uint32_t b = I.x[(nvec << 3) + tid];
         atomicAdd(hl + exp_lo(b) * 64, 1u);
     }
     __syncthreads();
@@ -210,12 +246,11 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(const uint16_t *__res
     __syncthreads();
     // Merge into one of kCalCopies global histograms (few workgroups per
     // address, so the device atomics do not queue up behind each other).
-    uint64_t *ghist = reinterpret_cast<uint64_t *>(ws + kWsCalHist);
+    uint64_t *ghist = reinterpret_cast<uint64_t *>(slot + kSlotHist);
     if (tid < 256) {
         const uint32_t s = part[tid] + part[256 + tid] + part[512 + tid] + part[768 + tid];
         if (s)
-            atomicAdd(reinterpret_cast<unsigned long long *>(
-                          ghist + (blockIdx.x % kCalCopies) * 256 + tid),
+            atomicAdd(reinterpret_cast<unsigned long long *>(ghist + (wg % kCalCopies) * 256 + tid),
                       (unsigned long long)s);
     }
     wait_vector_memory();
@@ -223,17 +258,17 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(const uint16_t *__res
 
     // Arrival: the last workgroup of each group of 16 reports to the top
     // counter; the last group merges the copies and selects the codes.
-    const uint32_t g = blockIdx.x / kCalGroup;
-    const uint32_t gsize = min((uint32_t)kCalGroup, gridDim.x - g * kCalGroup);
-    const uint32_t ngroups = (gridDim.x + kCalGroup - 1) / kCalGroup;
+    const uint32_t g = wg / kCalGroup;
+    const uint32_t gsize = min((uint32_t)kCalGroup, nwg - g * kCalGroup);
+    const uint32_t ngroups = (nwg + kCalGroup - 1) / kCalGroup;
     if (tid == 0) {
-        uint32_t *ctr = reinterpret_cast<uint32_t *>(ws + kWsCalLvl1 + 64 * g);
+        uint32_t *ctr = reinterpret_cast<uint32_t *>(slot + kSlotLvl1 + 64 * g);
         const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         uint32_t go = 0;
         if (prev == gsize - 1) {
             __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            uint32_t *top = reinterpret_cast<uint32_t *>(ws + kWsCalTop);
+            uint32_t *top = reinterpret_cast<uint32_t *>(slot + kSlotTop);
             const uint32_t p2 = __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
             if (p2 == ngroups - 1) {
@@ -269,6 +304,7 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(const uint16_t *__res
         part[tid] = r;
     }
     __syncthreads();
+    splitzip_codebook *cb = I.cb;
     uint32_t code = 16;
     if (tid < 256) {
         const uint32_t rank = part[tid] + part[256 + tid] + part[512 + tid] + part[768 + tid];
@@ -289,7 +325,7 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(const uint16_t *__res
         cb->n_codes = n_codes;
         cb->reserved = 0;
         cb->covered = covered;
-        cb->total = n;
+        cb->total = I.n;
     }
 }
 
@@ -297,15 +333,22 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(const uint16_t *__res
 // Encode (page 1, encode_torch + assemble_payload)
 // ---------------------------------------------------------------------------
 
-struct EncArgs {
+struct EncItem {
     const uint16_t *x;
     uint64_t n;
-    uint64_t ntiles;
     const splitzip_codebook *cb;
     uint8_t *payload;
-    uint64_t n_pairs, off_sm, off_cid;
-    uint32_t *tile_count;   // escapes per tile
-    uint32_t *stage;        // per tile: (position in tile << 8) | raw exponent, in order
+    uint64_t capacity;
+    splitzip_meta *meta;
+};
+
+struct EncArgs {
+    uint32_t count;
+    uint32_t blk_start[kMaxBatch + 1];    // first tail workgroup of each tensor
+    uint64_t tile_start[kMaxBatch + 1];   // first tile of each tensor
+    EncItem it[kMaxBatch];
+    uint32_t *tile_count;                 // escapes per tile
+    uint32_t *stage;                      // per tile: (position << 8) | raw exponent
 };
 
 // One 8-element unit: codes -> 4 pk bytes, sign/mantissa -> 8 sm bytes,
@@ -337,22 +380,28 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
     __shared__ uint8_t lut[256];
     __shared__ uint32_t wtot[kEncUnits][4];
 
+    const uint64_t gt = blockIdx.x;
+    const uint32_t item = find_item(a.tile_start, a.count, gt);
+    const EncItem I = a.it[item];
+    const uint64_t t = gt - a.tile_start[item];
+    const uint64_t ntiles = a.tile_start[item + 1] - a.tile_start[item];
+    const Layout L0 = layout_of(I.n, 0);
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const uint64_t t = blockIdx.x;
     const uint64_t base = t * kEncTile;
-    const bool full = base + kEncTile <= a.n;
+    const bool full = base + kEncTile <= I.n;
 
     u32x4 q[kEncUnits];
     if (full) {
 #pragma unroll
         for (int u = 0; u < kEncUnits; ++u) {
             const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
-            q[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.x + i0));
+            q[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(I.x + i0));
         }
     }
-    lut[tid] = a.cb->enc_lut_marked[tid];
+    lut[tid] = I.cb->enc_lut_marked[tid];
     __syncthreads();
 
     uint32_t flags[kEncUnits];
@@ -362,9 +411,10 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
             const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
             uint32_t pk, sm0, sm1;
             encode_unit(q[u], lut, pk, sm0, sm1, flags[u]);
-            __builtin_nontemporal_store(pk, reinterpret_cast<uint32_t *>(a.payload + i0 / 2));
+            __builtin_nontemporal_store(pk, reinterpret_cast<uint32_t *>(I.payload + i0 / 2));
             u32x2 smv = {sm0, sm1};
-            __builtin_nontemporal_store(smv, reinterpret_cast<u32x2_a4 *>(a.payload + a.off_sm + i0));
+            __builtin_nontemporal_store(smv,
+                                        reinterpret_cast<u32x2_a4 *>(I.payload + L0.off_sm + i0));
         }
     } else {
         // last, partial tile: element-wise with bounds checks
@@ -379,32 +429,32 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
                 const uint64_t i = i0 + j;
                 uint32_t b = 0;
                 codes[j] = 0;
-                if (i < a.n) {
-                    b = a.x[i];
+                if (i < I.n) {
+                    b = I.x[i];
                     const uint32_t m = lut[exp_lo(b)];
                     codes[j] = m & 15u;
                     f |= (m >> 4) << j;
-                    a.payload[a.off_sm + i] = (uint8_t)sm_of16(b);
+                    I.payload[L0.off_sm + i] = (uint8_t)sm_of16(b);
                 }
                 wv[j >> 1] |= b << (16 * (j & 1));
             }
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const uint64_t i = i0 + 2 * k;
-                if (i < a.n) {
-                    const uint32_t lo = (i + 1 < a.n) ? codes[2 * k + 1] : 0u;
-                    a.payload[i / 2] = (uint8_t)((codes[2 * k] << 4) | lo);
+                if (i < I.n) {
+                    const uint32_t lo = (i + 1 < I.n) ? codes[2 * k + 1] : 0u;
+                    I.payload[i / 2] = (uint8_t)((codes[2 * k] << 4) | lo);
                 }
             }
             q[u] = u32x4{wv[0], wv[1], wv[2], wv[3]};
             flags[u] = f;
         }
     }
-    if (t == a.ntiles - 1 && tid == 0) {
+    if (t == ntiles - 1 && tid == 0) {
         // zero padding between the dense sections (page 1: the payload is
         // assembled in a zero-filled buffer)
-        for (uint64_t b = a.n_pairs; b < a.off_sm; ++b) a.payload[b] = 0;
-        for (uint64_t b = a.off_sm + a.n; b < a.off_cid; ++b) a.payload[b] = 0;
+        for (uint64_t b = L0.n_pairs; b < L0.off_sm; ++b) I.payload[b] = 0;
+        for (uint64_t b = L0.off_sm + I.n; b < L0.off_cid; ++b) I.payload[b] = 0;
     }
 
     // Escape ranks inside the tile, in element order (unit, thread, j).
@@ -438,9 +488,9 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
             tile_total += wtot[u][w];
         }
     }
-    if (tid == 0) a.tile_count[t] = tile_total;
+    if (tid == 0) a.tile_count[gt] = tile_total;
     if (tile_total) {
-        uint32_t *stage = a.stage + t * kEncTile;
+        uint32_t *stage = a.stage + gt * kEncTile;
 #pragma unroll
         for (int u = 0; u < kEncUnits; ++u) {
             uint32_t f = flags[u];
@@ -457,17 +507,6 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
     }
 }
 
-struct TailArgs {
-    uint64_t n;
-    uint64_t ntiles;
-    const splitzip_codebook *cb;
-    uint8_t *payload;
-    uint64_t capacity;
-    splitzip_meta *meta;
-    const uint32_t *tile_count;
-    const uint32_t *stage;
-};
-
 // Inclusive scan of one value per thread across a 256-thread workgroup.
 __device__ inline uint32_t block_scan_incl(uint32_t v, uint32_t *lds_waves) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -482,49 +521,44 @@ __device__ inline uint32_t block_scan_incl(uint32_t v, uint32_t *lds_waves) {
     return v;
 }
 
-// Escape placement: every workgroup sums the tile counts before its range
-// (its first escape's rank) and over all tiles (the escape count, hence the
-// offsets of local_pos and esc_val), then writes its tiles' escapes at their
-// final ranks.  Workgroup 0 writes the padding and the metadata.
-__global__ __launch_bounds__(kThreads) void k_encode_tail(TailArgs a) {
+// Escape placement: every workgroup sums the tensor's tile counts before its
+// range (its first escape's rank) and over all of the tensor's tiles (the
+// escape count, hence the offsets of local_pos and esc_val), then writes its
+// tiles' escapes at their final ranks.  The tensor's first tail workgroup
+// writes the padding and the metadata.
+__global__ __launch_bounds__(kThreads) void k_encode_tail(EncArgs a) {
     __shared__ uint64_t red[2][kThreads / 64];
     __shared__ uint32_t waves[kThreads / 64];
     __shared__ uint32_t scan[kTailTiles + 1];
+    const uint32_t item = find_item(a.blk_start, a.count, blockIdx.x);
+    const EncItem I = a.it[item];
+    const uint32_t blk = blockIdx.x - a.blk_start[item];
+    const uint64_t tfirst = a.tile_start[item], tend = a.tile_start[item + 1];
+    const uint64_t ntiles = tend - tfirst;
+    const uint32_t *counts = a.tile_count + tfirst;
+
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint64_t t0 = (uint64_t)blockIdx.x * kTailTiles;
-    const uint64_t t1 = t0 + kTailTiles < a.ntiles ? t0 + kTailTiles : a.ntiles;
+    const uint64_t t0 = (uint64_t)blk * kTailTiles;
+    const uint64_t t1 = t0 + kTailTiles < ntiles ? t0 + kTailTiles : ntiles;
 
     // this block's own tile counts (issued first, used after the sweep)
     const uint64_t mine_t = t0 + tid;
-    const uint32_t mine_c = mine_t < t1 ? a.tile_count[mine_t] : 0u;
-    // counts of all tiles, 4 per load, 8 loads in flight per thread
+    const uint32_t mine_c = mine_t < t1 ? counts[mine_t] : 0u;
+    // counts of all the tensor's tiles, 8 loads in flight per thread
     uint64_t before = 0, all = 0;
-    const uint64_t nvec = a.ntiles / 4;
-    const u32x4 *cv = reinterpret_cast<const u32x4 *>(a.tile_count);
-    for (uint64_t v0 = 0; v0 < nvec; v0 += 8 * kThreads) {
-        u32x4 c4[8];
+    for (uint64_t k0 = 0; k0 < ntiles; k0 += 8 * kThreads) {
+        uint32_t c8[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint64_t v = v0 + j * kThreads + tid;
-            c4[j] = v < nvec ? cv[v] : u32x4{0, 0, 0, 0};
+            const uint64_t k = k0 + j * kThreads + tid;
+            c8[j] = k < ntiles ? counts[k] : 0u;
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint64_t t = 4 * (v0 + j * kThreads + tid);
-            const uint64_t s4 = (uint64_t)c4[j].x + c4[j].y + c4[j].z + c4[j].w;
-            all += s4;
-            if (t + 4 <= t0) before += s4;
-            else if (t < t0) {
-                before += c4[j].x;
-                if (t + 1 < t0) before += c4[j].y;
-                if (t + 2 < t0) before += c4[j].z;
-            }
+            const uint64_t k = k0 + j * kThreads + tid;
+            all += c8[j];
+            before += k < t0 ? c8[j] : 0u;
         }
-    }
-    for (uint64_t t = 4 * nvec + tid; t < a.ntiles; t += kThreads) {
-        const uint32_t c = a.tile_count[t];
-        all += c;
-        if (t < t0) before += c;
     }
     before = wave_sum_u64(before);
     all = wave_sum_u64(all);
@@ -543,9 +577,9 @@ __global__ __launch_bounds__(kThreads) void k_encode_tail(TailArgs a) {
         P += red[0][w];
         e += red[1][w];
     }
-    const Layout L = layout_of(a.n, e);
-    const bool fits = L.total <= a.capacity;
-    const uint32_t mine_total = scan[t1 - t0];
+    const Layout L = layout_of(I.n, e);
+    const bool fits = L.total <= I.capacity;
+    const uint32_t mine_total = t1 > t0 ? scan[t1 - t0] : 0u;
 
     for (uint32_t k = tid; k < mine_total; k += kThreads) {
         // tile j of this block holding the k-th escape: last j with scan[j] <= k
@@ -555,21 +589,21 @@ __global__ __launch_bounds__(kThreads) void k_encode_tail(TailArgs a) {
             if (scan[mid] <= k) lo = mid; else hi = mid;
         }
         const uint64_t tile = t0 + lo;
-        const uint32_t word = a.stage[tile * kEncTile + (k - scan[lo])];
+        const uint32_t word = a.stage[(tfirst + tile) * kEncTile + (k - scan[lo])];
         const uint64_t i = tile * kEncTile + (word >> 8);
         const uint64_t r = P + k;
-        if (L.off_cid + 4 * r + 4 <= a.capacity)
-            *reinterpret_cast<uint32_t *>(a.payload + L.off_cid + 4 * r) = (uint32_t)(i / kChunk);
+        if (L.off_cid + 4 * r + 4 <= I.capacity)
+            *reinterpret_cast<uint32_t *>(I.payload + L.off_cid + 4 * r) = (uint32_t)(i / kChunk);
         if (fits) {
-            *reinterpret_cast<uint16_t *>(a.payload + L.off_lpos + 2 * r) = (uint16_t)(i % kChunk);
-            a.payload[L.off_ev + r] = (uint8_t)(word & 0xFFu);
+            *reinterpret_cast<uint16_t *>(I.payload + L.off_lpos + 2 * r) = (uint16_t)(i % kChunk);
+            I.payload[L.off_ev + r] = (uint8_t)(word & 0xFFu);
         }
     }
-    if (blockIdx.x == 0 && tid == 0) {
+    if (blk == 0 && tid == 0) {
         if (fits)
-            for (uint64_t b = L.off_lpos + 2 * e; b < L.off_ev; ++b) a.payload[b] = 0;
-        splitzip_meta *m = a.meta;
-        m->n = a.n;
+            for (uint64_t b = L.off_lpos + 2 * e; b < L.off_ev; ++b) I.payload[b] = 0;
+        splitzip_meta *m = I.meta;
+        m->n = I.n;
         m->n_pairs = L.n_pairs;
         m->chunk_size = kChunk;
         m->n_esc = e;
@@ -579,8 +613,8 @@ __global__ __launch_bounds__(kThreads) void k_encode_tail(TailArgs a) {
         m->offsets[2] = L.off_cid;
         m->offsets[3] = L.off_lpos;
         m->offsets[4] = L.off_ev;
-        m->covered = a.cb->covered;
-        m->total = a.cb->total;
+        m->covered = I.cb->covered;
+        m->total = I.cb->total;
         m->status = fits ? SPLITZIP_OK : SPLITZIP_ERR_CAPACITY;
         m->reserved = 0;
     }
@@ -590,24 +624,30 @@ __global__ __launch_bounds__(kThreads) void k_encode_tail(TailArgs a) {
 // Decode (page 1, decode_torch)
 // ---------------------------------------------------------------------------
 
-struct DecArgs {
+struct DecItem {
     const uint8_t *payload;
     uint64_t payload_bytes;
     const splitzip_meta *meta;
     const uint8_t *dec_lut;
     uint16_t *out;
     uint64_t n;
+};
+
+struct DecArgs {
+    uint32_t count;
+    uint64_t tile_start[kMaxBatch + 1];   // first decode tile of each tensor
+    DecItem it[kMaxBatch];
     int32_t *status;
 };
 
 // Metadata must describe exactly the layout of (n, n_esc) and fit the buffer.
-__device__ inline bool meta_ok(const DecArgs &a, Layout &L) {
-    const splitzip_meta *m = a.meta;
-    if (m->n != a.n || m->chunk_size != kChunk || m->n_esc > a.n) return false;
-    L = layout_of(a.n, m->n_esc);
+__device__ inline bool meta_ok(const DecItem &I, Layout &L) {
+    const splitzip_meta *m = I.meta;
+    if (m->n != I.n || m->chunk_size != kChunk || m->n_esc > I.n) return false;
+    L = layout_of(I.n, m->n_esc);
     return m->n_pairs == L.n_pairs && m->offsets[0] == 0 && m->offsets[1] == L.off_sm &&
            m->offsets[2] == L.off_cid && m->offsets[3] == L.off_lpos &&
-           m->offsets[4] == L.off_ev && m->comp_bytes == L.total && L.total <= a.payload_bytes;
+           m->offsets[4] == L.off_ev && m->comp_bytes == L.total && L.total <= I.payload_bytes;
 }
 
 // First r in [lo, hi) with cid[r] >= key (hi when none), for chunk ids sorted
@@ -650,21 +690,24 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
     __shared__ uint32_t pair_lut[256];      // pk byte -> (even exponent, odd exponent << 16)
     __shared__ uint32_t esc_list[kRegisterPatchMax];
     __shared__ uint64_t range[2];
+    const uint64_t gt = blockIdx.x;
+    const uint32_t item = find_item(a.tile_start, a.count, gt);
+    const DecItem I = a.it[item];
     Layout L;
-    if (!meta_ok(a, L)) {
-        if (blockIdx.x == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
+    if (!meta_ok(I, L)) {
+        if (gt == a.tile_start[item] && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
         return;
     }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const uint64_t e = a.meta->n_esc;
-    const uint64_t base = (uint64_t)blockIdx.x * kDecTile;
-    const bool full = base + kDecTile <= a.n;
-    const uint8_t *pk = a.payload;
-    const uint8_t *sm = a.payload + L.off_sm;
-    const int32_t *cid = reinterpret_cast<const int32_t *>(a.payload + L.off_cid);
-    const uint16_t *lpos = reinterpret_cast<const uint16_t *>(a.payload + L.off_lpos);
-    const uint8_t *ev = a.payload + L.off_ev;
+    const uint64_t e = I.meta->n_esc;
+    const uint64_t base = (gt - a.tile_start[item]) * kDecTile;
+    const bool full = base + kDecTile <= I.n;
+    const uint8_t *pk = I.payload;
+    const uint8_t *sm = I.payload + L.off_sm;
+    const int32_t *cid = reinterpret_cast<const int32_t *>(I.payload + L.off_cid);
+    const uint16_t *lpos = reinterpret_cast<const uint16_t *>(I.payload + L.off_lpos);
+    const uint8_t *ev = I.payload + L.off_ev;
 
     uint32_t pkw[kDecUnits];
     u32x2 smw[kDecUnits];
@@ -676,12 +719,12 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
             smw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4 *>(sm + i0));
         }
     }
-    pair_lut[tid] = (uint32_t)a.dec_lut[tid >> 4] | ((uint32_t)a.dec_lut[tid & 15] << 16);
+    pair_lut[tid] = (uint32_t)I.dec_lut[tid >> 4] | ((uint32_t)I.dec_lut[tid & 15] << 16);
     if (tid < 64) {
         // escapes of chunks [c0, c1): the tile's range of the sorted stream
         uint64_t r0 = 0, r1 = 0;
         if (e) {
-            const uint64_t nchunks = (a.n + kChunk - 1) / kChunk;
+            const uint64_t nchunks = (I.n + kChunk - 1) / kChunk;
             const uint64_t c0 = base / kChunk, c1 = c0 + kDecTile / kChunk;
             r0 = lower_bound_wave(cid, 0, e, (int64_t)c0, (e * c0) / nchunks, lane);
             r1 = lower_bound_wave(cid, r0, e, (int64_t)c1, r0 + (e * (c1 - c0)) / nchunks, lane);
@@ -739,7 +782,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
         for (int u = 0; u < kDecUnits; ++u) {
             const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
             // plain stores: measured faster than non-temporal ones for this stream
-            *reinterpret_cast<u32x4 *>(a.out + i0) = o[u];
+            *reinterpret_cast<u32x4 *>(I.out + i0) = o[u];
         }
         return;
     }
@@ -757,47 +800,51 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
                 const uint32_t s = smw[u][k >> 1] >> (16 * (k & 1));
                 o[k] = join16(s & 0xFFu, ee & 0xFFu) | (join16((s >> 8) & 0xFFu, ee >> 16) << 16);
             }
-            *reinterpret_cast<u32x4 *>(a.out + i0) = o;
+            *reinterpret_cast<u32x4 *>(I.out + i0) = o;
         }
     } else {
-        for (uint64_t i = base + tid; i < a.n; i += kThreads) {
+        for (uint64_t i = base + tid; i < I.n; i += kThreads) {
             const uint32_t byte = pk[i / 2];
             const uint32_t code = (i & 1) ? (byte & 15u) : (byte >> 4);
-            a.out[i] = (uint16_t)join16(sm[i], a.dec_lut[code]);
+            I.out[i] = (uint16_t)join16(sm[i], I.dec_lut[code]);
         }
     }
     __syncthreads();
     for (uint64_t r = r0 + tid; r < r1; r += kThreads) {
         const int64_t idx = (int64_t)cid[r] * kChunk + lpos[r];
-        if (idx >= (int64_t)base && idx < (int64_t)(base + kDecTile) && idx < (int64_t)a.n)
-            a.out[idx] = (uint16_t)join16(sm[idx], ev[r]);
+        if (idx >= (int64_t)base && idx < (int64_t)(base + kDecTile) && idx < (int64_t)I.n)
+            I.out[idx] = (uint16_t)join16(sm[idx], ev[r]);
     }
 }
 
 // Validation (and order-independent re-application) of every escape.
 __global__ __launch_bounds__(kThreads) void k_decode_check(DecArgs a) {
-    Layout L;
-    if (!meta_ok(a, L)) return;   // reported by k_decode
-    const uint64_t e = a.meta->n_esc;
-    const uint8_t *sm = a.payload + L.off_sm;
-    const int32_t *cid = reinterpret_cast<const int32_t *>(a.payload + L.off_cid);
-    const uint16_t *lpos = reinterpret_cast<const uint16_t *>(a.payload + L.off_lpos);
-    const uint8_t *ev = a.payload + L.off_ev;
     const uint64_t gs = (uint64_t)gridDim.x * kThreads;
     int32_t bad = 0;
-    for (uint64_t r = (uint64_t)blockIdx.x * kThreads + threadIdx.x; r < e; r += gs) {
-        const int32_t c = cid[r];
-        const uint32_t pos = lpos[r];
-        if (c < 0) { bad |= 2; continue; }
-        if (pos >= kChunk) bad |= 4;
-        const uint64_t idx = (uint64_t)c * kChunk + pos;
-        if (idx >= a.n) { bad |= 2; continue; }
-        if (r > 0) {
-            const int32_t pc = cid[r - 1];
-            const uint64_t prev = (uint64_t)(uint32_t)pc * kChunk + lpos[r - 1];
-            if (pc < 0 || prev >= idx) bad |= 8;
+    for (uint32_t item = 0; item < a.count; ++item) {
+        const DecItem I = a.it[item];
+        if (I.n == 0) continue;
+        Layout L;
+        if (!meta_ok(I, L)) continue;   // reported by k_decode
+        const uint64_t e = I.meta->n_esc;
+        const uint8_t *sm = I.payload + L.off_sm;
+        const int32_t *cid = reinterpret_cast<const int32_t *>(I.payload + L.off_cid);
+        const uint16_t *lpos = reinterpret_cast<const uint16_t *>(I.payload + L.off_lpos);
+        const uint8_t *ev = I.payload + L.off_ev;
+        for (uint64_t r = (uint64_t)blockIdx.x * kThreads + threadIdx.x; r < e; r += gs) {
+            const int32_t c = cid[r];
+            const uint32_t pos = lpos[r];
+            if (c < 0) { bad |= 2; continue; }
+            if (pos >= kChunk) bad |= 4;
+            const uint64_t idx = (uint64_t)c * kChunk + pos;
+            if (idx >= I.n) { bad |= 2; continue; }
+            if (r > 0) {
+                const int32_t pc = cid[r - 1];
+                const uint64_t prev = (uint64_t)(uint32_t)pc * kChunk + lpos[r - 1];
+                if (pc < 0 || prev >= idx) bad |= 8;
+            }
+            I.out[idx] = (uint16_t)join16(sm[idx], ev[r]);
         }
-        a.out[idx] = (uint16_t)join16(sm[idx], ev[r]);
     }
     if (bad && a.status) atomicOr(a.status, bad);
 }
@@ -832,8 +879,139 @@ inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)
 
 inline uint64_t enc_tiles(uint64_t n) { return (n + kEncTile - 1) / kEncTile; }
 
+inline uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+// Device address of a codebook's dec_lut (address arithmetic only).
+inline const uint8_t *dec_lut_of(const splitzip_codebook *cb) {
+    return reinterpret_cast<const uint8_t *>(cb) + offsetof(splitzip_codebook, dec_lut);
+}
+
 int launched() {
     return hipGetLastError() == hipSuccess ? SPLITZIP_OK : SPLITZIP_ERR_HIP;
+}
+
+// Argument checks shared by the single and batched entry points.
+int check_calibrate_item(const uint16_t *x, uint64_t n, const splitzip_codebook *cb) {
+    if (n > SPLITZIP_MAX_N || (n && (!x || !aligned(x, 16))) || !cb || !aligned(cb, 8))
+        return SPLITZIP_ERR_INVALID;
+    return SPLITZIP_OK;
+}
+
+int check_encode_item(const uint16_t *x, uint64_t n, const splitzip_codebook *cb,
+                      const uint8_t *payload, uint64_t capacity, const splitzip_meta *meta) {
+    if (check_calibrate_item(x, n, cb) || !meta || !aligned(meta, 8) || (!payload && capacity) ||
+        !aligned(payload, 16))
+        return SPLITZIP_ERR_INVALID;
+    if (capacity < layout_of(n, 0).total) return SPLITZIP_ERR_CAPACITY;
+    return SPLITZIP_OK;
+}
+
+int check_decode_item(const uint8_t *payload, const splitzip_meta *meta, const uint8_t *dec_lut,
+                      const uint16_t *out, uint64_t n) {
+    if (n > SPLITZIP_MAX_N || !meta || !aligned(meta, 8) || !dec_lut ||
+        (n && (!payload || !aligned(payload, 16) || !out || !aligned(out, 16))))
+        return SPLITZIP_ERR_INVALID;
+    return SPLITZIP_OK;
+}
+
+// Calibrate launch for up to kMaxBatch tensors: the GPU's worth of resident
+// workgroups is shared out in proportion to size (at least one per tensor,
+// at most one per 4096 16-byte loads and kCalMaxGrid per tensor).
+int launch_calibrate(const CalItem *items, uint32_t count, uint8_t *ws, hipStream_t s) {
+    int cus = 0;
+    if (!cu_count(cus)) return SPLITZIP_ERR_HIP;
+    CalArgs a{};
+    a.count = count;
+    a.ws = ws;
+    uint64_t total = 0;
+    for (uint32_t k = 0; k < count; ++k) total += items[k].n;
+    const uint64_t target = (uint64_t)kCalTarget * cus;
+    uint32_t wg = 0;
+    for (uint32_t k = 0; k < count; ++k) {
+        a.it[k] = items[k];
+        uint64_t g = total ? ceil_div(target * items[k].n, total) : 1;
+        const uint64_t by_size = ceil_div(items[k].n >> 3, 4 * (uint64_t)kCalThreads);
+        if (g > by_size) g = by_size;
+        if (g > kCalMaxGrid) g = kCalMaxGrid;
+        if (g == 0) g = 1;
+        a.wg_start[k] = wg;
+        wg += (uint32_t)g;
+    }
+    a.wg_start[count] = wg;
+    k_calibrate<<<wg, kCalThreads, 0, s>>>(a);
+    return launched();
+}
+
+// Encode launch (main + tail) for up to kMaxBatch tensors whose tiles fit the
+// workspace plan.
+int launch_encode(const EncItem *items, uint32_t count, const WsPlan &P, uint8_t *ws,
+                  hipStream_t s) {
+    EncArgs a{};
+    a.count = count;
+    a.tile_count = reinterpret_cast<uint32_t *>(ws + P.off_count);
+    a.stage = reinterpret_cast<uint32_t *>(ws + P.off_stage);
+    uint64_t tiles = 0;
+    uint32_t blks = 0;
+    for (uint32_t k = 0; k < count; ++k) {
+        a.it[k] = items[k];
+        a.tile_start[k] = tiles;
+        a.blk_start[k] = blks;
+        const uint64_t t = enc_tiles(items[k].n);
+        tiles += t;
+        const uint64_t b = ceil_div(t, kTailTiles);
+        blks += (uint32_t)(b ? b : 1);   // an empty tensor still gets its metadata
+    }
+    a.tile_start[count] = tiles;
+    a.blk_start[count] = blks;
+    if (tiles > P.t_max) return SPLITZIP_ERR_WORKSPACE;
+    if (tiles) {
+        k_encode<<<(unsigned)tiles, kThreads, 0, s>>>(a);
+        if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
+    }
+    k_encode_tail<<<blks, kThreads, 0, s>>>(a);
+    return launched();
+}
+
+// Decode launch for up to kMaxBatch tensors.  Wider tiles keep more bytes in
+// flight per wave; the widest that still gives every CU four workgroups wins.
+int launch_decode(const DecItem *items, uint32_t count, int32_t *status, hipStream_t s) {
+    int cus = 0;
+    if (!cu_count(cus)) return SPLITZIP_ERR_HIP;
+    uint64_t t16 = 0, t8 = 0;
+    for (uint32_t k = 0; k < count; ++k) {
+        t16 += ceil_div(items[k].n, 16 * 2048);
+        t8 += ceil_div(items[k].n, 8 * 2048);
+    }
+    const uint64_t want = 4 * (uint64_t)cus;
+    const int units = t16 >= want ? 16 : (t8 >= want ? 8 : 4);
+    DecArgs a{};
+    a.count = count;
+    a.status = status;
+    uint64_t tiles = 0;
+    for (uint32_t k = 0; k < count; ++k) {
+        a.it[k] = items[k];
+        a.tile_start[k] = tiles;
+        tiles += ceil_div(items[k].n, (uint64_t)units * 2048);
+    }
+    a.tile_start[count] = tiles;
+    if (tiles) {
+        if (units == 16)
+            k_decode<16><<<(unsigned)tiles, kThreads, 0, s>>>(a);
+        else if (units == 8)
+            k_decode<8><<<(unsigned)tiles, kThreads, 0, s>>>(a);
+        else
+            k_decode<4><<<(unsigned)tiles, kThreads, 0, s>>>(a);
+        if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
+    }
+    if (status) {
+        uint64_t n = 0;
+        for (uint32_t k = 0; k < count; ++k) n += items[k].n;
+        uint64_t cgrid = ceil_div(n, 16 * kThreads);
+        if (cgrid > 1024) cgrid = 1024;
+        if (cgrid == 0) cgrid = 1;
+        k_decode_check<<<(unsigned)cgrid, kThreads, 0, s>>>(a);
+    }
+    return launched();
 }
 
 }  // namespace
@@ -869,91 +1047,127 @@ size_t splitzip_workspace_size(uint64_t n) {
     return (size_t)(kWsTiles + kWsSlack + t * (4 + 4 * (uint64_t)kEncTile));
 }
 
+size_t splitzip_workspace_size_batch(const uint64_t *n, uint32_t count) {
+    // tiles of the largest launch: consecutive groups of kMaxBatch tensors
+    uint64_t most = 0;
+    for (uint32_t k0 = 0; n && k0 < count; k0 += kMaxBatch) {
+        uint64_t t = 0;
+        for (uint32_t k = k0; k < count && k < k0 + kMaxBatch; ++k) t += enc_tiles(n[k]);
+        if (t > most) most = t;
+    }
+    if (most == 0) most = 1;
+    return (size_t)(kWsTiles + kWsSlack + most * (4 + 4 * (uint64_t)kEncTile));
+}
+
 int splitzip_workspace_init(void *d_ws, size_t ws_bytes, void *stream) {
     if (!d_ws || !aligned(d_ws, 16) || ws_bytes < splitzip_workspace_size(0))
         return SPLITZIP_ERR_INVALID;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    k_fill_zero<<<64, 256, 0, s>>>(reinterpret_cast<uint32_t *>(d_ws), kWsTiles / 4);
+    k_fill_zero<<<256, 256, 0, s>>>(reinterpret_cast<uint32_t *>(d_ws), kWsTiles / 4);
     return launched();
 }
 
 int splitzip_calibrate(const uint16_t *d_x, uint64_t n, splitzip_codebook *d_cb, void *d_ws,
                        size_t ws_bytes, void *stream) {
-    if (n > SPLITZIP_MAX_N || (n && (!d_x || !aligned(d_x, 16))) || !d_cb || !aligned(d_cb, 8) ||
-        !d_ws || !aligned(d_ws, 16))
+    if (check_calibrate_item(d_x, n, d_cb) || !d_ws || !aligned(d_ws, 16))
         return SPLITZIP_ERR_INVALID;
     if (ws_bytes < splitzip_workspace_size(0)) return SPLITZIP_ERR_WORKSPACE;
-    int cus = 0;
-    if (!cu_count(cus)) return SPLITZIP_ERR_HIP;
-    const uint64_t nvec = n >> 3;
-    uint64_t grid = (nvec + 4 * kCalThreads - 1) / (4 * kCalThreads);
-    uint64_t cap = 2 * (uint64_t)cus;
-    if (cap > kCalMaxGrid) cap = kCalMaxGrid;
-    if (grid > cap) grid = cap;
-    if (grid == 0) grid = 1;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    k_calibrate<<<(unsigned)grid, kCalThreads, 0, s>>>(d_x, n, d_cb,
-                                                      reinterpret_cast<uint8_t *>(d_ws));
-    return launched();
+    const CalItem it{d_x, n, d_cb};
+    return launch_calibrate(&it, 1, reinterpret_cast<uint8_t *>(d_ws),
+                            reinterpret_cast<hipStream_t>(stream));
 }
 
 int splitzip_encode(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_cb,
                     uint8_t *d_payload, uint64_t capacity, splitzip_meta *d_meta, void *d_ws,
                     size_t ws_bytes, void *stream) {
-    if (n > SPLITZIP_MAX_N || (n && (!d_x || !aligned(d_x, 16))) || !d_cb || !aligned(d_cb, 8) ||
-        !d_meta || !aligned(d_meta, 8) || !d_ws || !aligned(d_ws, 16) ||
-        (!d_payload && capacity) || !aligned(d_payload, 16))
-        return SPLITZIP_ERR_INVALID;
-    const Layout L0 = layout_of(n, 0);
-    if (capacity < L0.total) return SPLITZIP_ERR_CAPACITY;
-    const uint64_t ntiles = enc_tiles(n);
+    const int rc = check_encode_item(d_x, n, d_cb, d_payload, capacity, d_meta);
+    if (rc) return rc;
+    if (!d_ws || !aligned(d_ws, 16)) return SPLITZIP_ERR_INVALID;
     const WsPlan P = ws_plan(ws_bytes);
-    if (ws_bytes < splitzip_workspace_size(n) || P.t_max < ntiles) return SPLITZIP_ERR_WORKSPACE;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    uint8_t *ws = reinterpret_cast<uint8_t *>(d_ws);
-    uint32_t *counts = reinterpret_cast<uint32_t *>(ws + P.off_count);
-    uint32_t *stage = reinterpret_cast<uint32_t *>(ws + P.off_stage);
-    if (ntiles) {
-        EncArgs a{d_x, n, ntiles, d_cb, d_payload, L0.n_pairs, L0.off_sm, L0.off_cid, counts, stage};
-        k_encode<<<(unsigned)ntiles, kThreads, 0, s>>>(a);
-        if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
-    }
-    uint64_t tgrid = (ntiles + kTailTiles - 1) / kTailTiles;
-    if (tgrid == 0) tgrid = 1;
-    TailArgs t{n, ntiles, d_cb, d_payload, capacity, d_meta, counts, stage};
-    k_encode_tail<<<(unsigned)tgrid, kThreads, 0, s>>>(t);
-    return launched();
+    if (ws_bytes < splitzip_workspace_size(n) || P.t_max < enc_tiles(n))
+        return SPLITZIP_ERR_WORKSPACE;
+    const EncItem it{d_x, n, d_cb, d_payload, capacity, d_meta};
+    return launch_encode(&it, 1, P, reinterpret_cast<uint8_t *>(d_ws),
+                         reinterpret_cast<hipStream_t>(stream));
 }
 
 int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const splitzip_meta *d_meta,
                     const uint8_t *d_dec_lut, uint16_t *d_out, uint64_t n, int32_t *d_status,
                     void *stream) {
-    if (n > SPLITZIP_MAX_N || !d_meta || !aligned(d_meta, 8) || !d_dec_lut ||
-        (n && (!d_payload || !aligned(d_payload, 16) || !d_out || !aligned(d_out, 16))) ||
+    if (check_decode_item(d_payload, d_meta, d_dec_lut, d_out, n) ||
         (d_status && !aligned(d_status, 4)))
         return SPLITZIP_ERR_INVALID;
     if (n == 0) return SPLITZIP_OK;
+    const DecItem it{d_payload, payload_bytes, d_meta, d_dec_lut, d_out, n};
+    return launch_decode(&it, 1, d_status, reinterpret_cast<hipStream_t>(stream));
+}
+
+int splitzip_calibrate_batch(const splitzip_item *items, uint32_t count, void *d_ws,
+                             size_t ws_bytes, void *stream) {
+    if ((count && !items) || !d_ws || !aligned(d_ws, 16)) return SPLITZIP_ERR_INVALID;
+    for (uint32_t k = 0; k < count; ++k)
+        if (check_calibrate_item(items[k].x, items[k].n, items[k].cb)) return SPLITZIP_ERR_INVALID;
+    if (ws_bytes < splitzip_workspace_size(0)) return SPLITZIP_ERR_WORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    DecArgs a{d_payload, payload_bytes, d_meta, d_dec_lut, d_out, n, d_status};
-    // Wider tiles keep more bytes in flight per wave; use the widest that
-    // still gives every CU four workgroups.
-    int cus = 0;
-    if (!cu_count(cus)) return SPLITZIP_ERR_HIP;
-    const uint64_t want = 4 * (uint64_t)cus;
-    const uint64_t t16 = (n + 16 * 2048 - 1) / (16 * 2048), t8 = (n + 8 * 2048 - 1) / (8 * 2048);
-    if (t16 >= want)
-        k_decode<16><<<(unsigned)t16, kThreads, 0, s>>>(a);
-    else if (t8 >= want)
-        k_decode<8><<<(unsigned)t8, kThreads, 0, s>>>(a);
-    else
-        k_decode<4><<<(unsigned)((n + 4 * 2048 - 1) / (4 * 2048)), kThreads, 0, s>>>(a);
-    if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
-    if (d_status) {
-        uint64_t cgrid = (n + 16 * kThreads - 1) / (16 * kThreads);
-        if (cgrid > 1024) cgrid = 1024;
-        k_decode_check<<<(unsigned)cgrid, kThreads, 0, s>>>(a);
+    CalItem chunk[kMaxBatch];
+    for (uint32_t k0 = 0; k0 < count; k0 += kMaxBatch) {
+        const uint32_t m = count - k0 < (uint32_t)kMaxBatch ? count - k0 : (uint32_t)kMaxBatch;
+        for (uint32_t k = 0; k < m; ++k)
+            chunk[k] = CalItem{items[k0 + k].x, items[k0 + k].n, items[k0 + k].cb};
+        const int rc = launch_calibrate(chunk, m, reinterpret_cast<uint8_t *>(d_ws), s);
+        if (rc) return rc;
     }
-    return launched();
+    return SPLITZIP_OK;
+}
+
+int splitzip_encode_batch(const splitzip_item *items, uint32_t count, void *d_ws,
+                          size_t ws_bytes, void *stream) {
+    if ((count && !items) || !d_ws || !aligned(d_ws, 16)) return SPLITZIP_ERR_INVALID;
+    for (uint32_t k = 0; k < count; ++k) {
+        const splitzip_item &I = items[k];
+        const int rc = check_encode_item(I.x, I.n, I.cb, I.payload, I.capacity, I.meta);
+        if (rc) return rc;
+    }
+    const WsPlan P = ws_plan(ws_bytes);
+    for (uint32_t k0 = 0; k0 < count; k0 += kMaxBatch) {
+        uint64_t tiles = 0;
+        for (uint32_t k = k0; k < count && k < k0 + kMaxBatch; ++k) tiles += enc_tiles(items[k].n);
+        if (tiles > P.t_max) return SPLITZIP_ERR_WORKSPACE;
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    EncItem chunk[kMaxBatch];
+    for (uint32_t k0 = 0; k0 < count; k0 += kMaxBatch) {
+        const uint32_t m = count - k0 < (uint32_t)kMaxBatch ? count - k0 : (uint32_t)kMaxBatch;
+        for (uint32_t k = 0; k < m; ++k) {
+            const splitzip_item &I = items[k0 + k];
+            chunk[k] = EncItem{I.x, I.n, I.cb, I.payload, I.capacity, I.meta};
+        }
+        const int rc = launch_encode(chunk, m, P, reinterpret_cast<uint8_t *>(d_ws), s);
+        if (rc) return rc;
+    }
+    return SPLITZIP_OK;
+}
+
+int splitzip_decode_batch(const splitzip_item *items, uint32_t count, int32_t *d_status,
+                          void *stream) {
+    if ((count && !items) || (d_status && !aligned(d_status, 4))) return SPLITZIP_ERR_INVALID;
+    for (uint32_t k = 0; k < count; ++k) {
+        const splitzip_item &I = items[k];
+        if (!I.cb || check_decode_item(I.payload, I.meta, dec_lut_of(I.cb), I.out, I.n))
+            return SPLITZIP_ERR_INVALID;
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    DecItem chunk[kMaxBatch];
+    for (uint32_t k0 = 0; k0 < count; k0 += kMaxBatch) {
+        const uint32_t m = count - k0 < (uint32_t)kMaxBatch ? count - k0 : (uint32_t)kMaxBatch;
+        for (uint32_t k = 0; k < m; ++k) {
+            const splitzip_item &I = items[k0 + k];
+            chunk[k] = DecItem{I.payload, I.capacity, I.meta, dec_lut_of(I.cb), I.out, I.n};
+        }
+        const int rc = launch_decode(chunk, m, d_status, s);
+        if (rc) return rc;
+    }
+    return SPLITZIP_OK;
 }
 
 }  // extern "C"

@@ -25,7 +25,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = S.lib()
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 13, names
     for name in names:
         assert hasattr(lib, name), name
         assert name in _abi.SIGNATURES, name
@@ -79,3 +79,19 @@ def test_binding_rejects_non_bf16():
     import torch
     with pytest.raises(ValueError):
         S.codec._bits(torch.zeros(4, dtype=torch.float16))
+
+
+def test_batch_host_checks_need_no_device():
+    assert _abi.splitzip_calibrate_batch(None, 3, 0x1000, 1 << 20, 0) == _abi.ERR_INVALID
+    assert _abi.splitzip_encode_batch(None, 3, 0x1000, 1 << 20, 0) == _abi.ERR_INVALID
+    assert _abi.splitzip_decode_batch(None, 3, 0, 0) == _abi.ERR_INVALID
+    items = (_abi.Item * 2)()
+    items[0].x, items[0].n, items[0].cb = 0x1002, 10, 0x2000      # misaligned tensor
+    assert _abi.splitzip_calibrate_batch(items, 2, 0x1000, 1 << 20, 0) == _abi.ERR_INVALID
+    ns = [5, 8192 * 3, 0, 1 << 20]
+    w = _abi.splitzip_workspace_size_batch(ns)
+    assert w >= max(_abi.splitzip_workspace_size(n) for n in ns)
+    assert w >= _abi.splitzip_workspace_size(sum(ns))
+    # 40 tensors run as two launches of at most 32: the larger group decides
+    many = [1 << 16] * 40
+    assert _abi.splitzip_workspace_size_batch(many) == _abi.splitzip_workspace_size(32 << 16)

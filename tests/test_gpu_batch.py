@@ -1,0 +1,152 @@
+"""Batched calibrate / encode / decode (one codebook per tensor) through the
+C ABI: every item must equal the oracle exactly and equal the single-tensor
+calls byte for byte, across batches that need several launches."""
+import numpy as np
+import pytest
+import torch
+
+import lossless_bf16_tensor_splitzip_amd as S
+from lossless_bf16_tensor_splitzip_amd import _abi
+import oracle
+import oracle_pins as P
+import workloads as W
+from test_gpu_parity import DEV, check_codebook, check_meta, host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    S.lib()
+
+
+def mixed_inputs():
+    g = torch.Generator().manual_seed(5)
+    rb = torch.randint(-32768, 32768, (9_999,), dtype=torch.int32, generator=g).to(torch.int16)
+    return [
+        W.gaussian_weight(100_003, seed=50),
+        torch.zeros(0, dtype=torch.bfloat16),
+        W.log_uniform_stress(8192 * 3 + 1, seed=51),
+        W.gaussian_weight(1, seed=52),
+        W.subnormal_gaussian(70_001, seed=53),
+        rb.view(torch.bfloat16),
+        W.kv_layer(seed=2, stream=1, seq=512),
+        W.gaussian_weight(1_000_003, seed=54),
+        W.gaussian_weight(7, seed=55),
+    ]
+
+
+def run_batch(xs_cpu, status=True):
+    xs = [x.reshape(-1).to(DEV) for x in xs_cpu]
+    b = S.Batch(xs)
+    ws = S.Workspace(0, device=DEV, batch_ns=b.ns)
+    b.calibrate(ws)
+    b.encode(ws)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    b.decode(status=st if status else None)
+    torch.cuda.synchronize()
+    return b, int(st.item())
+
+
+def check_item(b, k, x_cpu):
+    xs = host_bits(x_cpu.reshape(-1))
+    ocb = oracle.calibrate(xs)
+    c = S.read_codebook(b.cbs[k])
+    check_codebook(c, ocb)
+    opay, om = oracle.encode(xs, ocb)
+    m = S.read_meta(b.metas[k])
+    check_meta(m, om, ocb)
+    assert b.payloads[k][: m.comp_bytes].cpu().numpy().tobytes() == opay, k
+    assert np.array_equal(host_bits(b.outs[k]), xs), k
+
+
+def test_mixed_batch_matches_oracle():
+    xs = mixed_inputs()
+    b, st = run_batch(xs)
+    assert st == 0
+    for k, x in enumerate(xs):
+        check_item(b, k, x)
+
+
+def test_batch_equals_single_calls():
+    xs = mixed_inputs()
+    b, _ = run_batch(xs, status=False)
+    for k, x in enumerate(xs):
+        n = x.numel()
+        xd = x.reshape(-1).to(DEV)
+        ws = S.Workspace(n, device=DEV)
+        cb = S.calibrate(xd, ws) if n else None
+        if n == 0:
+            continue
+        pay, meta = S.encode(xd, cb, ws)
+        torch.cuda.synchronize()
+        m = S.read_meta(meta)
+        assert bytes(S.read_codebook(cb)) == bytes(S.read_codebook(b.cbs[k]))
+        assert bytes(m) == bytes(S.read_meta(b.metas[k]))
+        assert torch.equal(pay[: m.comp_bytes], b.payloads[k][: m.comp_bytes])
+
+
+def test_batch_of_forty_needs_two_launches():
+    xs = [W.gaussian_weight(20_000 + 517 * k, seed=60 + k) if k % 3 else
+          W.log_uniform_stress(9_000 + 77 * k, seed=60 + k) for k in range(40)]
+    b, st = run_batch(xs)
+    assert st == 0
+    for k in (0, 1, 2, 31, 32, 33, 39):
+        check_item(b, k, xs[k])
+    for k, x in enumerate(xs):
+        assert torch.equal(b.outs[k].view(torch.int16).cpu(), W.bits(x))
+
+
+def test_batch_decode_flags_bad_item():
+    xs = [W.gaussian_weight(50_001, seed=70), W.gaussian_weight(60_001, seed=71)]
+    b, st = run_batch(xs)
+    assert st == 0
+    # break the second item's metadata: its n no longer matches
+    m = S.read_meta(b.metas[1])
+    m.n = m.n - 1
+    b.metas[1].copy_(torch.frombuffer(bytearray(bytes(m)), dtype=torch.uint8).to(DEV))
+    st_t = torch.zeros(1, dtype=torch.int32, device=DEV)
+    b.outs[0].zero_()
+    b.decode(status=st_t)
+    torch.cuda.synchronize()
+    assert int(st_t.item()) & _abi.DEC_BAD_META
+    assert torch.equal(b.outs[0].view(torch.int16).cpu(), W.bits(xs[0]))
+
+
+def test_batch_workspace_too_small():
+    xs = [W.gaussian_weight(3 * 8192, seed=72).to(DEV), W.gaussian_weight(3 * 8192, seed=73).to(DEV)]
+    b = S.Batch(xs)
+    ws = S.Workspace(3 * 8192, device=DEV)      # sized for one tensor, not both
+    b.calibrate(ws)
+    rc = _abi.splitzip_encode_batch(b.items, b.count, ws.ptr(), ws.nbytes,
+                                    torch.cuda.current_stream().cuda_stream)
+    assert rc == _abi.ERR_WORKSPACE
+    torch.cuda.synchronize()
+
+
+def test_workload_kv_stream_batched():
+    """The 4 GiB streaming KV cache through the batched calls, as timed by the
+    benchmark: every tensor round-trips and obeys the size identities; two
+    tensors are compared byte for byte with the oracle."""
+    xs = [W.kv_cache_tensor(layer, kv, device=DEV).reshape(-1)
+          for layer in range(32) for kv in range(2)]
+    b = S.Batch(xs)
+    ws = S.Workspace(0, device=DEV, batch_ns=b.ns)
+    b.calibrate(ws)
+    b.encode(ws)
+    b.decode()
+    torch.cuda.synchronize()
+    for k, x in enumerate(xs):
+        assert torch.equal(b.outs[k].view(torch.int16), x.view(torch.int16)), k
+        m = S.read_meta(b.metas[k])
+        c = S.read_codebook(b.cbs[k])
+        assert m.status == 0 and m.n_esc == m.n - c.covered
+        assert m.comp_bytes == P.closed_form_total(m.n, m.n_esc)
+    for k in (5, 62):
+        xh = host_bits(xs[k])
+        ocb = oracle.calibrate(xh)
+        opay, om = oracle.encode(xh, ocb)
+        m = S.read_meta(b.metas[k])
+        check_meta(m, om, ocb)
+        assert b.payloads[k][: m.comp_bytes].cpu().numpy().tobytes() == opay
