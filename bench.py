@@ -176,7 +176,7 @@ def main():
                     "alg_GBps": round(gbps(alg[k], v), 1)} for k, v in per_call_ms.items()}
     dom = max(phase_ms, key=phase_ms.get)
     kernel_of = {"calibrate": "k_calibrate", "encode": "k_encode (+ k_encode_tail)",
-                 "decode": "k_decode<16>"}
+                 "decode": "k_decode<4>"}
     achieved = gbps(alg[dom], phase_ms[dom])
     roofline = {"bound": "hbm", "kernel": kernel_of[dom], "phase": dom,
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

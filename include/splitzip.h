@@ -165,7 +165,9 @@ int splitzip_encode(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_
 /* Decode a payload back to BF16 bit patterns (page 1, decode_torch): dense
  * 16-entry table lookup plus the escape patch.
  *   d_payload  payload laid out as d_meta describes (device, 16-byte aligned),
- *              payload_bytes readable bytes
+ *              payload_bytes readable bytes; a buffer shorter than the dense
+ *              sections of n elements (splitzip_payload_size(n, 0)) is an
+ *              argument error
  *   d_meta     metadata of the payload (device); meta->n must equal n, the
  *              offsets must follow the layout rule for (n, meta->n_esc) and
  *              comp_bytes must not exceed payload_bytes, else nothing is

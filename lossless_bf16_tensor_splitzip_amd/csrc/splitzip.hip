@@ -34,12 +34,11 @@
 //                 counts it needs) and writes chunk id, chunk-local position
 //                 and raw exponent of every escape at its final rank, then the
 //                 padding and the metadata.
-//   k_decode      one tile of 8192, 16384 or 32768 elements per workgroup (the
-//                 widest that still gives each CU four workgroups): pk + sm ->
-//                 bf16 through a 256-entry pair table in LDS, with the tile's
-//                 escapes found by a wave-wide search of the sorted chunk ids
-//                 and patched in registers (few) or by scatter after the
-//                 16-byte stores (many).
+//   k_decode      one 8192-element tile per workgroup:
+//                 pk + sm -> bf16 through a 256-entry pair table in LDS and
+//                 16-byte stores; meanwhile one wave finds the tile's escapes
+//                 by a search of the sorted chunk ids, and after a workgroup
+//                 barrier they are patched over the dense output.
 //   k_decode_check  (only when a status word is requested) validates every
 //                 escape and re-applies it by scatter, which also makes the
 //                 decode correct for escape streams that are not sorted.
@@ -67,8 +66,8 @@ constexpr int kCalMaxGrid = 512;              // workgroups per tensor, at most
 constexpr int kCalTarget = 2;                 // resident 1024-thread workgroups per CU
 constexpr int kCalGroup = 16;                 // arrivals per first-level counter
 constexpr int kCalCopies = 16;                // global histogram copies per tensor
-constexpr int kRegisterPatchMax = 16;         // escapes per decode tile patched in registers
 constexpr int kTailTiles = 256;               // encode tiles placed per tail workgroup
+constexpr int kDecUnits = 4;                  // decode: units per thread per tile (8192 elements)
 
 // Workspace layout (bytes).  kMaxBatch calibrate slots, each with its
 // counters on separate cache lines and its histogram copies (all of which
@@ -684,31 +683,24 @@ __device__ inline uint64_t lower_bound_wave(const int32_t *cid, uint64_t lo, uin
     return lo + __popcll(__ballot(v < key));
 }
 
-template <int kDecUnits>
+template <int kUnits>
 __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
+    constexpr int kDecUnits = kUnits;
     constexpr int kDecTile = kThreads * kUnit * kDecUnits;
     __shared__ uint32_t pair_lut[256];      // pk byte -> (even exponent, odd exponent << 16)
-    __shared__ uint32_t esc_list[kRegisterPatchMax];
     __shared__ uint64_t range[2];
     const uint64_t gt = blockIdx.x;
     const uint32_t item = find_item(a.tile_start, a.count, gt);
     const DecItem I = a.it[item];
-    Layout L;
-    if (!meta_ok(I, L)) {
-        if (gt == a.tile_start[item] && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
-        return;
-    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const uint64_t e = I.meta->n_esc;
     const uint64_t base = (gt - a.tile_start[item]) * kDecTile;
     const bool full = base + kDecTile <= I.n;
+    // The dense sections depend on n alone (the host checked that the buffer
+    // holds them), so their loads go out before the metadata arrives.
+    const Layout L0 = layout_of(I.n, 0);
     const uint8_t *pk = I.payload;
-    const uint8_t *sm = I.payload + L.off_sm;
-    const int32_t *cid = reinterpret_cast<const int32_t *>(I.payload + L.off_cid);
-    const uint16_t *lpos = reinterpret_cast<const uint16_t *>(I.payload + L.off_lpos);
-    const uint8_t *ev = I.payload + L.off_ev;
-
+    const uint8_t *sm = I.payload + L0.off_sm;
     uint32_t pkw[kDecUnits];
     u32x2 smw[kDecUnits];
     if (full) {
@@ -719,76 +711,21 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
             smw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4 *>(sm + i0));
         }
     }
-    pair_lut[tid] = (uint32_t)I.dec_lut[tid >> 4] | ((uint32_t)I.dec_lut[tid & 15] << 16);
-    if (tid < 64) {
-        // escapes of chunks [c0, c1): the tile's range of the sorted stream
-        uint64_t r0 = 0, r1 = 0;
-        if (e) {
-            const uint64_t nchunks = (I.n + kChunk - 1) / kChunk;
-            const uint64_t c0 = base / kChunk, c1 = c0 + kDecTile / kChunk;
-            r0 = lower_bound_wave(cid, 0, e, (int64_t)c0, (e * c0) / nchunks, lane);
-            r1 = lower_bound_wave(cid, r0, e, (int64_t)c1, r0 + (e * (c1 - c0)) / nchunks, lane);
-        }
-        if (lane == 0) {
-            range[0] = r0;
-            range[1] = r1;
-        }
-    }
-    __syncthreads();
-    const uint64_t r0 = range[0], r1 = range[1];
-    const uint64_t c = r1 - r0;
-
-    if (full && c <= kRegisterPatchMax) {
-        if (tid < c) {
-            // local index in the tile, or all ones when the entry is unusable
-            const uint64_t r = r0 + tid;
-            const int64_t idx = (int64_t)cid[r] * kChunk + lpos[r];
-            const bool inside = idx >= (int64_t)base && idx < (int64_t)(base + kDecTile);
-            esc_list[tid] = inside ? ((uint32_t)(idx - base) | ((uint32_t)ev[r] << 16)) : ~0u;
-        }
-        __syncthreads();
-        u32x4 o[kDecUnits];
-#pragma unroll
-        for (int u = 0; u < kDecUnits; ++u) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t ee = pair_lut[(pkw[u] >> (8 * k)) & 0xFFu];
-                const uint32_t s = smw[u][k >> 1] >> (16 * (k & 1));
-                o[u][k] = join16(s & 0xFFu, ee & 0xFFu) | (join16((s >> 8) & 0xFFu, ee >> 16) << 16);
-            }
-        }
-        for (uint32_t k = 0; k < c; ++k) {
-            const uint32_t entry = esc_list[k];
-            if (entry == ~0u) continue;
-            const uint32_t loc = entry & 0xFFFFu;
-            if (((loc >> 3) & (kThreads - 1)) != (uint32_t)tid) continue;
-            const uint32_t j = loc & 7u;
-            const uint32_t ex = entry >> 16;
-#pragma unroll
-            for (int u = 0; u < kDecUnits; ++u) {
-                if ((loc >> 11) != (uint32_t)u) continue;
-                const uint32_t sw = (j < 4) ? smw[u][0] : smw[u][1];
-                const uint32_t s = (sw >> (8 * (j & 3))) & 0xFFu;
-                const uint32_t val = join16(s, ex);
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    if ((uint32_t)w != (j >> 1)) continue;
-                    o[u][w] = (j & 1) ? ((o[u][w] & 0xFFFFu) | (val << 16))
-                                      : ((o[u][w] & 0xFFFF0000u) | val);
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kDecUnits; ++u) {
-            const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
-            // plain stores: measured faster than non-temporal ones for this stream
-            *reinterpret_cast<u32x4 *>(I.out + i0) = o[u];
-        }
+    const uint32_t lut_entry = (uint32_t)I.dec_lut[tid >> 4] | ((uint32_t)I.dec_lut[tid & 15] << 16);
+    Layout L;
+    if (!meta_ok(I, L)) {   // nothing is written for inconsistent metadata
+        if (gt == a.tile_start[item] && tid == 0 && a.status) atomicOr(a.status, 1);
         return;
     }
+    const uint64_t e = I.meta->n_esc;
+    const int32_t *cid = reinterpret_cast<const int32_t *>(I.payload + L.off_cid);
+    const uint16_t *lpos = reinterpret_cast<const uint16_t *>(I.payload + L.off_lpos);
+    const uint8_t *ev = I.payload + L.off_ev;
 
-    // Many escapes, or the last partial tile: dense stores, then a scatter of
-    // the tile's escapes after the workgroup barrier.
+    pair_lut[tid] = lut_entry;
+    __syncthreads();
+
+    // Dense part first: every element through the pair table, 16-byte stores.
     if (full) {
 #pragma unroll
         for (int u = 0; u < kDecUnits; ++u) {
@@ -800,16 +737,35 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
                 const uint32_t s = smw[u][k >> 1] >> (16 * (k & 1));
                 o[k] = join16(s & 0xFFu, ee & 0xFFu) | (join16((s >> 8) & 0xFFu, ee >> 16) << 16);
             }
+            // plain stores: measured faster than non-temporal ones for this stream
             *reinterpret_cast<u32x4 *>(I.out + i0) = o;
         }
     } else {
         for (uint64_t i = base + tid; i < I.n; i += kThreads) {
             const uint32_t byte = pk[i / 2];
             const uint32_t code = (i & 1) ? (byte & 15u) : (byte >> 4);
-            I.out[i] = (uint16_t)join16(sm[i], I.dec_lut[code]);
+            I.out[i] = (uint16_t)join16(sm[i], pair_lut[code << 4] & 0xFFu);
+        }
+    }
+    if (e == 0) return;
+
+    // Escape patch: the tile's escapes are the chunk ids in [c0, c1) of the
+    // sorted stream, found by one wave while the dense stores drain; they are
+    // applied after the workgroup barrier, which orders them after the dense
+    // stores of every wave of the workgroup.
+    if (tid < 64) {
+        const uint64_t nchunks = (I.n + kChunk - 1) / kChunk;
+        const uint64_t c0 = base / kChunk, c1 = c0 + kDecTile / kChunk;
+        const uint64_t r0 = lower_bound_wave(cid, 0, e, (int64_t)c0, (e * c0) / nchunks, lane);
+        const uint64_t r1 =
+            lower_bound_wave(cid, r0, e, (int64_t)c1, r0 + (e * (c1 - c0)) / nchunks, lane);
+        if (lane == 0) {
+            range[0] = r0;
+            range[1] = r1;
         }
     }
     __syncthreads();
+    const uint64_t r0 = range[0], r1 = range[1];
     for (uint64_t r = r0 + tid; r < r1; r += kThreads) {
         const int64_t idx = (int64_t)cid[r] * kChunk + lpos[r];
         if (idx >= (int64_t)base && idx < (int64_t)(base + kDecTile) && idx < (int64_t)I.n)
@@ -906,11 +862,13 @@ int check_encode_item(const uint16_t *x, uint64_t n, const splitzip_codebook *cb
     return SPLITZIP_OK;
 }
 
-int check_decode_item(const uint8_t *payload, const splitzip_meta *meta, const uint8_t *dec_lut,
-                      const uint16_t *out, uint64_t n) {
+int check_decode_item(const uint8_t *payload, uint64_t payload_bytes, const splitzip_meta *meta,
+                      const uint8_t *dec_lut, const uint16_t *out, uint64_t n) {
     if (n > SPLITZIP_MAX_N || !meta || !aligned(meta, 8) || !dec_lut ||
         (n && (!payload || !aligned(payload, 16) || !out || !aligned(out, 16))))
         return SPLITZIP_ERR_INVALID;
+    // no payload of n elements is shorter than its dense sections
+    if (n && payload_bytes < layout_of(n, 0).total) return SPLITZIP_ERR_INVALID;
     return SPLITZIP_OK;
 }
 
@@ -972,18 +930,10 @@ int launch_encode(const EncItem *items, uint32_t count, const WsPlan &P, uint8_t
     return launched();
 }
 
-// Decode launch for up to kMaxBatch tensors.  Wider tiles keep more bytes in
-// flight per wave; the widest that still gives every CU four workgroups wins.
+// Decode launch for up to kMaxBatch tensors.  8192-element tiles: measured
+// against 16K and 32K tiles (and 4K), they stream fastest once the dense
+// stores no longer wait for the escape search.
 int launch_decode(const DecItem *items, uint32_t count, int32_t *status, hipStream_t s) {
-    int cus = 0;
-    if (!cu_count(cus)) return SPLITZIP_ERR_HIP;
-    uint64_t t16 = 0, t8 = 0;
-    for (uint32_t k = 0; k < count; ++k) {
-        t16 += ceil_div(items[k].n, 16 * 2048);
-        t8 += ceil_div(items[k].n, 8 * 2048);
-    }
-    const uint64_t want = 4 * (uint64_t)cus;
-    const int units = t16 >= want ? 16 : (t8 >= want ? 8 : 4);
     DecArgs a{};
     a.count = count;
     a.status = status;
@@ -991,16 +941,11 @@ int launch_decode(const DecItem *items, uint32_t count, int32_t *status, hipStre
     for (uint32_t k = 0; k < count; ++k) {
         a.it[k] = items[k];
         a.tile_start[k] = tiles;
-        tiles += ceil_div(items[k].n, (uint64_t)units * 2048);
+        tiles += ceil_div(items[k].n, (uint64_t)kDecUnits * kThreads * kUnit);
     }
     a.tile_start[count] = tiles;
     if (tiles) {
-        if (units == 16)
-            k_decode<16><<<(unsigned)tiles, kThreads, 0, s>>>(a);
-        else if (units == 8)
-            k_decode<8><<<(unsigned)tiles, kThreads, 0, s>>>(a);
-        else
-            k_decode<4><<<(unsigned)tiles, kThreads, 0, s>>>(a);
+        k_decode<kDecUnits><<<(unsigned)tiles, kThreads, 0, s>>>(a);
         if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     }
     if (status) {
@@ -1094,7 +1039,7 @@ int splitzip_encode(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_
 int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const splitzip_meta *d_meta,
                     const uint8_t *d_dec_lut, uint16_t *d_out, uint64_t n, int32_t *d_status,
                     void *stream) {
-    if (check_decode_item(d_payload, d_meta, d_dec_lut, d_out, n) ||
+    if (check_decode_item(d_payload, payload_bytes, d_meta, d_dec_lut, d_out, n) ||
         (d_status && !aligned(d_status, 4)))
         return SPLITZIP_ERR_INVALID;
     if (n == 0) return SPLITZIP_OK;
@@ -1153,7 +1098,7 @@ int splitzip_decode_batch(const splitzip_item *items, uint32_t count, int32_t *d
     if ((count && !items) || (d_status && !aligned(d_status, 4))) return SPLITZIP_ERR_INVALID;
     for (uint32_t k = 0; k < count; ++k) {
         const splitzip_item &I = items[k];
-        if (!I.cb || check_decode_item(I.payload, I.meta, dec_lut_of(I.cb), I.out, I.n))
+        if (!I.cb || check_decode_item(I.payload, I.capacity, I.meta, dec_lut_of(I.cb), I.out, I.n))
             return SPLITZIP_ERR_INVALID;
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
