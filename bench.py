@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle budget for the cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy 512 MiB device to device once (a "
+                         "reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -178,9 +181,13 @@ def main():
     kernel_of = {"calibrate": "k_calibrate", "encode": "k_encode (+ k_encode_tail)",
                  "decode": "k_decode<4>"}
     achieved = gbps(alg[dom], phase_ms[dom])
+    counter_key = {"calibrate": "k_calibrate", "encode": "k_encode", "decode": "k_decode<4>"}
     roofline = {"bound": "hbm", "kernel": kernel_of[dom], "phase": dom,
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": counted_traffic(counter_key[dom]),
+                "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+                "alg_bytes_per_launch": alg[dom] // launches}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -219,7 +226,35 @@ def main():
         "context_h200": {"encode_GBps": 613, "decode_GBps": 2182,
                          "note": "pages' figures on LLM KV activations, other hardware"},
     }
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = 512 << 20
     print(json.dumps(line))
+
+
+def counted_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when the kernel source has changed since it was taken."""
+    import hashlib
+
+    src = os.path.join(ROOT, "lossless_bf16_tensor_splitzip_amd", "csrc", "splitzip.hip")
+    summary = os.path.join(ROOT, "profiles", "kv_stream_4gib_hbm_counters.md")
+    try:
+        lines = open(summary).read().splitlines()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    recorded = [ln.split()[1] for ln in lines if ln.startswith("source_sha256 ")]
+    if not recorded or recorded[0] != sha:
+        return None
+    for ln in lines:
+        parts = ln.split()
+        if len(parts) == 3 and parts[0] == "traffic_bytes_per_launch" and parts[1] == kernel:
+            return int(parts[2])
+    return None
 
 
 def cpu_baseline(x_all, budget_s):
