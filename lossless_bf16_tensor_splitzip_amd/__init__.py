@@ -4,14 +4,16 @@ Hand-written HIP kernels behind the C ABI of include/splitzip.h
 (``_lib/libsplitzip.so``); this package is the thin Python binding:
 
 * ``_abi``   -- ctypes view of the C functions (same names) and structs;
-* ``codec``  -- torch-tensor marshalling: Workspace, calibrate, encode, decode.
+* ``codec``  -- torch-tensor marshalling: Workspace, calibrate, encode, decode;
+* ``persist`` -- codebook / metadata JSON and the 0.99 coverage gate.
 
 The method: page "splitzip_codec.py -- SplitZip codec adapter for
 diffusers-dynamic-offloader" and page "SplitZip in DDO -- VMM routes".
 """
 from ._abi import CHUNK, Codebook, Meta, SplitZipError, lib  # noqa: F401
+from . import persist  # noqa: F401
 from .codec import (Batch, Workspace, calibrate, decode, encode, payload_size,  # noqa: F401
                     read_codebook, read_meta)
 
 __all__ = ["CHUNK", "Batch", "Codebook", "Meta", "SplitZipError", "Workspace", "calibrate", "encode",
-           "decode", "payload_size", "read_codebook", "read_meta", "lib"]
+           "decode", "payload_size", "read_codebook", "read_meta", "lib", "persist"]

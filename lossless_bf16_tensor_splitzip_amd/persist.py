@@ -1,0 +1,113 @@
+"""Persistence of codebooks and payload metadata, and the coverage gate.
+
+Host-side policy helpers around the C ABI (no codec arithmetic):
+
+* JSON forms with the keys of the page "splitzip_codec.py -- SplitZip codec
+  adapter for diffusers-dynamic-offloader" (``SplitZipCodebook.to_json``: the
+  coverage and the four tables as base64 of their raw bytes;
+  ``PayloadMeta.to_json``: n, n_pairs, chunk_size, n_esc, comp_bytes, offsets,
+  coverage).  Our extra exact fields (n_codes, covered, total, counts) ride
+  along under their own keys; a reader of the pages' format ignores them.
+* The coverage gate of the page "SplitZip in DDO -- VMM routes" ("Build the
+  cache"; "Invariants common to both routes", item 3): a tensor whose top-16
+  coverage is below 0.99 is left uncompressed, because the size model no
+  longer holds and broad exponent distributions can expand.
+
+A payload is useless without its dec_lut (same page, invariant 2): keep the
+codebook JSON next to every stored payload.
+"""
+from __future__ import annotations
+
+import base64
+import ctypes
+
+from ._abi import Codebook, Meta
+
+COVERAGE_GATE = 0.99
+
+_TABLES = ("enc_lut", "enc_lut_marked", "dec_lut", "common_lut")
+
+
+def _b64(raw: bytes) -> str:
+    return base64.b64encode(raw).decode()
+
+
+def coverage(cb: Codebook) -> float:
+    """Fraction of elements whose exponent has a code (1 for an empty tensor)."""
+    return 1.0 if cb.total == 0 else cb.covered / cb.total
+
+
+def passes_coverage_gate(cb: Codebook, threshold: float = COVERAGE_GATE) -> bool:
+    """True when the tensor should be stored compressed."""
+    return coverage(cb) >= threshold
+
+
+def codebook_to_json(cb: Codebook) -> dict:
+    d = {"coverage": coverage(cb)}
+    for name in _TABLES:
+        d[name] = _b64(bytes(getattr(cb, name)))
+    d["n_codes"] = int(cb.n_codes)
+    d["covered"] = int(cb.covered)
+    d["total"] = int(cb.total)
+    d["counts"] = [int(c) for c in cb.counts]
+    return d
+
+
+def codebook_from_json(d: dict) -> Codebook:
+    """Rebuild a codebook; accepts the pages' four-table form as well (then
+    counts are zero, n_codes comes from common_lut and covered/total from the
+    coverage only approximately: total is 0)."""
+    cb = Codebook()
+    sizes = {"enc_lut": 256, "enc_lut_marked": 256, "dec_lut": 16, "common_lut": 256}
+    for name in _TABLES:
+        raw = base64.b64decode(d[name])
+        if len(raw) != sizes[name]:
+            raise ValueError("%s must hold %d bytes, got %d" % (name, sizes[name], len(raw)))
+        ctypes.memmove(ctypes.addressof(getattr(cb, name)), raw, len(raw))
+    cb.n_codes = int(d["n_codes"]) if "n_codes" in d else sum(bytes(cb.common_lut))
+    cb.covered = int(d.get("covered", 0))
+    cb.total = int(d.get("total", 0))
+    counts = d.get("counts")
+    if counts is not None:
+        if len(counts) != 256:
+            raise ValueError("counts must have 256 entries")
+        for k, c in enumerate(counts):
+            cb.counts[k] = int(c)
+    return cb
+
+
+def meta_to_json(m: Meta) -> dict:
+    return {
+        "n": int(m.n),
+        "n_pairs": int(m.n_pairs),
+        "chunk_size": int(m.chunk_size),
+        "n_esc": int(m.n_esc),
+        "comp_bytes": int(m.comp_bytes),
+        "offsets": [int(v) for v in m.offsets],
+        "coverage": 1.0 if m.total == 0 else m.covered / m.total,
+        "covered": int(m.covered),
+        "total": int(m.total),
+    }
+
+
+def meta_from_json(d: dict) -> Meta:
+    m = Meta()
+    m.n, m.n_pairs = int(d["n"]), int(d["n_pairs"])
+    m.chunk_size, m.n_esc, m.comp_bytes = int(d["chunk_size"]), int(d["n_esc"]), int(d["comp_bytes"])
+    offs = [int(v) for v in d["offsets"]]
+    if len(offs) != 5:
+        raise ValueError("offsets must have 5 entries")
+    for k, v in enumerate(offs):
+        m.offsets[k] = v
+    m.covered = int(d.get("covered", 0))
+    m.total = int(d.get("total", 0))
+    m.status = 0
+    return m
+
+
+def to_device(struct, device) -> "torch.Tensor":  # noqa: F821
+    """Copy a Codebook or Meta into a device uint8 tensor for the C ABI."""
+    import torch
+
+    raw = bytearray(bytes(struct))
+    return torch.frombuffer(raw, dtype=torch.uint8).to(device)

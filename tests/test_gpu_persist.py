@@ -1,0 +1,46 @@
+"""Codebook and metadata that went through their JSON form still decode the
+payload the GPU wrote; the coverage gate agrees with the GPU codebook."""
+import json
+
+import pytest
+import torch
+
+import lossless_bf16_tensor_splitzip_amd as S
+from lossless_bf16_tensor_splitzip_amd import persist
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    S.lib()
+
+
+@pytest.mark.parametrize("make,n,passes", [
+    (W.gaussian_weight, 300_007, True),
+    (W.log_uniform_stress, 200_003, False),
+])
+def test_json_round_trip_decodes(make, n, passes):
+    x = make(n, seed=90).to(DEV)
+    ws = S.Workspace(n, DEV)
+    cb = S.calibrate(x, ws)
+    payload, meta = S.encode(x, cb, ws)
+    host_cb, host_meta = S.read_codebook(cb), S.read_meta(meta)
+    assert persist.passes_coverage_gate(host_cb) is passes
+    cb_json = json.dumps(persist.codebook_to_json(host_cb))
+    meta_json = json.dumps(persist.meta_to_json(host_meta))
+    cb2 = persist.codebook_from_json(json.loads(cb_json))
+    meta2 = persist.meta_from_json(json.loads(meta_json))
+    assert bytes(cb2) == bytes(host_cb)
+    # stored form: the first comp_bytes bytes of the payload only
+    stored = payload[:meta2.comp_bytes].clone()
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = S.decode(stored, persist.to_device(meta2, DEV), persist.to_device(cb2, DEV), n,
+                   status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(out.view(torch.int16), x.view(torch.int16))
