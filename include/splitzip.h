@@ -186,6 +186,35 @@ int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const spli
                     const uint8_t *d_dec_lut, uint16_t *d_out, uint64_t n, int32_t *d_status,
                     void *stream);
 
+/* In-place decode of a payload that occupies the head of its own output
+ * buffer (page "splitzip_codec.py -- SplitZip codec adapter for
+ * diffusers-dynamic-offloader", GpuSplitZipDecoder.decode_slot_into; page
+ * "SplitZip in DDO -- VMM routes", the CUDA route: the transfer lands the
+ * compressed bytes in the weight's own slot and the slot is expanded in place
+ * on the upload stream).
+ *   d_slot      buffer of slot_bytes >= max(2n, splitzip_payload_size(n, 0))
+ *               bytes (device, 16-byte aligned); on entry bytes
+ *               [0, comp_bytes) hold the payload, on completion bytes [0, 2n)
+ *               hold the n decoded BF16 bit patterns
+ *   d_meta      metadata of the payload (device), checked as for
+ *               splitzip_decode; comp_bytes must not exceed slot_bytes nor
+ *               stash_bytes, else the slot is left untouched and status bit 1
+ *               is set
+ *   d_dec_lut   the codebook's 16-entry dec_lut (device)
+ *   d_stash     caller-owned device scratch of stash_bytes >= comp_bytes
+ *               (splitzip_payload_size(n, n_esc)) bytes, 16-byte aligned, not
+ *               overlapping the slot; the inputs of the tiles whose output
+ *               overlaps the payload, and the escape sections, are copied
+ *               there first (about three quarters of the payload)
+ *   d_status    optional, as for splitzip_decode (escapes are re-applied from
+ *               the decoded sign and mantissa)
+ * Two kernels (three with d_status) on `stream`; calls that share a stash
+ * must be ordered on one stream.
+ * Synchronous errors: INVALID (also for overlapping slot and stash), HIP. */
+int splitzip_decode_slot(uint8_t *d_slot, uint64_t slot_bytes, const splitzip_meta *d_meta,
+                         const uint8_t *d_dec_lut, uint64_t n, uint8_t *d_stash,
+                         uint64_t stash_bytes, int32_t *d_status, void *stream);
+
 /* Batched forms of calibrate / encode / decode for many tensors with one
  * codebook each (the per-tensor granularity of page 1, SplitZipCodebook):
  * the same computation as calling the single-tensor function on every item

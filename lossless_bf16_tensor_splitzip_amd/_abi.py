@@ -90,6 +90,7 @@ SIGNATURES = {
     "splitzip_calibrate": (ctypes.c_int, [_P, _U64, _P, _P, _SZ, _P]),
     "splitzip_encode": (ctypes.c_int, [_P, _U64, _P, _P, _U64, _P, _P, _SZ, _P]),
     "splitzip_decode": (ctypes.c_int, [_P, _U64, _P, _P, _P, _U64, _P, _P]),
+    "splitzip_decode_slot": (ctypes.c_int, [_P, _U64, _P, _P, _U64, _P, _U64, _P, _P]),
     "splitzip_workspace_size_batch": (_SZ, [ctypes.POINTER(ctypes.c_uint64), ctypes.c_uint32]),
     "splitzip_calibrate_batch": (ctypes.c_int, [_P, ctypes.c_uint32, _P, _SZ, _P]),
     "splitzip_encode_batch": (ctypes.c_int, [_P, ctypes.c_uint32, _P, _SZ, _P]),
@@ -168,6 +169,12 @@ def splitzip_decode(d_payload: int, payload_bytes: int, d_meta: int, d_dec_lut: 
                     n: int, d_status: int, stream: int) -> int:
     return lib().splitzip_decode(d_payload, payload_bytes, d_meta, d_dec_lut, d_out, n, d_status,
                                  stream)
+
+
+def splitzip_decode_slot(d_slot: int, slot_bytes: int, d_meta: int, d_dec_lut: int, n: int,
+                         d_stash: int, stash_bytes: int, d_status: int, stream: int) -> int:
+    return lib().splitzip_decode_slot(d_slot, slot_bytes, d_meta, d_dec_lut, n, d_stash,
+                                      stash_bytes, d_status, stream)
 
 
 def splitzip_workspace_size_batch(ns) -> int:

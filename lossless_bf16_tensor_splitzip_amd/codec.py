@@ -103,16 +103,41 @@ def decode(payload: torch.Tensor, meta: torch.Tensor, cb_or_dec_lut: torch.Tenso
         out = torch.empty(n, dtype=torch.bfloat16, device=dev)
     if out.dtype is not torch.bfloat16 or not out.is_contiguous() or out.numel() != n:
         raise ValueError("out must be a contiguous bfloat16 tensor of n elements")
-    lut_ptr = cb_or_dec_lut.data_ptr()
-    if cb_or_dec_lut.numel() == CODEBOOK_BYTES:
-        lut_ptr += _abi.DEC_LUT_OFFSET
-    elif cb_or_dec_lut.numel() != 16:
-        raise ValueError("expected a codebook or a 16-entry dec_lut")
+    lut_ptr = _lut_ptr(cb_or_dec_lut)
     st_ptr = 0 if status is None else status.data_ptr()
     _abi._check("splitzip_decode",
                 _abi.splitzip_decode(payload.data_ptr(), payload.numel(), meta.data_ptr(),
                                      lut_ptr, out.data_ptr(), n, st_ptr, _stream(stream, dev)))
     return out
+
+
+def _lut_ptr(cb_or_dec_lut: torch.Tensor) -> int:
+    if cb_or_dec_lut.numel() == CODEBOOK_BYTES:
+        return cb_or_dec_lut.data_ptr() + _abi.DEC_LUT_OFFSET
+    if cb_or_dec_lut.numel() != 16:
+        raise ValueError("expected a codebook or a 16-entry dec_lut")
+    return cb_or_dec_lut.data_ptr()
+
+
+def decode_slot(slot: torch.Tensor, meta: torch.Tensor, cb_or_dec_lut: torch.Tensor, n: int,
+                stash: torch.Tensor, status: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """Decode in place: ``slot`` (contiguous device tensor of any dtype, at
+    least max(2n, payload_size(n, 0)) bytes) holds the payload at its head;
+    afterwards its first 2n bytes hold the n bfloat16 values, returned as a
+    flat bfloat16 view.  ``stash`` is device scratch of at least comp_bytes
+    bytes that does not overlap the slot."""
+    if not slot.is_contiguous():
+        # page 1, decode_slot_into: the slot must be contiguous
+        raise ValueError("the slot tensor must be contiguous")
+    raw = slot.reshape(-1).view(torch.uint8)
+    st_ptr = 0 if status is None else status.data_ptr()
+    _abi._check("splitzip_decode_slot",
+                _abi.splitzip_decode_slot(raw.data_ptr(), raw.numel(), meta.data_ptr(),
+                                          _lut_ptr(cb_or_dec_lut), n, stash.data_ptr(),
+                                          stash.numel() * stash.element_size(), st_ptr,
+                                          _stream(stream, slot.device)))
+    return raw[: 2 * n].view(torch.bfloat16)
 
 
 def read_codebook(cb: torch.Tensor) -> Codebook:

@@ -637,6 +637,13 @@ struct DecArgs {
     uint64_t tile_start[kMaxBatch + 1];   // first decode tile of each tensor
     DecItem it[kMaxBatch];
     int32_t *status;
+    // In-place (slot) decode of it[0] only: the payload sits at the head of
+    // the output buffer.  Pass 1 stashes the inputs of the tiles whose output
+    // overlaps the payload into `stash` (same offsets as in the payload) and
+    // decodes the other tiles directly; pass 2 decodes the stashed tiles.
+    uint8_t *stash;
+    uint64_t other_bytes;   // size of the buffer the pass does not read from
+    uint64_t t_pre;         // pass 2: tiles certain to be stashed
 };
 
 // Metadata must describe exactly the layout of (n, n_esc) and fit the buffer.
@@ -647,6 +654,14 @@ __device__ inline bool meta_ok(const DecItem &I, Layout &L) {
     return m->n_pairs == L.n_pairs && m->offsets[0] == 0 && m->offsets[1] == L.off_sm &&
            m->offsets[2] == L.off_cid && m->offsets[3] == L.off_lpos &&
            m->offsets[4] == L.off_ev && m->comp_bytes == L.total && L.total <= I.payload_bytes;
+}
+
+enum DecMode { kPlain = 0, kSlotStage = 1, kSlotFinish = 2 };
+
+// Slot decode: first tile whose output lies wholly beyond the payload.
+__device__ inline uint64_t slot_split(uint64_t comp_bytes, uint64_t tiles, uint64_t tile) {
+    const uint64_t t = (comp_bytes + 2 * tile - 1) / (2 * tile);
+    return t < tiles ? t : tiles;
 }
 
 // First r in [lo, hi) with cid[r] >= key (hi when none), for chunk ids sorted
@@ -683,8 +698,8 @@ __device__ inline uint64_t lower_bound_wave(const int32_t *cid, uint64_t lo, uin
     return lo + __popcll(__ballot(v < key));
 }
 
-template <int kUnits>
-__global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
+template <int kUnits, int kMode>
+__device__ __forceinline__ void decode_tile(const DecArgs &a) {
     constexpr int kDecUnits = kUnits;
     constexpr int kDecTile = kThreads * kUnit * kDecUnits;
     __shared__ uint32_t pair_lut[256];      // pk byte -> (even exponent, odd exponent << 16)
@@ -694,16 +709,19 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
     const DecItem I = a.it[item];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const uint64_t base = (gt - a.tile_start[item]) * kDecTile;
+    const uint64_t tile = gt - a.tile_start[item];
+    const uint64_t base = tile * kDecTile;
     const bool full = base + kDecTile <= I.n;
     // The dense sections depend on n alone (the host checked that the buffer
-    // holds them), so their loads go out before the metadata arrives.
+    // holds them), so their loads go out before the metadata arrives; in the
+    // second slot pass only for tiles that are certain to be stashed.
     const Layout L0 = layout_of(I.n, 0);
     const uint8_t *pk = I.payload;
     const uint8_t *sm = I.payload + L0.off_sm;
     uint32_t pkw[kDecUnits];
     u32x2 smw[kDecUnits];
-    if (full) {
+    const bool early = full && (kMode != kSlotFinish || tile < a.t_pre);
+    if (early) {
 #pragma unroll
         for (int u = 0; u < kDecUnits; ++u) {
             const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
@@ -713,9 +731,53 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
     }
     const uint32_t lut_entry = (uint32_t)I.dec_lut[tid >> 4] | ((uint32_t)I.dec_lut[tid & 15] << 16);
     Layout L;
-    if (!meta_ok(I, L)) {   // nothing is written for inconsistent metadata
-        if (gt == a.tile_start[item] && tid == 0 && a.status) atomicOr(a.status, 1);
+    if (!meta_ok(I, L) || (kMode != kPlain && L.total > a.other_bytes)) {
+        // nothing is written for inconsistent metadata
+        if (kMode != kSlotFinish && gt == a.tile_start[item] && tid == 0 && a.status)
+            atomicOr(a.status, 1);
         return;
+    }
+    if (kMode != kPlain) {
+        const uint64_t tiles = (I.n + kDecTile - 1) / kDecTile;
+        const uint64_t t_split = slot_split(L.total, tiles, kDecTile);
+        if (kMode == kSlotStage) {
+            // Every workgroup copies its share of the escape sections.
+            const uint64_t esc_bytes = L.total - L.off_cid;
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(I.payload + L.off_cid);
+            uint32_t *dst = reinterpret_cast<uint32_t *>(a.stash + L.off_cid);
+            const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+            for (uint64_t w = gt * kThreads + tid; w < esc_bytes / 4; w += stride) dst[w] = src[w];
+            if (gt == 0 && tid < (int)(esc_bytes & 3)) {
+                const uint64_t b = L.off_cid + (esc_bytes & ~uint64_t(3)) + tid;
+                a.stash[b] = I.payload[b];
+            }
+            if (tile < t_split) {   // output overlaps the payload: stash the inputs
+                if (full) {
+#pragma unroll
+                    for (int u = 0; u < kDecUnits; ++u) {
+                        const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+                        *reinterpret_cast<uint32_t *>(a.stash + i0 / 2) = pkw[u];
+                        *reinterpret_cast<u32x2_a4 *>(a.stash + L0.off_sm + i0) = smw[u];
+                    }
+                } else {
+                    for (uint64_t b = base / 2 + tid; b < L0.n_pairs; b += kThreads)
+                        a.stash[b] = pk[b];
+                    for (uint64_t i = base + tid; i < I.n; i += kThreads)
+                        a.stash[L0.off_sm + i] = sm[i];
+                }
+                return;
+            }
+        } else {
+            if (tile >= t_split) return;   // decoded by the first pass
+            if (full && !early) {
+#pragma unroll
+                for (int u = 0; u < kDecUnits; ++u) {
+                    const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+                    pkw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(pk + i0 / 2));
+                    smw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4 *>(sm + i0));
+                }
+            }
+        }
     }
     const uint64_t e = I.meta->n_esc;
     const int32_t *cid = reinterpret_cast<const int32_t *>(I.payload + L.off_cid);
@@ -773,7 +835,21 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
     }
 }
 
-// Validation (and order-independent re-application) of every escape.
+template <int kUnits>
+__global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) { decode_tile<kUnits, kPlain>(a); }
+
+__global__ __launch_bounds__(kThreads) void k_decode_slot_stage(DecArgs a) {
+    decode_tile<kDecUnits, kSlotStage>(a);
+}
+
+__global__ __launch_bounds__(kThreads) void k_decode_slot_finish(DecArgs a) {
+    decode_tile<kDecUnits, kSlotFinish>(a);
+}
+
+// Validation (and order-independent re-application) of every escape.  The
+// sign and mantissa come from the payload, or, after a slot decode (whose
+// stash holds only part of the sm section), from the decoded output itself.
+template <bool kFromOut>
 __global__ __launch_bounds__(kThreads) void k_decode_check(DecArgs a) {
     const uint64_t gs = (uint64_t)gridDim.x * kThreads;
     int32_t bad = 0;
@@ -781,7 +857,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_check(DecArgs a) {
         const DecItem I = a.it[item];
         if (I.n == 0) continue;
         Layout L;
-        if (!meta_ok(I, L)) continue;   // reported by k_decode
+        if (!meta_ok(I, L) || (kFromOut && L.total > a.other_bytes))
+            continue;   // reported by k_decode
         const uint64_t e = I.meta->n_esc;
         const uint8_t *sm = I.payload + L.off_sm;
         const int32_t *cid = reinterpret_cast<const int32_t *>(I.payload + L.off_cid);
@@ -799,7 +876,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_check(DecArgs a) {
                 const uint64_t prev = (uint64_t)(uint32_t)pc * kChunk + lpos[r - 1];
                 if (pc < 0 || prev >= idx) bad |= 8;
             }
-            I.out[idx] = (uint16_t)join16(sm[idx], ev[r]);
+            const uint32_t keep = kFromOut ? sm_of16(I.out[idx]) : sm[idx];
+            I.out[idx] = (uint16_t)join16(keep, ev[r]);
         }
     }
     if (bad && a.status) atomicOr(a.status, bad);
@@ -954,7 +1032,40 @@ int launch_decode(const DecItem *items, uint32_t count, int32_t *status, hipStre
         uint64_t cgrid = ceil_div(n, 16 * kThreads);
         if (cgrid > 1024) cgrid = 1024;
         if (cgrid == 0) cgrid = 1;
-        k_decode_check<<<(unsigned)cgrid, kThreads, 0, s>>>(a);
+        k_decode_check<false><<<(unsigned)cgrid, kThreads, 0, s>>>(a);
+    }
+    return launched();
+}
+
+// In-place decode of one payload at the head of its output buffer: pass 1
+// stashes the inputs of the tiles whose output overlaps the payload and
+// decodes the rest, pass 2 decodes the stashed tiles over the payload.
+int launch_decode_slot(uint8_t *slot, uint64_t slot_bytes, const splitzip_meta *meta,
+                       const uint8_t *dec_lut, uint64_t n, uint8_t *stash, uint64_t stash_bytes,
+                       int32_t *status, hipStream_t s) {
+    constexpr uint64_t kTile = (uint64_t)kDecUnits * kThreads * kUnit;
+    DecArgs a{};
+    a.count = 1;
+    a.status = status;
+    a.tile_start[0] = 0;
+    a.tile_start[1] = ceil_div(n, kTile);
+    const unsigned tiles = (unsigned)a.tile_start[1];
+    a.it[0] = DecItem{slot, slot_bytes, meta, dec_lut, reinterpret_cast<uint16_t *>(slot), n};
+    a.stash = stash;
+    a.other_bytes = stash_bytes;
+    k_decode_slot_stage<<<tiles, kThreads, 0, s>>>(a);
+    if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
+    a.it[0].payload = stash;
+    a.it[0].payload_bytes = stash_bytes;
+    a.stash = nullptr;
+    a.other_bytes = slot_bytes;
+    a.t_pre = layout_of(n, 0).total / (2 * kTile);
+    k_decode_slot_finish<<<tiles, kThreads, 0, s>>>(a);
+    if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
+    if (status) {
+        uint64_t cgrid = ceil_div(n, 16 * kThreads);
+        if (cgrid > 1024) cgrid = 1024;
+        k_decode_check<true><<<(unsigned)cgrid, kThreads, 0, s>>>(a);
     }
     return launched();
 }
@@ -1045,6 +1156,24 @@ int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const spli
     if (n == 0) return SPLITZIP_OK;
     const DecItem it{d_payload, payload_bytes, d_meta, d_dec_lut, d_out, n};
     return launch_decode(&it, 1, d_status, reinterpret_cast<hipStream_t>(stream));
+}
+
+int splitzip_decode_slot(uint8_t *d_slot, uint64_t slot_bytes, const splitzip_meta *d_meta,
+                         const uint8_t *d_dec_lut, uint64_t n, uint8_t *d_stash,
+                         uint64_t stash_bytes, int32_t *d_status, void *stream) {
+    if (n > SPLITZIP_MAX_N || !d_meta || !aligned(d_meta, 8) || !d_dec_lut ||
+        (d_status && !aligned(d_status, 4)))
+        return SPLITZIP_ERR_INVALID;
+    if (n == 0) return SPLITZIP_OK;
+    const uint64_t dense = layout_of(n, 0).total;
+    const uint64_t need = dense > 2 * n ? dense : 2 * n;
+    if (!d_slot || !aligned(d_slot, 16) || slot_bytes < need || !d_stash ||
+        !aligned(d_stash, 16) || stash_bytes < dense)
+        return SPLITZIP_ERR_INVALID;
+    const uintptr_t a0 = (uintptr_t)d_slot, b0 = (uintptr_t)d_stash;
+    if (a0 < b0 + stash_bytes && b0 < a0 + slot_bytes) return SPLITZIP_ERR_INVALID;
+    return launch_decode_slot(d_slot, slot_bytes, d_meta, d_dec_lut, n, d_stash, stash_bytes,
+                              d_status, reinterpret_cast<hipStream_t>(stream));
 }
 
 int splitzip_calibrate_batch(const splitzip_item *items, uint32_t count, void *d_ws,

@@ -111,3 +111,68 @@ def to_device(struct, device) -> "torch.Tensor":  # noqa: F821
 
     raw = bytearray(bytes(struct))
     return torch.frombuffer(raw, dtype=torch.uint8).to(device)
+
+
+def manifest_entry(name: str, shape, cb: Codebook | None, m: Meta | None) -> dict:
+    """Manifest record of one stored tensor: the codebook travels with the
+    blob (a blob without its dec_lut cannot be decoded).  ``cb``/``m`` None
+    marks a tensor stored raw (it failed the coverage gate)."""
+    d = {"name": name, "dtype": "bfloat16", "shape": [int(v) for v in shape]}
+    if cb is None:
+        d["raw"] = True
+        return d
+    d["raw"] = False
+    d["codebook"] = codebook_to_json(cb)
+    d["meta"] = meta_to_json(m)
+    return d
+
+
+def pack(name: str, x, ws, threshold: float = COVERAGE_GATE):
+    """Gate, encode and verify one device bfloat16 tensor for storage.
+
+    Returns (manifest entry, blob) where blob is a device uint8 tensor of
+    exactly comp_bytes bytes, or a copy of the raw bytes when the tensor fails
+    the coverage gate.  The round trip is checked bit for bit on the device
+    before the blob is handed out (page "SplitZip in DDO -- VMM routes",
+    "Invariants common to both routes", item 4)."""
+    import torch
+
+    from . import codec
+
+    cb_dev = codec.calibrate(x, ws)
+    cb = codec.read_codebook(cb_dev)
+    flat = x.reshape(-1)
+    if not passes_coverage_gate(cb, threshold):
+        return manifest_entry(name, x.shape, None, None), flat.view(torch.uint8).clone()
+    payload, meta_dev = codec.encode(x, cb_dev, ws)
+    m = codec.read_meta(meta_dev)
+    if m.status != 0:
+        raise RuntimeError("encode of %s failed with status %d" % (name, m.status))
+    status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    back = codec.decode(payload, meta_dev, cb_dev, flat.numel(), status=status)
+    if int(status.item()) != 0 or not torch.equal(back.view(torch.int16), flat.view(torch.int16)):
+        raise RuntimeError("round trip of %s is not bit-exact" % name)
+    return manifest_entry(name, x.shape, cb, m), payload[: m.comp_bytes].clone()
+
+
+def unpack(entry: dict, blob, out=None, stream=None):
+    """Rebuild the bfloat16 tensor of a manifest entry from its device blob."""
+    import torch
+
+    from . import codec
+
+    shape = tuple(entry["shape"])
+    n = 1
+    for v in shape:
+        n *= v
+    if entry.get("raw"):
+        t = blob.view(torch.bfloat16)[:n]
+        return t.reshape(shape) if out is None else out.copy_(t.reshape(out.shape))
+    cb = codebook_from_json(entry["codebook"])
+    m = meta_from_json(entry["meta"])
+    if m.n != n:
+        raise ValueError("manifest shape and metadata disagree")
+    flat = None if out is None else out.reshape(-1)
+    res = codec.decode(blob, to_device(m, blob.device), to_device(cb, blob.device), n, out=flat,
+                       stream=stream)
+    return res.reshape(shape) if out is None else out

@@ -25,7 +25,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = S.lib()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), name
         assert name in _abi.SIGNATURES, name
@@ -65,6 +65,15 @@ def test_argument_errors_need_no_device():
     assert _abi.splitzip_calibrate(0, 5, 0, 0, 0, 0) == _abi.ERR_INVALID
     assert _abi.splitzip_encode(0, 5, 0, 0, 0, 0, 0, 0, 0) == _abi.ERR_INVALID
     assert _abi.splitzip_decode(0, 0, 0, 0, 0, 5, 0, 0) == _abi.ERR_INVALID
+    # in-place decode: slot below 2n bytes, stash missing, slot and stash overlapping
+    assert _abi.splitzip_decode_slot(0x10000, 9, 0x2000, 0x3000, 5, 0x40000, 1 << 10, 0, 0) == \
+        _abi.ERR_INVALID
+    assert _abi.splitzip_decode_slot(0x10000, 1 << 10, 0x2000, 0x3000, 5, 0, 1 << 10, 0, 0) == \
+        _abi.ERR_INVALID
+    assert _abi.splitzip_decode_slot(0x10000, 1 << 10, 0x2000, 0x3000, 5, 0x10200, 1 << 10, 0,
+                                     0) == _abi.ERR_INVALID
+    assert _abi.splitzip_decode_slot(0x10000, 1 << 10, 0x2000, 0x3000, 5, 0x40000, 4, 0, 0) == \
+        _abi.ERR_INVALID
     # misaligned tensor pointer
     assert _abi.splitzip_calibrate(0x1002, 5, 0x2000, 0x3000, 1 << 20, 0) == _abi.ERR_INVALID
     # n above the limit

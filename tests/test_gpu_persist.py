@@ -44,3 +44,21 @@ def test_json_round_trip_decodes(make, n, passes):
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     assert torch.equal(out.view(torch.int16), x.view(torch.int16))
+
+
+@pytest.mark.parametrize("make,n,compressed", [
+    (W.gaussian_weight, 3 * 8192 + 11, True),
+    (W.log_uniform_stress, 50_001, False),
+])
+def test_pack_unpack(make, n, compressed):
+    x = make(n, seed=91).reshape(-1).to(DEV)
+    ws = S.Workspace(n, DEV)
+    entry, blob = persist.pack("t", x.reshape(1, -1), ws)
+    entry = json.loads(json.dumps(entry))
+    assert entry["raw"] is (not compressed)
+    if compressed:
+        assert blob.numel() == entry["meta"]["comp_bytes"] < 2 * n
+    back = persist.unpack(entry, blob)
+    torch.cuda.synchronize()
+    assert back.shape == (1, n)
+    assert torch.equal(back.reshape(-1).view(torch.int16), x.view(torch.int16))

@@ -1,0 +1,211 @@
+"""In-place decode: the payload sits at the head of the buffer that receives
+the decoded tensor (page "splitzip_codec.py -- SplitZip codec adapter for
+diffusers-dynamic-offloader", GpuSplitZipDecoder.decode_slot_into), checked
+element by element against the input and the oracle's payload, and a
+host-to-device pipeline that lands payloads in their slots on a copy stream
+while another stream expands them."""
+import numpy as np
+import pytest
+import torch
+
+import lossless_bf16_tensor_splitzip_amd as S
+from lossless_bf16_tensor_splitzip_amd import _abi
+import oracle
+import workloads as W
+from test_gpu_parity import DEV, _say, host_bits, meta_to_device, workspace
+
+pytestmark = pytest.mark.gpu
+
+TILE = 8192
+FILL = 0xA5
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    S.lib()
+
+
+def slot_for(payload: bytes, n: int, extra: int = 0) -> torch.Tensor:
+    size = max(2 * n, S.payload_size(n, 0), len(payload)) + extra
+    slot = torch.full((size,), FILL, dtype=torch.uint8)
+    slot[: len(payload)] = torch.frombuffer(bytearray(payload), dtype=torch.uint8)
+    return slot.to(DEV)
+
+
+def stash_for(comp: int, extra: int = 0) -> torch.Tensor:
+    return torch.full((max(comp, 16) + extra,), 0x5A, dtype=torch.uint8, device=DEV)
+
+
+def oracle_case(x_cpu):
+    xs = host_bits(x_cpu.reshape(-1))
+    ocb = oracle.calibrate(xs)
+    opay, om = oracle.encode(xs, ocb)
+    return xs, ocb, opay, om
+
+
+def run_slot(opay, om, dec_lut, validate=True, extra=0, stash_extra=0):
+    n = om.n
+    slot = slot_for(opay, n, extra)
+    stash = stash_for(om.comp_bytes, stash_extra)
+    lut = torch.tensor(np.asarray(dec_lut, np.uint8)).to(DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV) if validate else None
+    out = S.decode_slot(slot, meta_to_device(om), lut, n, stash, status=st)
+    torch.cuda.synchronize()
+    return slot, host_bits(out), (int(st.item()) if validate else 0)
+
+
+def check_slot(x_cpu, name, extra=0):
+    xs, ocb, opay, om = oracle_case(x_cpu)
+    n = om.n
+    _say("slot case %s n=%d e=%d comp=%d" % (name, n, om.n_esc, om.comp_bytes))
+    for validate in (False, True):
+        slot, out, st = run_slot(opay, om, ocb.dec_lut, validate, extra)
+        assert st == 0
+        assert np.array_equal(out, xs), name
+        # bytes past the decoded tensor and past the payload are left alone
+        tail = slot[max(2 * n, om.comp_bytes):].cpu().numpy()
+        assert (tail == FILL).all(), name
+        if om.comp_bytes > 2 * n:   # payload longer than the tensor: its tail stays
+            assert slot[2 * n: om.comp_bytes].cpu().numpy().tobytes() == opay[2 * n:]
+
+
+SIZES = [1, 2, 3, 7, 8, 9, 1023, 1025, 4095, 8191, 8192, 8193, 2 * TILE, 2 * TILE + 1,
+         3 * TILE - 1, 4 * TILE, 4 * TILE + 5, 11 * TILE + 3, 100_003, 1_000_003]
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_slot_gaussian(n):
+    check_slot(W.gaussian_weight(n, seed=100 + n % 97), "gaussian")
+
+
+@pytest.mark.parametrize("n", [1, 9, 8193, 3 * TILE + 77, 65_537])
+def test_slot_escape_heavy(n):
+    # most exponents escape: the payload is longer than the tensor's 2n bytes
+    check_slot(W.log_uniform_stress(n, seed=200 + n % 89), "escape heavy")
+
+
+@pytest.mark.parametrize("n,esc_every", [(16 * TILE, 40), (16 * TILE + 3, 7), (40 * TILE, 3)])
+def test_slot_split_positions(n, esc_every):
+    """Escape densities that move the first directly decoded tile."""
+    b = host_bits(W.gaussian_weight(n, seed=300 + esc_every)).copy()
+    k = np.arange(0, n, esc_every)
+    # planted values over 40 large exponents: most of them escape
+    b[k] = ((k & 1) << 15) | ((150 + (k // esc_every) % 40) << 7) | (k & 0x7F)
+    x = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+    check_slot(x, "esc every %d" % esc_every, extra=12345)
+
+
+def test_slot_matches_gpu_encode_and_plain_decode():
+    """GPU encode -> payload copied to the slot head -> in-place decode, equal
+    to the out-of-place decode, on one 33,554,432-element KV-cache tensor."""
+    x = W.kv_cache_tensor(3, 1, device=DEV).reshape(-1)
+    n = x.numel()
+    ws = workspace(n)
+    cb = S.calibrate(x, ws)
+    payload, meta = S.encode(x, cb, ws)
+    plain = S.decode(payload, meta, cb, n)
+    m = S.read_meta(meta)
+    slot = torch.empty(2 * n, dtype=torch.uint8, device=DEV)
+    slot[: m.comp_bytes].copy_(payload[: m.comp_bytes])
+    stash = torch.empty(m.comp_bytes, dtype=torch.uint8, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = S.decode_slot(slot, meta, cb, n, stash, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(out.view(torch.int16), x.view(torch.int16))
+    assert torch.equal(plain.view(torch.int16), x.view(torch.int16))
+    # and again without validation, into the same slot
+    slot[: m.comp_bytes].copy_(payload[: m.comp_bytes])
+    out = S.decode_slot(slot, meta, cb, n, stash)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), x.view(torch.int16))
+
+
+def test_slot_rejects_bad_metadata_and_leaves_slot():
+    x = W.gaussian_weight(5 * TILE + 11, seed=400)
+    xs, ocb, opay, om = oracle_case(x)
+    n = om.n
+    lut = torch.tensor(np.asarray(ocb.dec_lut, np.uint8)).to(DEV)
+    # stash shorter than the payload
+    slot = slot_for(opay, n)
+    before = slot.cpu().clone()
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    S.decode_slot(slot, meta_to_device(om), lut, n, stash_for(om.comp_bytes)[: om.comp_bytes - 1],
+                  status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & _abi.DEC_BAD_META
+    assert torch.equal(slot.cpu(), before)
+    # offsets that do not follow the layout
+    bad = oracle.Meta(om.n, om.n_pairs, om.chunk_size, om.n_esc, om.comp_bytes,
+                      (0, om.offsets[1] + 4) + tuple(om.offsets[2:]))
+    st.zero_()
+    S.decode_slot(slot, meta_to_device(bad), lut, n, stash_for(om.comp_bytes), status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & _abi.DEC_BAD_META
+    assert torch.equal(slot.cpu(), before)
+    # non-contiguous slot and overlapping stash are argument errors
+    with pytest.raises(ValueError):
+        S.decode_slot(slot.view(-1, 2)[:, 0], meta_to_device(om), lut, n, stash_for(16))
+    with pytest.raises(S.SplitZipError):
+        S.decode_slot(slot, meta_to_device(om), lut, n, slot[-om.comp_bytes:])
+
+
+def test_slot_unsorted_escape_stream_with_validation():
+    n = 6 * TILE + 77
+    x = torch.full((n,), 1.0, dtype=torch.bfloat16)
+    pos = [3, 900, 5000, 8191, 8192, 9000, 17000, 24000, 40000, n - 1]
+    x[pos] = torch.tensor([2.0, -4.0, 8.0, 0.5, 16.0, -0.25, 3.0, 64.0, -8.0, -2.0],
+                          dtype=torch.bfloat16)
+    xs = host_bits(x)
+    ocb = oracle.calibrate(np.array([0x3F80], np.uint16))
+    opay, om = oracle.encode(xs, ocb)
+    e = om.n_esc
+    buf = bytearray(opay)
+    for sec, width in ((2, 4), (3, 2), (4, 1)):
+        at = om.offsets[sec]
+        items = [bytes(buf[at + width * r: at + width * (r + 1)]) for r in range(e)]
+        for k, r in enumerate(range(e)[::-1]):
+            buf[at + width * k: at + width * (k + 1)] = items[r]
+    _, out, st = run_slot(bytes(buf), om, ocb.dec_lut)
+    assert st & _abi.DEC_NOT_INCREASING
+    assert np.array_equal(out, xs)
+
+
+def test_h2d_pipeline_into_slots():
+    """Payloads in pinned host memory are copied into the heads of their
+    slots on a copy stream; a second stream waits on each copy's event and
+    expands the slot in place, while the next copies proceed."""
+    sizes = [1_000_003, 4 * TILE, 2_500_001, 77, 3_000_000, 8193]
+    xs = [W.gaussian_weight(n, seed=500 + k) if k != 3 else W.log_uniform_stress(n, seed=9)
+          for k, n in enumerate(sizes)]
+    ws = workspace(max(sizes))
+    host, metas, cbs = [], [], []
+    for x in xs:
+        xd = x.to(DEV)
+        cb = S.calibrate(xd, ws)
+        payload, meta = S.encode(xd, cb, ws)
+        m = S.read_meta(meta)
+        h = torch.empty(m.comp_bytes, dtype=torch.uint8, pin_memory=True)
+        h.copy_(payload[: m.comp_bytes].cpu())
+        host.append(h)
+        metas.append(meta)
+        cbs.append(cb)
+    slots = [torch.empty(max(2 * n, h.numel()), dtype=torch.uint8, device=DEV)
+             for n, h in zip(sizes, host)]
+    stash = torch.empty(max(h.numel() for h in host), dtype=torch.uint8, device=DEV)
+    copy_s, dec_s = torch.cuda.Stream(), torch.cuda.Stream()
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()
+    outs = []
+    for k, n in enumerate(sizes):
+        with torch.cuda.stream(copy_s):
+            slots[k][: host[k].numel()].copy_(host[k], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(copy_s)
+        dec_s.wait_event(ev)
+        outs.append(S.decode_slot(slots[k], metas[k], cbs[k], n, stash, status=st, stream=dec_s))
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    for x, out in zip(xs, outs):
+        assert np.array_equal(host_bits(out.cpu()), host_bits(x))

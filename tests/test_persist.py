@@ -77,3 +77,19 @@ def test_coverage_gate():
     _, good = oracle_codebook(W.bits(W.gaussian_weight(100_000, seed=83)).numpy().view(np.uint16))
     _, bad = oracle_codebook(W.bits(W.log_uniform_stress(100_000, seed=84)).numpy().view(np.uint16))
     assert persist.passes_coverage_gate(good) and not persist.passes_coverage_gate(bad)
+
+
+def test_manifest_entry_format():
+    x = W.bits(W.gaussian_weight(4097, seed=85)).numpy().view(np.uint16)
+    ocb, cb = oracle_codebook(x)
+    _, om = oracle.encode(x, ocb)
+    m = S.Meta()
+    m.n, m.n_pairs, m.chunk_size, m.n_esc, m.comp_bytes = om.n, om.n_pairs, 1024, om.n_esc, om.comp_bytes
+    for k in range(5):
+        m.offsets[k] = om.offsets[k]
+    e = json.loads(json.dumps(persist.manifest_entry("w", (17, 241), cb, m)))
+    assert e["raw"] is False and e["shape"] == [17, 241] and e["dtype"] == "bfloat16"
+    assert base64.b64decode(e["codebook"]["dec_lut"]) == ocb.dec_lut.tobytes()
+    assert e["meta"]["comp_bytes"] == om.comp_bytes
+    r = persist.manifest_entry("w", (3,), None, None)
+    assert r["raw"] is True and "codebook" not in r
