@@ -78,7 +78,8 @@ typedef struct splitzip_codebook {
 typedef struct splitzip_meta {
     uint64_t n;          /* elements                                          */
     uint64_t n_pairs;    /* ceil(n/2) = bytes of pk                           */
-    uint64_t chunk_size; /* 1024                                              */
+    uint64_t chunk_size; /* elements per chunk: 1024, or as given to
+                            splitzip_encode_chunked                           */
     uint64_t n_esc;      /* escapes                                           */
     uint64_t comp_bytes; /* payload size; when status is CAPACITY, the size
                             that would have been needed                       */
@@ -162,6 +163,17 @@ int splitzip_encode(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_
                     uint8_t *d_payload, uint64_t capacity, splitzip_meta *d_meta, void *d_ws,
                     size_t ws_bytes, void *stream);
 
+/* Encode with another escape-stream chunk size (page 1, encode, parameter
+ * chunk_size): chunk id = element / chunk_size, local position = element %
+ * chunk_size.  Only the escape sections and meta->chunk_size differ from
+ * splitzip_encode, which is this call with chunk_size = 1024.
+ * Synchronous errors as for splitzip_encode, and INVALID unless
+ * 1 <= chunk_size <= 65536 (positions are uint16) and ceil(n / chunk_size)
+ * <= 2^31 (chunk ids are int32). */
+int splitzip_encode_chunked(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_cb,
+                            uint32_t chunk_size, uint8_t *d_payload, uint64_t capacity,
+                            splitzip_meta *d_meta, void *d_ws, size_t ws_bytes, void *stream);
+
 /* Decode a payload back to BF16 bit patterns (page 1, decode_torch): dense
  * 16-entry table lookup plus the escape patch.
  *   d_payload  payload laid out as d_meta describes (device, 16-byte aligned),
@@ -178,9 +190,10 @@ int splitzip_encode(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_
  *   d_status   optional (may be NULL) device int32 that the caller has set to
  *              0; decode ORs in 1 for inconsistent metadata (see d_meta),
  *              2 when an escape points outside the tensor,
- *              4 when a chunk-local position is >= 1024, 8 when escapes are
- *              not strictly increasing.  Decode never writes outside
- *              d_out[0..n).
+ *              4 when a chunk-local position is >= chunk_size, 8 when escapes
+ *              are not strictly increasing.  Decode never writes outside
+ *              d_out[0..n).  Any chunk_size in [1, 65536] whose chunk ids fit
+ *              int32 is accepted.
  * Synchronous errors: INVALID, HIP. */
 int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const splitzip_meta *d_meta,
                     const uint8_t *d_dec_lut, uint16_t *d_out, uint64_t n, int32_t *d_status,
@@ -219,7 +232,7 @@ int splitzip_decode_slot(uint8_t *d_slot, uint64_t slot_bytes, const splitzip_me
  * codebook each (the per-tensor granularity of page 1, SplitZipCodebook):
  * the same computation as calling the single-tensor function on every item
  * in order, with the tensors of up to 32 consecutive items sharing each
- * kernel launch.  `items` is a host array of `count` entries, read before the
+ * kernel launch (encode uses chunk_size 1024).  `items` is a host array of `count` entries, read before the
  * call returns.  Error codes as for the single-tensor calls; on an argument
  * error nothing is enqueued.  Encode needs a workspace of at least
  * splitzip_workspace_size_batch(n, count) bytes.  For decode, d_status (may

@@ -89,6 +89,8 @@ SIGNATURES = {
     "splitzip_workspace_init": (ctypes.c_int, [_P, _SZ, _P]),
     "splitzip_calibrate": (ctypes.c_int, [_P, _U64, _P, _P, _SZ, _P]),
     "splitzip_encode": (ctypes.c_int, [_P, _U64, _P, _P, _U64, _P, _P, _SZ, _P]),
+    "splitzip_encode_chunked": (ctypes.c_int, [_P, _U64, _P, ctypes.c_uint32, _P, _U64, _P, _P, _SZ,
+                                               _P]),
     "splitzip_decode": (ctypes.c_int, [_P, _U64, _P, _P, _P, _U64, _P, _P]),
     "splitzip_decode_slot": (ctypes.c_int, [_P, _U64, _P, _P, _U64, _P, _U64, _P, _P]),
     "splitzip_workspace_size_batch": (_SZ, [ctypes.POINTER(ctypes.c_uint64), ctypes.c_uint32]),
@@ -163,6 +165,13 @@ def splitzip_calibrate(d_x: int, n: int, d_cb: int, d_ws: int, ws_bytes: int, st
 def splitzip_encode(d_x: int, n: int, d_cb: int, d_payload: int, capacity: int, d_meta: int,
                     d_ws: int, ws_bytes: int, stream: int) -> int:
     return lib().splitzip_encode(d_x, n, d_cb, d_payload, capacity, d_meta, d_ws, ws_bytes, stream)
+
+
+def splitzip_encode_chunked(d_x: int, n: int, d_cb: int, chunk_size: int, d_payload: int,
+                            capacity: int, d_meta: int, d_ws: int, ws_bytes: int,
+                            stream: int) -> int:
+    return lib().splitzip_encode_chunked(d_x, n, d_cb, chunk_size, d_payload, capacity, d_meta,
+                                         d_ws, ws_bytes, stream)
 
 
 def splitzip_decode(d_payload: int, payload_bytes: int, d_meta: int, d_dec_lut: int, d_out: int,

@@ -76,7 +76,7 @@ def calibrate(x: torch.Tensor, ws: Workspace, cb: torch.Tensor | None = None,
 
 
 def encode(x: torch.Tensor, cb: torch.Tensor, ws: Workspace, payload: torch.Tensor | None = None,
-           meta: torch.Tensor | None = None, stream=None):
+           meta: torch.Tensor | None = None, stream=None, chunk_size: int = CHUNK):
     """Encode into ``payload`` (allocated for the worst case when None).
     Returns (payload, meta) as device uint8 tensors; the payload occupies the
     first meta.comp_bytes bytes."""
@@ -86,10 +86,11 @@ def encode(x: torch.Tensor, cb: torch.Tensor, ws: Workspace, payload: torch.Tens
         payload = torch.empty(max(payload_size(n, n), 16), dtype=torch.uint8, device=x.device)
     if meta is None:
         meta = new_meta(x.device)
-    _abi._check("splitzip_encode",
-                _abi.splitzip_encode(xb.data_ptr(), n, cb.data_ptr(), payload.data_ptr(),
-                                     payload.numel(), meta.data_ptr(), ws.ptr(), ws.nbytes,
-                                     _stream(stream, x.device)))
+    _abi._check("splitzip_encode_chunked",
+                _abi.splitzip_encode_chunked(xb.data_ptr(), n, cb.data_ptr(), chunk_size,
+                                             payload.data_ptr(), payload.numel(),
+                                             meta.data_ptr(), ws.ptr(), ws.nbytes,
+                                             _stream(stream, x.device)))
     return payload, meta
 
 

@@ -67,6 +67,8 @@ constexpr int kCalTarget = 2;                 // resident 1024-thread workgroups
 constexpr int kCalGroup = 16;                 // arrivals per first-level counter
 constexpr int kCalCopies = 16;                // global histogram copies per tensor
 constexpr int kTailTiles = 256;               // encode tiles placed per tail workgroup
+constexpr uint64_t kTailDirect = 8;           // tail workgroups per tensor read tile counts directly
+constexpr uint32_t kMaxChunk = 65536;         // chunk-local positions are uint16
 constexpr int kDecUnits = 4;                  // decode: units per thread per tile (8192 elements)
 
 // Workspace layout (bytes).  kMaxBatch calibrate slots, each with its
@@ -80,6 +82,7 @@ constexpr size_t kCalSlot = (kSlotHist + 8 * 256 * kCalCopies + 255) & ~size_t(2
 constexpr size_t kWsTiles = kCalSlot * kMaxBatch;                        // uint32[t_max], stage
 constexpr size_t kWsSlack = 64;
 static_assert(kWsTiles % 256 == 0, "alignment");
+static_assert(kTailTiles == kThreads, "one tile count per tail thread");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -108,16 +111,41 @@ __host__ __device__ inline Layout layout_of(uint64_t n, uint64_t e) {
 struct WsPlan {
     uint64_t t_max;       // encode tiles the workspace holds
     uint64_t off_count;   // uint32[t_max] escapes per tile
+    uint64_t off_bsum;    // uint32[t_max + 64] escapes per tail workgroup
     uint64_t off_stage;   // uint32[t_max * kEncTile] staged escapes
 };
 
+constexpr uint64_t kWsPerTile = 8 + 4 * (uint64_t)kEncTile;   // count, block sum, stage
+constexpr uint64_t kWsFixed = kWsTiles + kWsSlack + 4 * 64;
+
 __host__ inline WsPlan ws_plan(size_t ws_bytes) {
-    WsPlan P{0, 0, 0};
-    if (ws_bytes < kWsTiles + kWsSlack) return P;
-    P.t_max = (ws_bytes - kWsTiles - kWsSlack) / (4 + 4 * (uint64_t)kEncTile);
+    WsPlan P{0, 0, 0, 0};
+    if (ws_bytes < kWsFixed) return P;
+    P.t_max = (ws_bytes - kWsFixed) / kWsPerTile;
     P.off_count = kWsTiles;
-    P.off_stage = align16(kWsTiles + 4 * P.t_max);
+    P.off_bsum = align16(P.off_count + 4 * P.t_max);
+    P.off_stage = align16(P.off_bsum + 4 * (P.t_max + 64));
     return P;
+}
+
+// Chunk id and chunk-local position of element i (shift and mask when the
+// chunk size is a power of two).
+__host__ __device__ inline void chunk_split(uint64_t i, uint32_t chunk, uint64_t &cid,
+                                            uint32_t &pos) {
+    if ((chunk & (chunk - 1)) == 0) {
+        const int sh = __builtin_ctz(chunk);
+        cid = i >> sh;
+        pos = (uint32_t)(i & (chunk - 1));
+    } else {
+        cid = i / chunk;
+        pos = (uint32_t)(i - cid * chunk);
+    }
+}
+
+// A chunk size the wire format can carry for n elements: positions fit
+// uint16 and chunk ids int32.
+__host__ __device__ inline bool chunk_ok(uint64_t n, uint64_t chunk) {
+    return chunk >= 1 && chunk <= kMaxChunk && (n + chunk - 1) / chunk <= (1ull << 31);
 }
 
 __device__ inline uint64_t ld_agent(const uint64_t *p) {
@@ -339,6 +367,7 @@ struct EncItem {
     uint8_t *payload;
     uint64_t capacity;
     splitzip_meta *meta;
+    uint32_t chunk;                       // elements per chunk of the escape stream
 };
 
 struct EncArgs {
@@ -347,6 +376,7 @@ struct EncArgs {
     uint64_t tile_start[kMaxBatch + 1];   // first tile of each tensor
     EncItem it[kMaxBatch];
     uint32_t *tile_count;                 // escapes per tile
+    uint32_t *blk_sum;                    // escapes per tail workgroup, or null
     uint32_t *stage;                      // per tile: (position << 8) | raw exponent
 };
 
@@ -520,6 +550,27 @@ __device__ inline uint32_t block_scan_incl(uint32_t v, uint32_t *lds_waves) {
     return v;
 }
 
+// Escapes per tail workgroup (its kTailTiles tiles), for tensors whose tail
+// workgroups would otherwise each read all of the tensor's tile counts.
+__global__ __launch_bounds__(kThreads) void k_encode_sums(EncArgs a) {
+    __shared__ uint32_t part[kThreads / 64];
+    const uint32_t item = find_item(a.blk_start, a.count, blockIdx.x);
+    const uint32_t blk = blockIdx.x - a.blk_start[item];
+    const uint64_t tfirst = a.tile_start[item];
+    const uint64_t ntiles = a.tile_start[item + 1] - tfirst;
+    const uint64_t t = (uint64_t)blk * kTailTiles + threadIdx.x;
+    uint64_t v = t < ntiles ? a.tile_count[tfirst + t] : 0u;
+    v = wave_sum_u64(v);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = (uint32_t)v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t sum = 0;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) sum += part[w];
+        a.blk_sum[blockIdx.x] = sum;
+    }
+}
+
 // Escape placement: every workgroup sums the tensor's tile counts before its
 // range (its first escape's rank) and over all of the tensor's tiles (the
 // escape count, hence the offsets of local_pos and esc_val), then writes its
@@ -543,20 +594,28 @@ __global__ __launch_bounds__(kThreads) void k_encode_tail(EncArgs a) {
     // this block's own tile counts (issued first, used after the sweep)
     const uint64_t mine_t = t0 + tid;
     const uint32_t mine_c = mine_t < t1 ? counts[mine_t] : 0u;
-    // counts of all the tensor's tiles, 8 loads in flight per thread
+    // counts of all the tensor's tiles (or, for large tensors, the sums per
+    // tail workgroup), 8 loads in flight per thread
+    const uint32_t *src = counts;
+    uint64_t nsrc = ntiles, split = t0;
+    if (a.blk_sum) {
+        src = a.blk_sum + a.blk_start[item];
+        nsrc = a.blk_start[item + 1] - a.blk_start[item];
+        split = blk;
+    }
     uint64_t before = 0, all = 0;
-    for (uint64_t k0 = 0; k0 < ntiles; k0 += 8 * kThreads) {
+    for (uint64_t k0 = 0; k0 < nsrc; k0 += 8 * kThreads) {
         uint32_t c8[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint64_t k = k0 + j * kThreads + tid;
-            c8[j] = k < ntiles ? counts[k] : 0u;
+            c8[j] = k < nsrc ? src[k] : 0u;
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint64_t k = k0 + j * kThreads + tid;
             all += c8[j];
-            before += k < t0 ? c8[j] : 0u;
+            before += k < split ? c8[j] : 0u;
         }
     }
     before = wave_sum_u64(before);
@@ -591,10 +650,13 @@ __global__ __launch_bounds__(kThreads) void k_encode_tail(EncArgs a) {
         const uint32_t word = a.stage[(tfirst + tile) * kEncTile + (k - scan[lo])];
         const uint64_t i = tile * kEncTile + (word >> 8);
         const uint64_t r = P + k;
+        uint64_t cid;
+        uint32_t pos;
+        chunk_split(i, I.chunk, cid, pos);
         if (L.off_cid + 4 * r + 4 <= I.capacity)
-            *reinterpret_cast<uint32_t *>(I.payload + L.off_cid + 4 * r) = (uint32_t)(i / kChunk);
+            *reinterpret_cast<uint32_t *>(I.payload + L.off_cid + 4 * r) = (uint32_t)cid;
         if (fits) {
-            *reinterpret_cast<uint16_t *>(I.payload + L.off_lpos + 2 * r) = (uint16_t)(i % kChunk);
+            *reinterpret_cast<uint16_t *>(I.payload + L.off_lpos + 2 * r) = (uint16_t)pos;
             I.payload[L.off_ev + r] = (uint8_t)(word & 0xFFu);
         }
     }
@@ -604,7 +666,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_tail(EncArgs a) {
         splitzip_meta *m = I.meta;
         m->n = I.n;
         m->n_pairs = L.n_pairs;
-        m->chunk_size = kChunk;
+        m->chunk_size = I.chunk;
         m->n_esc = e;
         m->comp_bytes = L.total;
         m->offsets[0] = 0;
@@ -649,7 +711,7 @@ struct DecArgs {
 // Metadata must describe exactly the layout of (n, n_esc) and fit the buffer.
 __device__ inline bool meta_ok(const DecItem &I, Layout &L) {
     const splitzip_meta *m = I.meta;
-    if (m->n != I.n || m->chunk_size != kChunk || m->n_esc > I.n) return false;
+    if (m->n != I.n || !chunk_ok(I.n, m->chunk_size) || m->n_esc > I.n) return false;
     L = layout_of(I.n, m->n_esc);
     return m->n_pairs == L.n_pairs && m->offsets[0] == 0 && m->offsets[1] == L.off_sm &&
            m->offsets[2] == L.off_cid && m->offsets[3] == L.off_lpos &&
@@ -811,16 +873,28 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     }
     if (e == 0) return;
 
-    // Escape patch: the tile's escapes are the chunk ids in [c0, c1) of the
-    // sorted stream, found by one wave while the dense stores drain; they are
+    // Escape patch: the tile's escapes are among those with chunk ids in
+    // [c0, c1) of the sorted stream (exactly those when tiles and chunks
+    // align), found by one wave while the dense stores drain; they are
     // applied after the workgroup barrier, which orders them after the dense
     // stores of every wave of the workgroup.
+    const uint32_t chunk = (uint32_t)I.meta->chunk_size;
     if (tid < 64) {
-        const uint64_t nchunks = (I.n + kChunk - 1) / kChunk;
-        const uint64_t c0 = base / kChunk, c1 = c0 + kDecTile / kChunk;
-        const uint64_t r0 = lower_bound_wave(cid, 0, e, (int64_t)c0, (e * c0) / nchunks, lane);
-        const uint64_t r1 =
-            lower_bound_wave(cid, r0, e, (int64_t)c1, r0 + (e * (c1 - c0)) / nchunks, lane);
+        // chunks that hold the tile's elements: [c0, c1)
+        uint64_t c0, c1, nchunks;
+        uint32_t p0, p1, pn;
+        chunk_split(base, chunk, c0, p0);
+        chunk_split(base + kDecTile - 1, chunk, c1, p1);
+        chunk_split(I.n - 1, chunk, nchunks, pn);
+        ++c1;
+        ++nchunks;
+        if (c1 > nchunks) c1 = nchunks;
+        // interpolated guesses (hints only: the search is exact for any guess)
+        const double per_chunk = (double)e / (double)nchunks;
+        const uint64_t r0 =
+            lower_bound_wave(cid, 0, e, (int64_t)c0, (uint64_t)(per_chunk * (double)c0), lane);
+        const uint64_t r1 = lower_bound_wave(cid, r0, e, (int64_t)c1,
+                                             r0 + (uint64_t)(per_chunk * (double)(c1 - c0)), lane);
         if (lane == 0) {
             range[0] = r0;
             range[1] = r1;
@@ -829,7 +903,7 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     __syncthreads();
     const uint64_t r0 = range[0], r1 = range[1];
     for (uint64_t r = r0 + tid; r < r1; r += kThreads) {
-        const int64_t idx = (int64_t)cid[r] * kChunk + lpos[r];
+        const int64_t idx = (int64_t)cid[r] * chunk + lpos[r];
         if (idx >= (int64_t)base && idx < (int64_t)(base + kDecTile) && idx < (int64_t)I.n)
             I.out[idx] = (uint16_t)join16(sm[idx], ev[r]);
     }
@@ -860,6 +934,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_check(DecArgs a) {
         if (!meta_ok(I, L) || (kFromOut && L.total > a.other_bytes))
             continue;   // reported by k_decode
         const uint64_t e = I.meta->n_esc;
+        const uint64_t chunk = I.meta->chunk_size;
         const uint8_t *sm = I.payload + L.off_sm;
         const int32_t *cid = reinterpret_cast<const int32_t *>(I.payload + L.off_cid);
         const uint16_t *lpos = reinterpret_cast<const uint16_t *>(I.payload + L.off_lpos);
@@ -868,12 +943,12 @@ __global__ __launch_bounds__(kThreads) void k_decode_check(DecArgs a) {
             const int32_t c = cid[r];
             const uint32_t pos = lpos[r];
             if (c < 0) { bad |= 2; continue; }
-            if (pos >= kChunk) bad |= 4;
-            const uint64_t idx = (uint64_t)c * kChunk + pos;
+            if (pos >= chunk) bad |= 4;
+            const uint64_t idx = (uint64_t)c * chunk + pos;
             if (idx >= I.n) { bad |= 2; continue; }
             if (r > 0) {
                 const int32_t pc = cid[r - 1];
-                const uint64_t prev = (uint64_t)(uint32_t)pc * kChunk + lpos[r - 1];
+                const uint64_t prev = (uint64_t)(uint32_t)pc * chunk + lpos[r - 1];
                 if (pc < 0 || prev >= idx) bad |= 8;
             }
             const uint32_t keep = kFromOut ? sm_of16(I.out[idx]) : sm[idx];
@@ -986,7 +1061,7 @@ int launch_encode(const EncItem *items, uint32_t count, const WsPlan &P, uint8_t
     a.count = count;
     a.tile_count = reinterpret_cast<uint32_t *>(ws + P.off_count);
     a.stage = reinterpret_cast<uint32_t *>(ws + P.off_stage);
-    uint64_t tiles = 0;
+    uint64_t tiles = 0, most = 0;
     uint32_t blks = 0;
     for (uint32_t k = 0; k < count; ++k) {
         a.it[k] = items[k];
@@ -995,6 +1070,7 @@ int launch_encode(const EncItem *items, uint32_t count, const WsPlan &P, uint8_t
         const uint64_t t = enc_tiles(items[k].n);
         tiles += t;
         const uint64_t b = ceil_div(t, kTailTiles);
+        if (b > most) most = b;
         blks += (uint32_t)(b ? b : 1);   // an empty tensor still gets its metadata
     }
     a.tile_start[count] = tiles;
@@ -1002,6 +1078,14 @@ int launch_encode(const EncItem *items, uint32_t count, const WsPlan &P, uint8_t
     if (tiles > P.t_max) return SPLITZIP_ERR_WORKSPACE;
     if (tiles) {
         k_encode<<<(unsigned)tiles, kThreads, 0, s>>>(a);
+        if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
+    }
+    // Past kTailDirect tail workgroups per tensor, one more launch that sums
+    // the counts per workgroup is cheaper than every workgroup reading all of
+    // a tensor's counts.
+    if (most > kTailDirect) {
+        a.blk_sum = reinterpret_cast<uint32_t *>(ws + P.off_bsum);
+        k_encode_sums<<<blks, kThreads, 0, s>>>(a);
         if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     }
     k_encode_tail<<<blks, kThreads, 0, s>>>(a);
@@ -1100,7 +1184,7 @@ size_t splitzip_workspace_size(uint64_t n) {
     uint64_t t = enc_tiles(n);
     if (t == 0) t = 1;
     // smallest size whose plan holds t tiles
-    return (size_t)(kWsTiles + kWsSlack + t * (4 + 4 * (uint64_t)kEncTile));
+    return (size_t)(kWsFixed + t * kWsPerTile);
 }
 
 size_t splitzip_workspace_size_batch(const uint64_t *n, uint32_t count) {
@@ -1112,7 +1196,7 @@ size_t splitzip_workspace_size_batch(const uint64_t *n, uint32_t count) {
         if (t > most) most = t;
     }
     if (most == 0) most = 1;
-    return (size_t)(kWsTiles + kWsSlack + most * (4 + 4 * (uint64_t)kEncTile));
+    return (size_t)(kWsFixed + most * kWsPerTile);
 }
 
 int splitzip_workspace_init(void *d_ws, size_t ws_bytes, void *stream) {
@@ -1133,18 +1217,25 @@ int splitzip_calibrate(const uint16_t *d_x, uint64_t n, splitzip_codebook *d_cb,
                             reinterpret_cast<hipStream_t>(stream));
 }
 
-int splitzip_encode(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_cb,
-                    uint8_t *d_payload, uint64_t capacity, splitzip_meta *d_meta, void *d_ws,
-                    size_t ws_bytes, void *stream) {
+int splitzip_encode_chunked(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_cb,
+                            uint32_t chunk_size, uint8_t *d_payload, uint64_t capacity,
+                            splitzip_meta *d_meta, void *d_ws, size_t ws_bytes, void *stream) {
     const int rc = check_encode_item(d_x, n, d_cb, d_payload, capacity, d_meta);
     if (rc) return rc;
-    if (!d_ws || !aligned(d_ws, 16)) return SPLITZIP_ERR_INVALID;
+    if (!d_ws || !aligned(d_ws, 16) || !chunk_ok(n, chunk_size)) return SPLITZIP_ERR_INVALID;
     const WsPlan P = ws_plan(ws_bytes);
     if (ws_bytes < splitzip_workspace_size(n) || P.t_max < enc_tiles(n))
         return SPLITZIP_ERR_WORKSPACE;
-    const EncItem it{d_x, n, d_cb, d_payload, capacity, d_meta};
+    const EncItem it{d_x, n, d_cb, d_payload, capacity, d_meta, chunk_size};
     return launch_encode(&it, 1, P, reinterpret_cast<uint8_t *>(d_ws),
                          reinterpret_cast<hipStream_t>(stream));
+}
+
+int splitzip_encode(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_cb,
+                    uint8_t *d_payload, uint64_t capacity, splitzip_meta *d_meta, void *d_ws,
+                    size_t ws_bytes, void *stream) {
+    return splitzip_encode_chunked(d_x, n, d_cb, kChunk, d_payload, capacity, d_meta, d_ws,
+                                   ws_bytes, stream);
 }
 
 int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const splitzip_meta *d_meta,
@@ -1214,7 +1305,7 @@ int splitzip_encode_batch(const splitzip_item *items, uint32_t count, void *d_ws
         const uint32_t m = count - k0 < (uint32_t)kMaxBatch ? count - k0 : (uint32_t)kMaxBatch;
         for (uint32_t k = 0; k < m; ++k) {
             const splitzip_item &I = items[k0 + k];
-            chunk[k] = EncItem{I.x, I.n, I.cb, I.payload, I.capacity, I.meta};
+            chunk[k] = EncItem{I.x, I.n, I.cb, I.payload, I.capacity, I.meta, kChunk};
         }
         const int rc = launch_encode(chunk, m, P, reinterpret_cast<uint8_t *>(d_ws), s);
         if (rc) return rc;

@@ -25,7 +25,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = S.lib()
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for name in names:
         assert hasattr(lib, name), name
         assert name in _abi.SIGNATURES, name
@@ -74,6 +74,10 @@ def test_argument_errors_need_no_device():
                                      0) == _abi.ERR_INVALID
     assert _abi.splitzip_decode_slot(0x10000, 1 << 10, 0x2000, 0x3000, 5, 0x40000, 4, 0, 0) == \
         _abi.ERR_INVALID
+    # chunk sizes the wire format cannot carry
+    for chunk, n in ((0, 5), (65537, 5), (1, (1 << 31) + 1)):
+        assert _abi.splitzip_encode_chunked(0x1000, n, 0x2000, chunk, 0x4000, 1 << 40, 0x3000,
+                                            0x5000, 1 << 40, 0) == _abi.ERR_INVALID
     # misaligned tensor pointer
     assert _abi.splitzip_calibrate(0x1002, 5, 0x2000, 0x3000, 1 << 20, 0) == _abi.ERR_INVALID
     # n above the limit

@@ -104,3 +104,35 @@ def test_decode_rejects_corrupt(o):
     bad = oracle.Meta(meta.n, meta.n_pairs, meta.chunk_size, meta.n_esc, meta.comp_bytes,
                       (0, meta.offsets[1] + 4) + tuple(meta.offsets[2:]))
     assert o.decode_status(payload, bad, cb.dec_lut)[0] == oracle.ECORRUPT
+
+
+def test_chunk_size_parameter(o):
+    """Page 1, encode(x, codebook, chunk_size): each escape is stored as (chunk
+    number, position inside the chunk) of its element; only the escape
+    sections depend on the chunk size.  Pinned by planted escape positions and
+    the two degenerate chunkings (one element per chunk; one chunk for all)."""
+    n = 70_001
+    x = np.full(n, 0x3F80, np.uint16)
+    planted = np.array([0, 2, 999, 1000, 1023, 1024, 4097, 12344, 12345, 65535, 65536, n - 1])
+    x[planted] = 0x4000                  # exponent 128 escapes under this codebook
+    cb = o.calibrate(np.array([0x3F80], np.uint16))
+    ref, ref_meta = o.encode(x, cb)
+    dense = ref_meta.offsets[2]
+    for chunk in (1, 3, 1000, 1024, 4096, 12345, 65536):
+        payload, meta = o.encode(x, cb, chunk)
+        assert meta.chunk_size == chunk and meta.n_esc == planted.size
+        assert payload[:dense] == ref[:dense]          # pk, sm and their padding
+        cid = np.frombuffer(payload, "<i4", planted.size, meta.offsets[2])
+        pos = np.frombuffer(payload, "<u2", planted.size, meta.offsets[3])
+        ev = np.frombuffer(payload, np.uint8, planted.size, meta.offsets[4])
+        assert np.array_equal(cid, planted // chunk) and np.array_equal(pos, planted % chunk)
+        assert np.all(ev == 128)
+        if chunk == 1:
+            assert np.all(pos == 0) and np.array_equal(cid, planted)
+        assert np.array_equal(o.decode(payload, meta, cb.dec_lut), x)
+    # one chunk holds everything when chunk_size >= n
+    y = x[:60_000]
+    payload, meta = o.encode(y, cb, 65536)
+    cid = np.frombuffer(payload, "<i4", meta.n_esc, meta.offsets[2])
+    pos = np.frombuffer(payload, "<u2", meta.n_esc, meta.offsets[3])
+    assert np.all(cid == 0) and np.array_equal(pos, planted[planted < 60_000])
