@@ -42,9 +42,98 @@ def parse():
                     help="after the timed steps, copy 512 MiB device to device once (a "
                          "reference for hardware byte counters)")
     ap.add_argument("--no-h2d", action="store_true", help="skip the host-to-device pipeline")
+    ap.add_argument("--no-small", action="store_true", help="skip the small single-tensor configs")
     ap.add_argument("--h2d-tensors", type=int, default=8,
                     help="KV tensors in the host-to-device pipeline sample")
     return ap.parse_args()
+
+
+def d2d_copy(x_all, stream):
+    """Device-to-device copy of the 4 GiB workload (torch's copy kernel): the
+    practical streaming ceiling next to the codec's rates."""
+    import torch
+
+    dst = torch.empty_like(x_all)
+    dst.copy_(x_all)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        dst.copy_(x_all)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    moved = 2 * x_all.numel() * 2
+    del dst
+    return {"ms": round(ms, 4), "bytes_moved": moved, "GBps": round(moved / ms / 1e6, 1),
+            "hbm_frac": round(moved / ms / 1e6 / HBM_PEAK_GBPS, 4), "kernel": "torch copy_"}
+
+
+def small_configs(S, W, dev, stream):
+    """The smaller single-tensor workloads: one call per phase, median GPU
+    time of 20 calls (100 decodes into one output buffer for the linear
+    weight), warm (after 3 warm-up calls; they fit the 256 MB last-level
+    cache) and cold (a 512 MiB buffer is written before each call).  No
+    roofline claim is made for these."""
+    import statistics
+
+    import torch
+
+    cfgs = {
+        "weight_1m_odd": [W.gaussian_weight(1_000_003, seed=0, device=dev)],
+        "kv_layer_8x4096x128": [W.kv_layer(seed=2, stream=kv, device=dev) for kv in (0, 1)],
+        "stress_16m_log_uniform": [W.log_uniform_stress(1 << 24, seed=3, stream=0, device=dev)],
+        "stress_16m_subnormal": [W.subnormal_gaussian(1 << 24, seed=3, stream=1, device=dev)],
+        "linear_weight_12288x3072": [W.weight_with_outliers(seed=4, device=dev)],
+    }
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ws = S.Workspace(1 << 26, device=dev)
+
+    def gpu_time(fn, reps, cold):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(reps):
+            if cold:
+                scrub.fill_(1)
+            torch.cuda._sleep(100_000)      # keep the GPU busy while the call is enqueued
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return statistics.median(ts)
+
+    out = {}
+    for name, xs in cfgs.items():
+        rec = {"tensors": len(xs), "elements": sum(x.numel() for x in xs)}
+        comp = esc = 0
+        for mode in ("warm", "cold"):
+            us = {"calibrate": 0.0, "encode": 0.0, "decode": 0.0}
+            for x in xs:
+                cb = S.calibrate(x, ws)
+                payload, meta = S.encode(x, cb, ws)
+                dst = torch.empty(x.numel(), dtype=torch.bfloat16, device=dev)
+                reps = 100 if name.startswith("linear") else 20
+                us["calibrate"] += gpu_time(lambda: S.calibrate(x, ws, cb=cb), 20, mode == "cold")
+                us["encode"] += gpu_time(lambda: S.encode(x, cb, ws, payload=payload, meta=meta),
+                                         20, mode == "cold")
+                us["decode"] += gpu_time(lambda: S.decode(payload, meta, cb, x.numel(), out=dst),
+                                         reps, mode == "cold")
+                if not torch.equal(dst.view(torch.int16), x.reshape(-1).view(torch.int16)):
+                    raise AssertionError("round trip failed on " + name)
+                if mode == "warm":
+                    m = S.read_meta(meta)
+                    comp += m.comp_bytes
+                    esc += m.n_esc
+            raw = 2 * rec["elements"]
+            rec[mode] = {k: {"us": round(v, 2), "raw_GBps": round(raw / v / 1e3, 1)}
+                         for k, v in us.items()}
+        rec["payload_over_raw"] = round(comp / (2 * rec["elements"]), 6)
+        rec["escape_fraction"] = round(esc / rec["elements"], 6)
+        out[name] = rec
+    del scrub
+    return out
 
 
 def slot_decode_phase(S, batch, metas_h, x_all, stream, passes):
@@ -286,6 +375,8 @@ def main():
                 "alg_bytes_per_launch": alg[dom] // launches}
 
     slot = slot_decode_phase(S, batch, metas_h, x_all, stream, max(2, args.steps // 2))
+    copy = d2d_copy(x_all, stream)
+    small = None if args.no_small else small_configs(S, W, dev, stream)
     h2d = None if args.no_h2d else h2d_pipeline(S, batch, metas_h, x_all, dev, args.h2d_tensors)
 
     cpu = None
@@ -320,7 +411,9 @@ def main():
         "coverage": round(covered / (N * T), 6),
         "phases": phases,
         "per_call_phases": per_call,
+        "d2d_copy": copy,
         "slot_decode": slot,
+        "small_configs": small,
         "h2d_pipeline": h2d,
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -368,19 +461,36 @@ def cpu_baseline(x_all, budget_s):
 
     o = oracle.default()
     done, t_cpu = 0, 0.0
+    t_ph = [0.0, 0.0, 0.0]
     while done < x_all.shape[0] and (t_cpu < budget_s or done == 0):
         xs = x_all[done].view(torch.int16).cpu().numpy().view(np.uint16)
         t0 = time.perf_counter()
         cb = o.calibrate(xs)
+        t1 = time.perf_counter()
         payload, meta = o.encode(xs, cb)
+        t2 = time.perf_counter()
         out = o.decode(payload, meta, cb.dec_lut)
-        t_cpu += time.perf_counter() - t0
+        t3 = time.perf_counter()
+        t_cpu += t3 - t0
+        for k, dt in enumerate((t1 - t0, t2 - t1, t3 - t2)):
+            t_ph[k] += dt
         if not np.array_equal(out, xs):
             raise AssertionError("oracle round trip failed on tensor %d" % done)
         done += 1
     raw = 2 * N * done
+    model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(raw / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d of 64 tensors (calibrate+encode+decode each), %.1f s" % (done, t_cpu)}
+            "sample": "%d of 64 tensors (calibrate+encode+decode each), %.1f s" % (done, t_cpu),
+            "phases_GBps": {k: round(raw / t / 1e9, 3)
+                            for k, t in zip(("calibrate", "encode", "decode"), t_ph)},
+            "host": {"nproc": os.cpu_count(), "cpu": model}}
 
 
 if __name__ == "__main__":

@@ -66,8 +66,28 @@ constexpr int kCalMaxGrid = 512;              // workgroups per tensor, at most
 constexpr int kCalTarget = 2;                 // resident 1024-thread workgroups per CU
 constexpr int kCalGroup = 16;                 // arrivals per first-level counter
 constexpr int kCalCopies = 16;                // global histogram copies per tensor
-constexpr int kTailTiles = 256;               // encode tiles placed per tail workgroup
-constexpr uint64_t kTailDirect = 8;           // tail workgroups per tensor read tile counts directly
+#ifndef SPLITZIP_TAIL_MIN_TILES
+#define SPLITZIP_TAIL_MIN_TILES 8
+#endif
+#ifndef SPLITZIP_TAIL_TARGET_WGS
+#define SPLITZIP_TAIL_TARGET_WGS 2048
+#endif
+#ifndef SPLITZIP_TAIL_DIRECT
+#define SPLITZIP_TAIL_DIRECT 1024
+#endif
+// Encode tiles placed per tail workgroup: chosen per launch, a power of two
+// from kTailMinTiles (enough workgroups to spread dense escape streams over
+// the GPU) to kTailMaxTiles (fewer workgroups when the launch has many tiles).
+constexpr int kTailMinTiles = SPLITZIP_TAIL_MIN_TILES;
+constexpr int kTailMaxTiles = 64;
+constexpr uint64_t kTailTargetWgs = SPLITZIP_TAIL_TARGET_WGS;
+#ifndef SPLITZIP_TAIL_THREADS
+#define SPLITZIP_TAIL_THREADS 256
+#endif
+constexpr int kTailThreads = SPLITZIP_TAIL_THREADS;   // escape placement workgroup
+constexpr int kSuperTiles = 256;              // tiles per second-level count sum
+constexpr uint64_t kTailDirect = SPLITZIP_TAIL_DIRECT;  // up to this many tiles per tensor,
+                                              // tail workgroups read tile counts directly
 constexpr uint32_t kMaxChunk = 65536;         // chunk-local positions are uint16
 constexpr int kDecUnits = 4;                  // decode: units per thread per tile (8192 elements)
 
@@ -82,7 +102,10 @@ constexpr size_t kCalSlot = (kSlotHist + 8 * 256 * kCalCopies + 255) & ~size_t(2
 constexpr size_t kWsTiles = kCalSlot * kMaxBatch;                        // uint32[t_max], stage
 constexpr size_t kWsSlack = 64;
 static_assert(kWsTiles % 256 == 0, "alignment");
-static_assert(kTailTiles == kThreads, "one tile count per tail thread");
+static_assert(kSuperTiles == kThreads && kTailMaxTiles <= 64 && kTailMaxTiles <= kTailThreads &&
+                  kTailThreads % 64 == 0 && (kTailMinTiles & (kTailMinTiles - 1)) == 0 &&
+                  kTailMinTiles <= kTailMaxTiles,
+              "count sums: one tile per thread, whole tail blocks per superblock");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -111,20 +134,22 @@ __host__ __device__ inline Layout layout_of(uint64_t n, uint64_t e) {
 struct WsPlan {
     uint64_t t_max;       // encode tiles the workspace holds
     uint64_t off_count;   // uint32[t_max] escapes per tile
-    uint64_t off_bsum;    // uint32[t_max + 64] escapes per tail workgroup
+    uint64_t off_bsum;    // uint32[t_max / kTailMinTiles + 64] escapes per tail workgroup
+    uint64_t off_ssum;    // uint32[t_max / kSuperTiles + 64] escapes per kSuperTiles tiles
     uint64_t off_stage;   // uint32[t_max * kEncTile] staged escapes
 };
 
 constexpr uint64_t kWsPerTile = 8 + 4 * (uint64_t)kEncTile;   // count, block sum, stage
-constexpr uint64_t kWsFixed = kWsTiles + kWsSlack + 4 * 64;
+constexpr uint64_t kWsFixed = kWsTiles + kWsSlack + 4 * 128;
 
 __host__ inline WsPlan ws_plan(size_t ws_bytes) {
-    WsPlan P{0, 0, 0, 0};
+    WsPlan P{0, 0, 0, 0, 0};
     if (ws_bytes < kWsFixed) return P;
     P.t_max = (ws_bytes - kWsFixed) / kWsPerTile;
     P.off_count = kWsTiles;
     P.off_bsum = align16(P.off_count + 4 * P.t_max);
-    P.off_stage = align16(P.off_bsum + 4 * (P.t_max + 64));
+    P.off_ssum = align16(P.off_bsum + 4 * (P.t_max / kTailMinTiles + 64));
+    P.off_stage = align16(P.off_ssum + 4 * (P.t_max / kSuperTiles + 64));
     return P;
 }
 
@@ -373,10 +398,13 @@ struct EncItem {
 struct EncArgs {
     uint32_t count;
     uint32_t blk_start[kMaxBatch + 1];    // first tail workgroup of each tensor
+    uint32_t sup_start[kMaxBatch + 1];    // first superblock (kSuperTiles tiles) of each tensor
     uint64_t tile_start[kMaxBatch + 1];   // first tile of each tensor
     EncItem it[kMaxBatch];
     uint32_t *tile_count;                 // escapes per tile
     uint32_t *blk_sum;                    // escapes per tail workgroup, or null
+    uint32_t *sup_sum;                    // escapes per superblock, or null
+    uint32_t tail_tiles;                  // tiles per tail workgroup (power of two)
     uint32_t *stage;                      // per tile: (position << 8) | raw exponent
 };
 
@@ -550,36 +578,86 @@ __device__ inline uint32_t block_scan_incl(uint32_t v, uint32_t *lds_waves) {
     return v;
 }
 
-// Escapes per tail workgroup (its kTailTiles tiles), for tensors whose tail
-// workgroups would otherwise each read all of the tensor's tile counts.
+// Count sums for large tensors: one workgroup per superblock of kSuperTiles
+// tiles writes the escapes of each of its tail blocks (tail_tiles tiles) and
+// of the whole superblock, so that a tail workgroup needs only a few dozen
+// loads for its prefix.
 __global__ __launch_bounds__(kThreads) void k_encode_sums(EncArgs a) {
     __shared__ uint32_t part[kThreads / 64];
-    const uint32_t item = find_item(a.blk_start, a.count, blockIdx.x);
-    const uint32_t blk = blockIdx.x - a.blk_start[item];
+    const uint32_t item = find_item(a.sup_start, a.count, blockIdx.x);
+    const uint32_t sup = blockIdx.x - a.sup_start[item];
     const uint64_t tfirst = a.tile_start[item];
     const uint64_t ntiles = a.tile_start[item + 1] - tfirst;
-    const uint64_t t = (uint64_t)blk * kTailTiles + threadIdx.x;
-    uint64_t v = t < ntiles ? a.tile_count[tfirst + t] : 0u;
-    v = wave_sum_u64(v);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = (uint32_t)v;
+    const int tid = threadIdx.x;
+    const uint64_t t = (uint64_t)sup * kSuperTiles + tid;
+    uint32_t v = t < ntiles ? a.tile_count[tfirst + t] : 0u;
+    const uint64_t w = wave_sum_u64(v);
+    if ((tid & 63) == 0) part[tid >> 6] = (uint32_t)w;
+    // sums over aligned groups of tail_tiles (<= 64) lanes
+    const uint32_t tt = a.tail_tiles;
+    uint32_t g = v;
+    for (uint32_t off = 1; off < tt; off <<= 1) g += __shfl_xor(g, (int)off, 64);
     __syncthreads();
-    if (threadIdx.x == 0) {
+    const uint64_t blk = (uint64_t)sup * (kSuperTiles / tt) + tid / tt;
+    const uint64_t nblk = a.blk_start[item + 1] - a.blk_start[item];
+    if (tid % tt == 0 && blk < nblk) a.blk_sum[a.blk_start[item] + blk] = g;
+    if (tid == 0) {
         uint32_t sum = 0;
 #pragma unroll
-        for (int w = 0; w < kThreads / 64; ++w) sum += part[w];
-        a.blk_sum[blockIdx.x] = sum;
+        for (int k = 0; k < kThreads / 64; ++k) sum += part[k];
+        a.sup_sum[blockIdx.x] = sum;
     }
 }
 
-// Escape placement: every workgroup sums the tensor's tile counts before its
-// range (its first escape's rank) and over all of the tensor's tiles (the
-// escape count, hence the offsets of local_pos and esc_val), then writes its
-// tiles' escapes at their final ranks.  The tensor's first tail workgroup
+// Sum of src[0, n) and of src[0, split), 8 loads in flight per thread,
+// reduced over the workgroup (results in red[0] / red[1] after a barrier).
+__device__ inline void sum_prefix(const uint32_t *src, uint64_t n, uint64_t split,
+                                  uint64_t &before, uint64_t &all) {
+    const int tid = threadIdx.x;
+    for (uint64_t k0 = 0; k0 < n; k0 += 8 * kTailThreads) {
+        uint32_t c8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint64_t k = k0 + j * kTailThreads + tid;
+            c8[j] = k < n ? src[k] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint64_t k = k0 + j * kTailThreads + tid;
+            all += c8[j];
+            before += k < split ? c8[j] : 0u;
+        }
+    }
+}
+
+// Escape of rank r, staged as (position in tile << 8) | raw exponent for the
+// tile starting at element tile_base: chunk id, chunk-local position and raw
+// exponent at their offsets (the chunk ids that fit are written even when
+// the payload does not fit, as the capacity error reports).
+__device__ inline void place_escape(const EncItem &I, const Layout &L, bool fits,
+                                    uint64_t tile_base, uint32_t word, uint64_t r) {
+    const uint64_t i = tile_base + (word >> 8);
+    uint64_t cid;
+    uint32_t pos;
+    chunk_split(i, I.chunk, cid, pos);
+    if (L.off_cid + 4 * r + 4 <= I.capacity)
+        *reinterpret_cast<uint32_t *>(I.payload + L.off_cid + 4 * r) = (uint32_t)cid;
+    if (fits) {
+        *reinterpret_cast<uint16_t *>(I.payload + L.off_lpos + 2 * r) = (uint16_t)pos;
+        I.payload[L.off_ev + r] = (uint8_t)(word & 0xFFu);
+    }
+}
+
+// Escape placement: every workgroup takes tail_tiles tiles of one tensor,
+// finds the rank of its first escape and the tensor's escape count (from the
+// tile counts, or for large tensors from the superblock and block sums),
+// then copies each tile's staged escapes to their final ranks as chunk id,
+// chunk-local position and raw exponent.  The tensor's first tail workgroup
 // writes the padding and the metadata.
-__global__ __launch_bounds__(kThreads) void k_encode_tail(EncArgs a) {
-    __shared__ uint64_t red[2][kThreads / 64];
-    __shared__ uint32_t waves[kThreads / 64];
-    __shared__ uint32_t scan[kTailTiles + 1];
+__global__ __launch_bounds__(kTailThreads) void k_encode_tail(EncArgs a) {
+    __shared__ uint64_t red[2][kTailThreads / 64];
+    __shared__ uint32_t waves[kTailThreads / 64];
+    __shared__ uint32_t scan[kTailMaxTiles + 1];
     const uint32_t item = find_item(a.blk_start, a.count, blockIdx.x);
     const EncItem I = a.it[item];
     const uint32_t blk = blockIdx.x - a.blk_start[item];
@@ -588,35 +666,24 @@ __global__ __launch_bounds__(kThreads) void k_encode_tail(EncArgs a) {
     const uint32_t *counts = a.tile_count + tfirst;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint64_t t0 = (uint64_t)blk * kTailTiles;
-    const uint64_t t1 = t0 + kTailTiles < ntiles ? t0 + kTailTiles : ntiles;
+    const uint32_t tt = a.tail_tiles;
+    const uint64_t t0 = (uint64_t)blk * tt;
+    const uint64_t t1 = t0 + tt < ntiles ? t0 + tt : ntiles;
 
     // this block's own tile counts (issued first, used after the sweep)
     const uint64_t mine_t = t0 + tid;
-    const uint32_t mine_c = mine_t < t1 ? counts[mine_t] : 0u;
-    // counts of all the tensor's tiles (or, for large tensors, the sums per
-    // tail workgroup), 8 loads in flight per thread
-    const uint32_t *src = counts;
-    uint64_t nsrc = ntiles, split = t0;
-    if (a.blk_sum) {
-        src = a.blk_sum + a.blk_start[item];
-        nsrc = a.blk_start[item + 1] - a.blk_start[item];
-        split = blk;
-    }
+    const uint32_t mine_c = ((uint32_t)tid < tt && mine_t < t1) ? counts[mine_t] : 0u;
     uint64_t before = 0, all = 0;
-    for (uint64_t k0 = 0; k0 < nsrc; k0 += 8 * kThreads) {
-        uint32_t c8[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint64_t k = k0 + j * kThreads + tid;
-            c8[j] = k < nsrc ? src[k] : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint64_t k = k0 + j * kThreads + tid;
-            all += c8[j];
-            before += k < split ? c8[j] : 0u;
-        }
+    if (a.sup_sum) {
+        // superblocks before this one and in total, then the blocks of this
+        // superblock before this block
+        const uint64_t sup = t0 / kSuperTiles;
+        sum_prefix(a.sup_sum + a.sup_start[item], a.sup_start[item + 1] - a.sup_start[item], sup,
+                   before, all);
+        const uint64_t b0 = sup * (kSuperTiles / tt);
+        if (b0 + tid < blk) before += a.blk_sum[a.blk_start[item] + b0 + tid];
+    } else {
+        sum_prefix(counts, ntiles, t0, before, all);
     }
     before = wave_sum_u64(before);
     all = wave_sum_u64(all);
@@ -626,38 +693,65 @@ __global__ __launch_bounds__(kThreads) void k_encode_tail(EncArgs a) {
     }
     // exclusive scan of this block's tile counts
     const uint32_t incl = block_scan_incl(mine_c, waves);
-    scan[tid + 1] = incl;
+    if ((uint32_t)tid < tt) scan[tid + 1] = incl;
     if (tid == 0) scan[0] = 0;
     __syncthreads();
     uint64_t P = 0, e = 0;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) {
+    for (int w = 0; w < kTailThreads / 64; ++w) {
         P += red[0][w];
         e += red[1][w];
     }
     const Layout L = layout_of(I.n, e);
     const bool fits = L.total <= I.capacity;
-    const uint32_t mine_total = t1 > t0 ? scan[t1 - t0] : 0u;
 
-    for (uint32_t k = tid; k < mine_total; k += kThreads) {
-        // tile j of this block holding the k-th escape: last j with scan[j] <= k
-        uint32_t lo = 0, hi = (uint32_t)(t1 - t0);
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (scan[mid] <= k) lo = mid; else hi = mid;
+    const uint32_t nt = (uint32_t)(t1 - t0);
+    const uint32_t total = scan[nt];
+    if (total <= 8 * kTailThreads) {
+        // few escapes: one pass over all of them, the tile of escape k found
+        // in the block's scan, 8 staged loads in flight
+        uint32_t w8[8], j8[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t k = q * kTailThreads + tid;
+            uint32_t lo = 0;
+            w8[q] = 0;
+            if (k < total) {
+                uint32_t hi = nt;   // last j with scan[j] <= k
+                while (hi - lo > 1) {
+                    const uint32_t mid = (lo + hi) >> 1;
+                    if (scan[mid] <= k) lo = mid; else hi = mid;
+                }
+                w8[q] = a.stage[(tfirst + t0 + lo) * kEncTile + (k - scan[lo])];
+            }
+            j8[q] = lo;
         }
-        const uint64_t tile = t0 + lo;
-        const uint32_t word = a.stage[(tfirst + tile) * kEncTile + (k - scan[lo])];
-        const uint64_t i = tile * kEncTile + (word >> 8);
-        const uint64_t r = P + k;
-        uint64_t cid;
-        uint32_t pos;
-        chunk_split(i, I.chunk, cid, pos);
-        if (L.off_cid + 4 * r + 4 <= I.capacity)
-            *reinterpret_cast<uint32_t *>(I.payload + L.off_cid + 4 * r) = (uint32_t)cid;
-        if (fits) {
-            *reinterpret_cast<uint16_t *>(I.payload + L.off_lpos + 2 * r) = (uint16_t)pos;
-            I.payload[L.off_ev + r] = (uint8_t)(word & 0xFFu);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t k = q * kTailThreads + tid;
+            if (k >= total) break;
+            place_escape(I, L, fits, (t0 + j8[q]) * kEncTile, w8[q], P + k);
+        }
+    } else {
+        // many: tile by tile, every thread takes every kTailThreads-th escape
+        // of the tile, 8 staged loads in flight
+        for (uint32_t j = 0; j < nt; ++j) {
+            const uint32_t k_first = scan[j], c = scan[j + 1] - k_first;
+            const uint32_t *st = a.stage + (tfirst + t0 + j) * kEncTile;
+            for (uint32_t k0 = 0; k0 < c; k0 += 8 * kTailThreads) {
+                uint32_t w8[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint32_t k = k0 + q * kTailThreads + tid;
+                    w8[q] = k < c ? st[k] : 0u;
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint32_t k = k0 + q * kTailThreads + tid;
+                    if (k >= c) break;
+                    place_escape(I, L, fits, (t0 + j) * kEncTile, w8[q], P + k_first + k);
+                }
+            }
         }
     }
     if (blk == 0 && tid == 0) {
@@ -743,6 +837,24 @@ __device__ inline uint64_t lower_bound_wave(const int32_t *cid, uint64_t lo, uin
         if (!left_ok) hi = wlo;              // answer in [lo, wlo]
         else lo = wlo + 64;                  // whole window below the key
     }
+    // Then 64 samples 64 apart around the guess (dense streams, where the
+    // guess is off by more than the window): brackets the answer within 64.
+    if (hi > lo + 64 * 64) {
+        uint64_t blo = guess > 32 * 64 ? guess - 32 * 64 : 0;
+        if (blo < lo) blo = lo;
+        if (blo > hi - 64 * 64) blo = hi - 64 * 64;
+        const uint64_t sx = blo + (uint64_t)lane * 64;
+        const int64_t v = cid[sx];
+        const uint32_t k = __popcll(__ballot(v < key));
+        const uint64_t s_lo = __shfl(sx, k > 0 ? (int)k - 1 : 0, 64);
+        const uint64_t s_hi = __shfl(sx, k < 64 ? (int)k : 63, 64);
+        if (k == 0) hi = blo;                // answer in [lo, blo]
+        else if (k == 64) lo = s_lo + 1;     // every sample below the key
+        else {
+            lo = s_lo + 1;                   // answer in (s_lo, s_hi]
+            hi = s_hi;
+        }
+    }
     while (hi > lo + 63) {
         const uint64_t span = hi - lo;
         const uint64_t s = lo + (span * (uint64_t)(lane + 1)) / 65;
@@ -766,6 +878,7 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     constexpr int kDecTile = kThreads * kUnit * kDecUnits;
     __shared__ uint32_t pair_lut[256];      // pk byte -> (even exponent, odd exponent << 16)
     __shared__ uint64_t range[2];
+    __shared__ uint32_t sm_tile[kDecTile / 4];   // sm bytes of a tile with many escapes
     const uint64_t gt = blockIdx.x;
     const uint32_t item = find_item(a.tile_start, a.count, gt);
     const DecItem I = a.it[item];
@@ -902,10 +1015,42 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     }
     __syncthreads();
     const uint64_t r0 = range[0], r1 = range[1];
-    for (uint64_t r = r0 + tid; r < r1; r += kThreads) {
-        const int64_t idx = (int64_t)cid[r] * chunk + lpos[r];
-        if (idx >= (int64_t)base && idx < (int64_t)(base + kDecTile) && idx < (int64_t)I.n)
-            I.out[idx] = (uint16_t)join16(sm[idx], ev[r]);
+    // A tile with many escapes keeps its sm bytes (still in registers) in LDS
+    // for the patch, instead of reading each one back from memory.
+    const bool staged = full && r1 - r0 > 2 * kThreads;
+    if (staged) {
+#pragma unroll
+        for (int u = 0; u < kDecUnits; ++u) {
+            const int o = u * (kThreads * kUnit) + tid * kUnit;
+            sm_tile[o / 4] = smw[u].x;
+            sm_tile[o / 4 + 1] = smw[u].y;
+        }
+        __syncthreads();
+    }
+    const uint8_t *sm_lds = reinterpret_cast<const uint8_t *>(sm_tile);
+    // 4 escapes per thread in flight: their stream entries, then their sm
+    // bytes, then the stores
+    for (uint64_t rb = r0; rb < r1; rb += 4 * kThreads) {
+        int64_t idx[4];
+        uint32_t evv[4], smv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint64_t r = rb + q * kThreads + tid;
+            idx[q] = -1;
+            evv[q] = 0;
+            if (r < r1) {
+                const int64_t v = (int64_t)cid[r] * chunk + lpos[r];
+                evv[q] = ev[r];
+                if (v >= (int64_t)base && v < (int64_t)(base + kDecTile) && v < (int64_t)I.n)
+                    idx[q] = v;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            smv[q] = idx[q] < 0 ? 0u : (staged ? sm_lds[idx[q] - (int64_t)base] : sm[idx[q]]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (idx[q] >= 0) I.out[idx[q]] = (uint16_t)join16(smv[q], evv[q]);
     }
 }
 
@@ -1062,33 +1207,45 @@ int launch_encode(const EncItem *items, uint32_t count, const WsPlan &P, uint8_t
     a.tile_count = reinterpret_cast<uint32_t *>(ws + P.off_count);
     a.stage = reinterpret_cast<uint32_t *>(ws + P.off_stage);
     uint64_t tiles = 0, most = 0;
-    uint32_t blks = 0;
+    for (uint32_t k = 0; k < count; ++k) {
+        const uint64_t t = enc_tiles(items[k].n);
+        tiles += t;
+        if (t > most) most = t;
+    }
+    uint32_t tt = kTailMinTiles;
+    while (tt < (uint32_t)kTailMaxTiles && tiles / (2 * tt) >= kTailTargetWgs) tt *= 2;
+    a.tail_tiles = tt;
+    tiles = 0;
+    uint32_t blks = 0, sups = 0;
     for (uint32_t k = 0; k < count; ++k) {
         a.it[k] = items[k];
         a.tile_start[k] = tiles;
         a.blk_start[k] = blks;
+        a.sup_start[k] = sups;
         const uint64_t t = enc_tiles(items[k].n);
         tiles += t;
-        const uint64_t b = ceil_div(t, kTailTiles);
-        if (b > most) most = b;
+        const uint64_t b = ceil_div(t, tt);
         blks += (uint32_t)(b ? b : 1);   // an empty tensor still gets its metadata
+        sups += (uint32_t)ceil_div(t, kSuperTiles);
     }
     a.tile_start[count] = tiles;
     a.blk_start[count] = blks;
+    a.sup_start[count] = sups;
     if (tiles > P.t_max) return SPLITZIP_ERR_WORKSPACE;
     if (tiles) {
         k_encode<<<(unsigned)tiles, kThreads, 0, s>>>(a);
         if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     }
-    // Past kTailDirect tail workgroups per tensor, one more launch that sums
-    // the counts per workgroup is cheaper than every workgroup reading all of
-    // a tensor's counts.
+    // Past kTailDirect tiles per tensor, one more launch that sums the counts
+    // per tail block and per superblock is cheaper than every tail workgroup
+    // reading all of a tensor's counts.
     if (most > kTailDirect) {
         a.blk_sum = reinterpret_cast<uint32_t *>(ws + P.off_bsum);
-        k_encode_sums<<<blks, kThreads, 0, s>>>(a);
+        a.sup_sum = reinterpret_cast<uint32_t *>(ws + P.off_ssum);
+        k_encode_sums<<<sups, kThreads, 0, s>>>(a);
         if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     }
-    k_encode_tail<<<blks, kThreads, 0, s>>>(a);
+    k_encode_tail<<<blks, kTailThreads, 0, s>>>(a);
     return launched();
 }
 
