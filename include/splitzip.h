@@ -106,6 +106,19 @@ typedef struct splitzip_item {
     uint16_t *out;         /* decoded output (16-byte aligned)                       */
 } splitzip_item;
 
+/* One payload of a batched in-place decode (splitzip_decode_slot_batch);
+ * the array lives in host memory, the pointers are device pointers with the
+ * meaning they have for splitzip_decode_slot. */
+typedef struct splitzip_slot_item {
+    uint8_t *slot;               /* payload at its head; receives the n values   */
+    uint64_t slot_bytes;
+    const splitzip_meta *meta;
+    const uint8_t *dec_lut;      /* the codebook's 16-entry dec_lut              */
+    uint64_t n;
+    uint8_t *stash;              /* scratch of stash_bytes >= comp_bytes         */
+    uint64_t stash_bytes;
+} splitzip_slot_item;
+
 /* ABI version of the loaded library (SPLITZIP_ABI_VERSION). */
 int splitzip_abi_version(void);
 
@@ -227,6 +240,16 @@ int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const spli
 int splitzip_decode_slot(uint8_t *d_slot, uint64_t slot_bytes, const splitzip_meta *d_meta,
                          const uint8_t *d_dec_lut, uint64_t n, uint8_t *d_stash,
                          uint64_t stash_bytes, int32_t *d_status, void *stream);
+
+/* In-place decode of a group of slots (page "SplitZip in DDO -- VMM routes",
+ * "Files added": the staging route decodes a group of slots at a time): the
+ * same result as splitzip_decode_slot on every item in order, with up to 32
+ * items sharing each pair of launches.  Each item needs its own stash; no
+ * slot or stash may overlap another item's buffers.  d_status (optional)
+ * collects the status bits of all items.
+ * Synchronous errors: INVALID (any item; nothing is enqueued), HIP. */
+int splitzip_decode_slot_batch(const splitzip_slot_item *items, uint32_t count, int32_t *d_status,
+                               void *stream);
 
 /* Batched forms of calibrate / encode / decode for many tensors with one
  * codebook each (the per-tensor granularity of page 1, SplitZipCodebook):

@@ -74,6 +74,19 @@ class Item(ctypes.Structure):
     ]
 
 
+class SlotItem(ctypes.Structure):
+    """Mirror of splitzip_slot_item (one payload of a batched in-place decode)."""
+    _fields_ = [
+        ("slot", ctypes.c_void_p),
+        ("slot_bytes", ctypes.c_uint64),
+        ("meta", ctypes.c_void_p),
+        ("dec_lut", ctypes.c_void_p),
+        ("n", ctypes.c_uint64),
+        ("stash", ctypes.c_void_p),
+        ("stash_bytes", ctypes.c_uint64),
+    ]
+
+
 DEC_LUT_OFFSET = Codebook.dec_lut.offset
 
 # name -> (restype, argtypes), exactly the functions of include/splitzip.h
@@ -93,6 +106,7 @@ SIGNATURES = {
                                                _P]),
     "splitzip_decode": (ctypes.c_int, [_P, _U64, _P, _P, _P, _U64, _P, _P]),
     "splitzip_decode_slot": (ctypes.c_int, [_P, _U64, _P, _P, _U64, _P, _U64, _P, _P]),
+    "splitzip_decode_slot_batch": (ctypes.c_int, [_P, ctypes.c_uint32, _P, _P]),
     "splitzip_workspace_size_batch": (_SZ, [ctypes.POINTER(ctypes.c_uint64), ctypes.c_uint32]),
     "splitzip_calibrate_batch": (ctypes.c_int, [_P, ctypes.c_uint32, _P, _SZ, _P]),
     "splitzip_encode_batch": (ctypes.c_int, [_P, ctypes.c_uint32, _P, _SZ, _P]),
@@ -184,6 +198,10 @@ def splitzip_decode_slot(d_slot: int, slot_bytes: int, d_meta: int, d_dec_lut: i
                          d_stash: int, stash_bytes: int, d_status: int, stream: int) -> int:
     return lib().splitzip_decode_slot(d_slot, slot_bytes, d_meta, d_dec_lut, n, d_stash,
                                       stash_bytes, d_status, stream)
+
+
+def splitzip_decode_slot_batch(items, count: int, d_status: int, stream: int) -> int:
+    return lib().splitzip_decode_slot_batch(_items_ptr(items), count, d_status, stream)
 
 
 def splitzip_workspace_size_batch(ns) -> int:

@@ -8,7 +8,7 @@ import ctypes
 import torch
 
 from . import _abi
-from ._abi import CHUNK, Codebook, Item, Meta, SplitZipError
+from ._abi import CHUNK, Codebook, Item, Meta, SlotItem, SplitZipError
 
 CODEBOOK_BYTES = ctypes.sizeof(Codebook)
 META_BYTES = ctypes.sizeof(Meta)
@@ -139,6 +139,32 @@ def decode_slot(slot: torch.Tensor, meta: torch.Tensor, cb_or_dec_lut: torch.Ten
                                           stash.numel() * stash.element_size(), st_ptr,
                                           _stream(stream, slot.device)))
     return raw[: 2 * n].view(torch.bfloat16)
+
+
+def decode_slots(slots, metas, cbs_or_luts, ns, stashes, status: torch.Tensor | None = None,
+                 stream=None):
+    """In-place decode of a group of slots (see ``decode_slot``), up to 32
+    per pair of launches.  Returns the flat bfloat16 views of the slots."""
+    count = len(slots)
+    if not (len(metas) == len(cbs_or_luts) == len(ns) == len(stashes) == count):
+        raise ValueError("one meta, codebook, size and stash per slot")
+    items = (SlotItem * max(count, 1))()
+    raws = []
+    for k in range(count):
+        if not slots[k].is_contiguous():
+            raise ValueError("the slot tensors must be contiguous")
+        raw = slots[k].reshape(-1).view(torch.uint8)
+        raws.append(raw)
+        it = items[k]
+        it.slot, it.slot_bytes = raw.data_ptr(), raw.numel()
+        it.meta, it.dec_lut, it.n = metas[k].data_ptr(), _lut_ptr(cbs_or_luts[k]), ns[k]
+        it.stash = stashes[k].data_ptr()
+        it.stash_bytes = stashes[k].numel() * stashes[k].element_size()
+    st_ptr = 0 if status is None else status.data_ptr()
+    dev = slots[0].device if count else torch.device("cuda")
+    _abi._check("splitzip_decode_slot_batch",
+                _abi.splitzip_decode_slot_batch(items, count, st_ptr, _stream(stream, dev)))
+    return [raw[: 2 * n].view(torch.bfloat16) for raw, n in zip(raws, ns)]
 
 
 def read_codebook(cb: torch.Tensor) -> Codebook:

@@ -786,6 +786,12 @@ struct DecItem {
     const uint8_t *dec_lut;
     uint16_t *out;
     uint64_t n;
+    // In-place (slot) decode: the payload sits at the head of the output
+    // buffer.  Pass 1 stashes the inputs of the tiles whose output overlaps
+    // the payload into `stash` (same offsets as in the payload) and decodes
+    // the other tiles directly; pass 2 decodes the stashed tiles.
+    uint8_t *stash;         // pass 1 only
+    uint64_t other_bytes;   // size of the buffer the pass does not read from
 };
 
 struct DecArgs {
@@ -793,13 +799,6 @@ struct DecArgs {
     uint64_t tile_start[kMaxBatch + 1];   // first decode tile of each tensor
     DecItem it[kMaxBatch];
     int32_t *status;
-    // In-place (slot) decode of it[0] only: the payload sits at the head of
-    // the output buffer.  Pass 1 stashes the inputs of the tiles whose output
-    // overlaps the payload into `stash` (same offsets as in the payload) and
-    // decodes the other tiles directly; pass 2 decodes the stashed tiles.
-    uint8_t *stash;
-    uint64_t other_bytes;   // size of the buffer the pass does not read from
-    uint64_t t_pre;         // pass 2: tiles certain to be stashed
 };
 
 // Metadata must describe exactly the layout of (n, n_esc) and fit the buffer.
@@ -895,7 +894,8 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     const uint8_t *sm = I.payload + L0.off_sm;
     uint32_t pkw[kDecUnits];
     u32x2 smw[kDecUnits];
-    const bool early = full && (kMode != kSlotFinish || tile < a.t_pre);
+    // second slot pass: tiles before the dense sections' end are certainly stashed
+    const bool early = full && (kMode != kSlotFinish || tile < L0.total / (2 * kDecTile));
     if (early) {
 #pragma unroll
         for (int u = 0; u < kDecUnits; ++u) {
@@ -906,7 +906,7 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     }
     const uint32_t lut_entry = (uint32_t)I.dec_lut[tid >> 4] | ((uint32_t)I.dec_lut[tid & 15] << 16);
     Layout L;
-    if (!meta_ok(I, L) || (kMode != kPlain && L.total > a.other_bytes)) {
+    if (!meta_ok(I, L) || (kMode != kPlain && L.total > I.other_bytes)) {
         // nothing is written for inconsistent metadata
         if (kMode != kSlotFinish && gt == a.tile_start[item] && tid == 0 && a.status)
             atomicOr(a.status, 1);
@@ -916,29 +916,30 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
         const uint64_t tiles = (I.n + kDecTile - 1) / kDecTile;
         const uint64_t t_split = slot_split(L.total, tiles, kDecTile);
         if (kMode == kSlotStage) {
-            // Every workgroup copies its share of the escape sections.
+            // Every workgroup of the tensor copies its share of the escape
+            // sections.
             const uint64_t esc_bytes = L.total - L.off_cid;
             const uint32_t *src = reinterpret_cast<const uint32_t *>(I.payload + L.off_cid);
-            uint32_t *dst = reinterpret_cast<uint32_t *>(a.stash + L.off_cid);
-            const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-            for (uint64_t w = gt * kThreads + tid; w < esc_bytes / 4; w += stride) dst[w] = src[w];
-            if (gt == 0 && tid < (int)(esc_bytes & 3)) {
+            uint32_t *dst = reinterpret_cast<uint32_t *>(I.stash + L.off_cid);
+            const uint64_t stride = tiles * kThreads;
+            for (uint64_t w = tile * kThreads + tid; w < esc_bytes / 4; w += stride) dst[w] = src[w];
+            if (tile == 0 && tid < (int)(esc_bytes & 3)) {
                 const uint64_t b = L.off_cid + (esc_bytes & ~uint64_t(3)) + tid;
-                a.stash[b] = I.payload[b];
+                I.stash[b] = I.payload[b];
             }
             if (tile < t_split) {   // output overlaps the payload: stash the inputs
                 if (full) {
 #pragma unroll
                     for (int u = 0; u < kDecUnits; ++u) {
                         const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
-                        *reinterpret_cast<uint32_t *>(a.stash + i0 / 2) = pkw[u];
-                        *reinterpret_cast<u32x2_a4 *>(a.stash + L0.off_sm + i0) = smw[u];
+                        *reinterpret_cast<uint32_t *>(I.stash + i0 / 2) = pkw[u];
+                        *reinterpret_cast<u32x2_a4 *>(I.stash + L0.off_sm + i0) = smw[u];
                     }
                 } else {
                     for (uint64_t b = base / 2 + tid; b < L0.n_pairs; b += kThreads)
-                        a.stash[b] = pk[b];
+                        I.stash[b] = pk[b];
                     for (uint64_t i = base + tid; i < I.n; i += kThreads)
-                        a.stash[L0.off_sm + i] = sm[i];
+                        I.stash[L0.off_sm + i] = sm[i];
                 }
                 return;
             }
@@ -1076,7 +1077,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_check(DecArgs a) {
         const DecItem I = a.it[item];
         if (I.n == 0) continue;
         Layout L;
-        if (!meta_ok(I, L) || (kFromOut && L.total > a.other_bytes))
+        if (!meta_ok(I, L) || (kFromOut && L.total > I.other_bytes))
             continue;   // reported by k_decode
         const uint64_t e = I.meta->n_esc;
         const uint64_t chunk = I.meta->chunk_size;
@@ -1278,37 +1279,57 @@ int launch_decode(const DecItem *items, uint32_t count, int32_t *status, hipStre
     return launched();
 }
 
-// In-place decode of one payload at the head of its output buffer: pass 1
-// stashes the inputs of the tiles whose output overlaps the payload and
-// decodes the rest, pass 2 decodes the stashed tiles over the payload.
-int launch_decode_slot(uint8_t *slot, uint64_t slot_bytes, const splitzip_meta *meta,
-                       const uint8_t *dec_lut, uint64_t n, uint8_t *stash, uint64_t stash_bytes,
-                       int32_t *status, hipStream_t s) {
+// In-place decode of up to kMaxBatch payloads, each at the head of its own
+// output buffer (a slot): pass 1 stashes the inputs of the tiles whose
+// output overlaps the payload and decodes the rest, pass 2 decodes the
+// stashed tiles over the payload.
+int launch_decode_slot(const splitzip_slot_item *items, uint32_t count, int32_t *status,
+                       hipStream_t s) {
     constexpr uint64_t kTile = (uint64_t)kDecUnits * kThreads * kUnit;
     DecArgs a{};
-    a.count = 1;
+    a.count = count;
     a.status = status;
-    a.tile_start[0] = 0;
-    a.tile_start[1] = ceil_div(n, kTile);
-    const unsigned tiles = (unsigned)a.tile_start[1];
-    a.it[0] = DecItem{slot, slot_bytes, meta, dec_lut, reinterpret_cast<uint16_t *>(slot), n};
-    a.stash = stash;
-    a.other_bytes = stash_bytes;
-    k_decode_slot_stage<<<tiles, kThreads, 0, s>>>(a);
+    uint64_t tiles = 0, n_all = 0;
+    for (uint32_t k = 0; k < count; ++k) {
+        const splitzip_slot_item &I = items[k];
+        a.it[k] = DecItem{I.slot, I.slot_bytes, I.meta, I.dec_lut,
+                          reinterpret_cast<uint16_t *>(I.slot), I.n, I.stash, I.stash_bytes};
+        a.tile_start[k] = tiles;
+        tiles += ceil_div(I.n, kTile);
+        n_all += I.n;
+    }
+    a.tile_start[count] = tiles;
+    if (tiles == 0) return SPLITZIP_OK;
+    k_decode_slot_stage<<<(unsigned)tiles, kThreads, 0, s>>>(a);
     if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
-    a.it[0].payload = stash;
-    a.it[0].payload_bytes = stash_bytes;
-    a.stash = nullptr;
-    a.other_bytes = slot_bytes;
-    a.t_pre = layout_of(n, 0).total / (2 * kTile);
-    k_decode_slot_finish<<<tiles, kThreads, 0, s>>>(a);
+    for (uint32_t k = 0; k < count; ++k) {
+        a.it[k].payload = items[k].stash;
+        a.it[k].payload_bytes = items[k].stash_bytes;
+        a.it[k].stash = nullptr;
+        a.it[k].other_bytes = items[k].slot_bytes;
+    }
+    k_decode_slot_finish<<<(unsigned)tiles, kThreads, 0, s>>>(a);
     if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     if (status) {
-        uint64_t cgrid = ceil_div(n, 16 * kThreads);
+        uint64_t cgrid = ceil_div(n_all, 16 * kThreads);
         if (cgrid > 1024) cgrid = 1024;
         k_decode_check<true><<<(unsigned)cgrid, kThreads, 0, s>>>(a);
     }
     return launched();
+}
+
+int check_slot_item(const splitzip_slot_item &I) {
+    if (I.n > SPLITZIP_MAX_N || !I.meta || !aligned(I.meta, 8) || !I.dec_lut)
+        return SPLITZIP_ERR_INVALID;
+    if (I.n == 0) return SPLITZIP_OK;
+    const uint64_t dense = layout_of(I.n, 0).total;
+    const uint64_t need = dense > 2 * I.n ? dense : 2 * I.n;
+    if (!I.slot || !aligned(I.slot, 16) || I.slot_bytes < need || !I.stash ||
+        !aligned(I.stash, 16) || I.stash_bytes < dense)
+        return SPLITZIP_ERR_INVALID;
+    const uintptr_t a0 = (uintptr_t)I.slot, b0 = (uintptr_t)I.stash;
+    if (a0 < b0 + I.stash_bytes && b0 < a0 + I.slot_bytes) return SPLITZIP_ERR_INVALID;
+    return SPLITZIP_OK;
 }
 
 }  // namespace
@@ -1402,26 +1423,29 @@ int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const spli
         (d_status && !aligned(d_status, 4)))
         return SPLITZIP_ERR_INVALID;
     if (n == 0) return SPLITZIP_OK;
-    const DecItem it{d_payload, payload_bytes, d_meta, d_dec_lut, d_out, n};
+    const DecItem it{d_payload, payload_bytes, d_meta, d_dec_lut, d_out, n, nullptr, 0};
     return launch_decode(&it, 1, d_status, reinterpret_cast<hipStream_t>(stream));
 }
 
 int splitzip_decode_slot(uint8_t *d_slot, uint64_t slot_bytes, const splitzip_meta *d_meta,
                          const uint8_t *d_dec_lut, uint64_t n, uint8_t *d_stash,
                          uint64_t stash_bytes, int32_t *d_status, void *stream) {
-    if (n > SPLITZIP_MAX_N || !d_meta || !aligned(d_meta, 8) || !d_dec_lut ||
-        (d_status && !aligned(d_status, 4)))
-        return SPLITZIP_ERR_INVALID;
-    if (n == 0) return SPLITZIP_OK;
-    const uint64_t dense = layout_of(n, 0).total;
-    const uint64_t need = dense > 2 * n ? dense : 2 * n;
-    if (!d_slot || !aligned(d_slot, 16) || slot_bytes < need || !d_stash ||
-        !aligned(d_stash, 16) || stash_bytes < dense)
-        return SPLITZIP_ERR_INVALID;
-    const uintptr_t a0 = (uintptr_t)d_slot, b0 = (uintptr_t)d_stash;
-    if (a0 < b0 + stash_bytes && b0 < a0 + slot_bytes) return SPLITZIP_ERR_INVALID;
-    return launch_decode_slot(d_slot, slot_bytes, d_meta, d_dec_lut, n, d_stash, stash_bytes,
-                              d_status, reinterpret_cast<hipStream_t>(stream));
+    const splitzip_slot_item it{d_slot, slot_bytes, d_meta, d_dec_lut, n, d_stash, stash_bytes};
+    return splitzip_decode_slot_batch(&it, 1, d_status, stream);
+}
+
+int splitzip_decode_slot_batch(const splitzip_slot_item *items, uint32_t count, int32_t *d_status,
+                               void *stream) {
+    if ((count && !items) || (d_status && !aligned(d_status, 4))) return SPLITZIP_ERR_INVALID;
+    for (uint32_t k = 0; k < count; ++k)
+        if (check_slot_item(items[k])) return SPLITZIP_ERR_INVALID;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (uint32_t k0 = 0; k0 < count; k0 += kMaxBatch) {
+        const uint32_t m = count - k0 < (uint32_t)kMaxBatch ? count - k0 : (uint32_t)kMaxBatch;
+        const int rc = launch_decode_slot(items + k0, m, d_status, s);
+        if (rc) return rc;
+    }
+    return SPLITZIP_OK;
 }
 
 int splitzip_calibrate_batch(const splitzip_item *items, uint32_t count, void *d_ws,
@@ -1484,7 +1508,7 @@ int splitzip_decode_batch(const splitzip_item *items, uint32_t count, int32_t *d
         const uint32_t m = count - k0 < (uint32_t)kMaxBatch ? count - k0 : (uint32_t)kMaxBatch;
         for (uint32_t k = 0; k < m; ++k) {
             const splitzip_item &I = items[k0 + k];
-            chunk[k] = DecItem{I.payload, I.capacity, I.meta, dec_lut_of(I.cb), I.out, I.n};
+            chunk[k] = DecItem{I.payload, I.capacity, I.meta, dec_lut_of(I.cb), I.out, I.n, nullptr, 0};
         }
         const int rc = launch_decode(chunk, m, d_status, s);
         if (rc) return rc;

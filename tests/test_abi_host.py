@@ -25,7 +25,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = S.lib()
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(lib, name), name
         assert name in _abi.SIGNATURES, name
@@ -39,6 +39,7 @@ def test_struct_layout_matches_header():
     assert meta.value == ctypes.sizeof(_abi.Meta) == 104
     assert _abi.Codebook.dec_lut.offset == 512
     assert _abi.Meta.status.offset == 96
+    assert ctypes.sizeof(_abi.SlotItem) == 56 and ctypes.sizeof(_abi.Item) == 56
     assert S.lib().splitzip_abi_version() == 1
 
 
@@ -74,6 +75,14 @@ def test_argument_errors_need_no_device():
                                      0) == _abi.ERR_INVALID
     assert _abi.splitzip_decode_slot(0x10000, 1 << 10, 0x2000, 0x3000, 5, 0x40000, 4, 0, 0) == \
         _abi.ERR_INVALID
+    # a batch with one bad item enqueues nothing
+    items = (_abi.SlotItem * 2)()
+    items[0].slot, items[0].slot_bytes, items[0].meta, items[0].dec_lut = 0x10000, 1 << 10, 0x2000, 0x3000
+    items[0].n, items[0].stash, items[0].stash_bytes = 5, 0x40000, 1 << 10
+    items[1] = items[0]
+    items[1].stash = 0x10100                      # overlaps its slot
+    assert _abi.splitzip_decode_slot_batch(items, 2, 0, 0) == _abi.ERR_INVALID
+    assert _abi.splitzip_decode_slot_batch(None, 1, 0, 0) == _abi.ERR_INVALID
     # chunk sizes the wire format cannot carry
     for chunk, n in ((0, 5), (65537, 5), (1, (1 << 31) + 1)):
         assert _abi.splitzip_encode_chunked(0x1000, n, 0x2000, chunk, 0x4000, 1 << 40, 0x3000,

@@ -29,7 +29,8 @@ def setup_module(module):
 def slot_for(payload: bytes, n: int, extra: int = 0) -> torch.Tensor:
     size = max(2 * n, S.payload_size(n, 0), len(payload)) + extra
     slot = torch.full((size,), FILL, dtype=torch.uint8)
-    slot[: len(payload)] = torch.frombuffer(bytearray(payload), dtype=torch.uint8)
+    if payload:
+        slot[: len(payload)] = torch.frombuffer(bytearray(payload), dtype=torch.uint8)
     return slot.to(DEV)
 
 
@@ -209,3 +210,28 @@ def test_h2d_pipeline_into_slots():
     assert int(st.item()) == 0
     for x, out in zip(xs, outs):
         assert np.array_equal(host_bits(out.cpu()), host_bits(x))
+
+
+def test_slot_batch_matches_inputs_across_launches():
+    """40 payloads of mixed sizes and escape densities (two launch pairs),
+    each at the head of its own slot, decoded in place as one group."""
+    g = torch.Generator().manual_seed(11)
+    sizes = [int(v) for v in torch.randint(1, 200_000, (40,), generator=g)]
+    sizes[3], sizes[17], sizes[33] = 0, 8192, 3 * 8192 + 1
+    xs = [W.log_uniform_stress(n, seed=700 + k) if k % 7 == 3 else W.gaussian_weight(n, seed=700 + k)
+          for k, n in enumerate(sizes)]
+    slots, metas, luts, stashes, want = [], [], [], [], []
+    for x in xs:
+        xs_h, ocb, opay, om = oracle_case(x)
+        slots.append(slot_for(opay, om.n))
+        metas.append(meta_to_device(om))
+        luts.append(torch.tensor(np.asarray(ocb.dec_lut, np.uint8)).to(DEV))
+        stashes.append(stash_for(om.comp_bytes))
+        want.append(xs_h)
+    _say("slot batch of %d" % len(xs))
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    outs = S.decode_slots(slots, metas, luts, sizes, stashes, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    for k, (out, w) in enumerate(zip(outs, want)):
+        assert np.array_equal(host_bits(out.cpu()), w), k
