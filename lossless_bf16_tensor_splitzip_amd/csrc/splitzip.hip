@@ -30,10 +30,13 @@
 //                 ballots to rank the tile's escapes, which are staged in the
 //                 workspace with the tile's escape count.  Tiles never talk
 //                 to each other.
-//   k_encode_tail scans the tile counts of a tensor (every workgroup sums the
-//                 counts it needs) and writes chunk id, chunk-local position
-//                 and raw exponent of every escape at its final rank, then the
-//                 padding and the metadata.
+//   k_encode_sums (large tensors only) escapes per block of tiles and per
+//                 256-tile superblock, so escape placement needs few loads.
+//   k_encode_tail every workgroup takes a block of 8-64 tiles, finds the rank
+//                 of its first escape and the tensor's escape count, and
+//                 writes chunk id, chunk-local position and raw exponent of
+//                 each of its escapes at its final rank; the tensor's first
+//                 workgroup writes the padding and the metadata.
 //   k_decode      one 8192-element tile per workgroup:
 //                 pk + sm -> bf16 through a 256-entry pair table in LDS and
 //                 16-byte stores; meanwhile one wave finds the tile's escapes
@@ -42,6 +45,11 @@
 //   k_decode_check  (only when a status word is requested) validates every
 //                 escape and re-applies it by scatter, which also makes the
 //                 decode correct for escape streams that are not sorted.
+//   k_decode_slot_stage / k_decode_slot_finish  in-place decode of payloads
+//                 that sit at the head of their own output buffers: the first
+//                 pass stashes the inputs of the tiles whose output overlaps
+//                 the payload and decodes the others, the second decodes the
+//                 stashed tiles.
 
 #include <hip/hip_runtime.h>
 
@@ -52,13 +60,27 @@
 
 namespace {
 
+// Build-time tuning knobs; the defaults are the measured best on MI355X.
+#ifndef SPLITZIP_ENC_UNITS
+#define SPLITZIP_ENC_UNITS 4        // encode: 8-element units per thread per tile
+#endif
+#ifndef SPLITZIP_TAIL_MIN_TILES
+#define SPLITZIP_TAIL_MIN_TILES 8   // escape placement: fewest tiles per workgroup
+#endif
+#ifndef SPLITZIP_TAIL_TARGET_WGS
+#define SPLITZIP_TAIL_TARGET_WGS 2048   // ... and the workgroup count it aims at
+#endif
+#ifndef SPLITZIP_TAIL_DIRECT
+#define SPLITZIP_TAIL_DIRECT 1024   // tiles per tensor up to which no count sums run
+#endif
+#ifndef SPLITZIP_TAIL_THREADS
+#define SPLITZIP_TAIL_THREADS 256   // escape placement workgroup size
+#endif
+
 constexpr uint32_t kChunk = SPLITZIP_CHUNK;
 constexpr int kMaxBatch = 32;                 // tensors per launch
 constexpr int kThreads = 256;                 // encode / decode workgroup
 constexpr int kUnit = 8;                      // elements per 16-byte load
-#ifndef SPLITZIP_ENC_UNITS
-#define SPLITZIP_ENC_UNITS 4
-#endif
 constexpr int kEncUnits = SPLITZIP_ENC_UNITS; // units per thread per tile
 constexpr int kEncTile = kThreads * kUnit * kEncUnits;   // 8192 elements
 constexpr int kCalThreads = 1024;
@@ -66,35 +88,23 @@ constexpr int kCalMaxGrid = 512;              // workgroups per tensor, at most
 constexpr int kCalTarget = 2;                 // resident 1024-thread workgroups per CU
 constexpr int kCalGroup = 16;                 // arrivals per first-level counter
 constexpr int kCalCopies = 16;                // global histogram copies per tensor
-#ifndef SPLITZIP_TAIL_MIN_TILES
-#define SPLITZIP_TAIL_MIN_TILES 8
-#endif
-#ifndef SPLITZIP_TAIL_TARGET_WGS
-#define SPLITZIP_TAIL_TARGET_WGS 2048
-#endif
-#ifndef SPLITZIP_TAIL_DIRECT
-#define SPLITZIP_TAIL_DIRECT 1024
-#endif
 // Encode tiles placed per tail workgroup: chosen per launch, a power of two
 // from kTailMinTiles (enough workgroups to spread dense escape streams over
 // the GPU) to kTailMaxTiles (fewer workgroups when the launch has many tiles).
 constexpr int kTailMinTiles = SPLITZIP_TAIL_MIN_TILES;
 constexpr int kTailMaxTiles = 64;
 constexpr uint64_t kTailTargetWgs = SPLITZIP_TAIL_TARGET_WGS;
-#ifndef SPLITZIP_TAIL_THREADS
-#define SPLITZIP_TAIL_THREADS 256
-#endif
-constexpr int kTailThreads = SPLITZIP_TAIL_THREADS;   // escape placement workgroup
+constexpr int kTailThreads = SPLITZIP_TAIL_THREADS;
 constexpr int kSuperTiles = 256;              // tiles per second-level count sum
-constexpr uint64_t kTailDirect = SPLITZIP_TAIL_DIRECT;  // up to this many tiles per tensor,
-                                              // tail workgroups read tile counts directly
+constexpr uint64_t kTailDirect = SPLITZIP_TAIL_DIRECT;
 constexpr uint32_t kMaxChunk = 65536;         // chunk-local positions are uint16
 constexpr int kDecUnits = 4;                  // decode: units per thread per tile (8192 elements)
 
 // Workspace layout (bytes).  kMaxBatch calibrate slots, each with its
 // counters on separate cache lines and its histogram copies (all of which
-// return to zero at the end of every call), then the encode tile counts and
-// staging area, whose size depends only on the workspace size.
+// return to zero at the end of every call), then the encode tile counts, the
+// count sums per tail block and per superblock, and the escape staging area,
+// whose sizes depend only on the workspace size.
 constexpr size_t kSlotTop = 0;                                           // uint32
 constexpr size_t kSlotLvl1 = 64;                                         // uint32, 64 B apart
 constexpr size_t kSlotHist = kSlotLvl1 + 64 * (kCalMaxGrid / kCalGroup); // uint64[16][256]
@@ -139,7 +149,7 @@ struct WsPlan {
     uint64_t off_stage;   // uint32[t_max * kEncTile] staged escapes
 };
 
-constexpr uint64_t kWsPerTile = 8 + 4 * (uint64_t)kEncTile;   // count, block sum, stage
+constexpr uint64_t kWsPerTile = 8 + 4 * (uint64_t)kEncTile;   // count, count sums, stage
 constexpr uint64_t kWsFixed = kWsTiles + kWsSlack + 4 * 128;
 
 __host__ inline WsPlan ws_plan(size_t ws_bytes) {
@@ -564,7 +574,8 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
     }
 }
 
-// Inclusive scan of one value per thread across a 256-thread workgroup.
+// Inclusive scan of one value per thread across the workgroup (a multiple of
+// 64 threads; lds_waves holds one word per wave).
 __device__ inline uint32_t block_scan_incl(uint32_t v, uint32_t *lds_waves) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
