@@ -127,8 +127,8 @@ def test_batch_workspace_too_small():
 
 def test_workload_kv_stream_batched():
     """The 4 GiB streaming KV cache through the batched calls, as timed by the
-    benchmark: every tensor round-trips and obeys the size identities; two
-    tensors are compared byte for byte with the oracle."""
+    benchmark: every tensor round-trips, obeys the size identities and is
+    compared byte for byte with the oracle (codebook, metadata, payload)."""
     xs = [W.kv_cache_tensor(layer, kv, device=DEV).reshape(-1)
           for layer in range(32) for kv in range(2)]
     b = S.Batch(xs)
@@ -143,10 +143,11 @@ def test_workload_kv_stream_batched():
         c = S.read_codebook(b.cbs[k])
         assert m.status == 0 and m.n_esc == m.n - c.covered
         assert m.comp_bytes == P.closed_form_total(m.n, m.n_esc)
-    for k in (5, 62):
+    for k in range(len(xs)):
         xh = host_bits(xs[k])
         ocb = oracle.calibrate(xh)
         opay, om = oracle.encode(xh, ocb)
+        check_codebook(S.read_codebook(b.cbs[k]), ocb)
         m = S.read_meta(b.metas[k])
         check_meta(m, om, ocb)
-        assert b.payloads[k][: m.comp_bytes].cpu().numpy().tobytes() == opay
+        assert b.payloads[k][: m.comp_bytes].cpu().numpy().tobytes() == opay, k
