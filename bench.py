@@ -399,6 +399,9 @@ def main():
     copy = d2d_copy(x_all, stream)
     small = None if args.no_small else small_configs(S, W, dev, stream)
     h2d = None if args.no_h2d else h2d_pipeline(S, batch, metas_h, x_all, dev, args.h2d_tensors)
+    if h2d:
+        # the decode must outrun the link it sits behind (raw bytes per second)
+        h2d["decode_over_raw_h2d"] = round(phases["decode"]["raw_GBps"] / h2d["raw_h2d_GBps"], 1)
 
     cpu = None
     if not args.no_cpu_baseline:
