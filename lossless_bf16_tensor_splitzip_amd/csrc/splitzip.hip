@@ -894,7 +894,9 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     constexpr int kDecTile = kThreads * kUnit * kDecUnits;
     __shared__ uint32_t pair_lut[256];      // pk byte -> (even exponent, odd exponent << 16)
     __shared__ uint64_t range[2];
-    __shared__ uint32_t sm_tile[kDecTile / 4];   // sm bytes of a tile with many escapes
+    // Output tile of a tensor with dense escapes, or the sm bytes of a tile
+    // with many escapes in an otherwise sparse tensor.
+    __shared__ uint32_t tile_buf[kDecTile / 2];
     const uint64_t gt = blockIdx.x;
     const uint32_t item = find_item(a.tile_start, a.count, gt);
     const DecItem I = a.it[item];
@@ -978,13 +980,18 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     const uint8_t *ev = I.payload + L.off_ev;
 
     pair_lut[tid] = lut_entry;
+    // A tensor whose escapes average more than 512 per tile is decoded tile
+    // by tile in LDS (dense values, the patch, then one coalesced store):
+    // scattering thousands of 2-byte stores per tile to memory costs more
+    // than writing the tile twice.
+    const bool in_lds = full && e * (uint64_t)kDecTile > 512 * I.n;
     __syncthreads();
 
     // Dense part first: every element through the pair table, 16-byte stores.
     if (full) {
 #pragma unroll
         for (int u = 0; u < kDecUnits; ++u) {
-            const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+            const int l0 = u * (kThreads * kUnit) + tid * kUnit;
             u32x4 o;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -992,8 +999,10 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
                 const uint32_t s = smw[u][k >> 1] >> (16 * (k & 1));
                 o[k] = join16(s & 0xFFu, ee & 0xFFu) | (join16((s >> 8) & 0xFFu, ee >> 16) << 16);
             }
-            // plain stores: measured faster than non-temporal ones for this stream
-            *reinterpret_cast<u32x4 *>(I.out + i0) = o;
+            if (in_lds)
+                *reinterpret_cast<u32x4 *>(tile_buf + l0 / 2) = o;
+            else   // plain stores: measured faster than non-temporal ones for this stream
+                *reinterpret_cast<u32x4 *>(I.out + base + l0) = o;
         }
     } else {
         for (uint64_t i = base + tid; i < I.n; i += kThreads) {
@@ -1033,26 +1042,62 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     }
     __syncthreads();
     const uint64_t r0 = range[0], r1 = range[1];
-    // A tile with many escapes keeps its sm bytes (still in registers) in LDS
-    // for the patch, instead of reading each one back from memory.
+    if (in_lds) {
+        // the decoded value already holds the sign and mantissa
+        uint16_t *t16 = reinterpret_cast<uint16_t *>(tile_buf);
+        for (uint64_t rb = r0; rb < r1; rb += 8 * kThreads) {
+            int32_t l8[8];
+            uint32_t e8[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint64_t r = rb + q * kThreads + tid;
+                l8[q] = -1;
+                e8[q] = 0;
+                if (r < r1) {
+                    const int64_t v = (int64_t)cid[r] * chunk + lpos[r] - (int64_t)base;
+                    e8[q] = ev[r];
+                    if (v >= 0 && v < kDecTile) l8[q] = (int32_t)v;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (l8[q] >= 0)
+                    t16[l8[q]] = (uint16_t)((t16[l8[q]] & 0x807Fu) | (e8[q] << 7));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kDecUnits; ++u) {
+            const int l0 = u * (kThreads * kUnit) + tid * kUnit;
+            *reinterpret_cast<u32x4 *>(I.out + base + l0) =
+                *reinterpret_cast<const u32x4 *>(tile_buf + l0 / 2);
+        }
+        return;
+    }
+    // A tile with many escapes in a sparse tensor keeps its sm bytes (still
+    // in registers) in LDS for the patch, instead of reading each one back
+    // from memory.
     const bool staged = full && r1 - r0 > 2 * kThreads;
     if (staged) {
 #pragma unroll
         for (int u = 0; u < kDecUnits; ++u) {
             const int o = u * (kThreads * kUnit) + tid * kUnit;
-            sm_tile[o / 4] = smw[u].x;
-            sm_tile[o / 4 + 1] = smw[u].y;
+            tile_buf[o / 4] = smw[u].x;
+            tile_buf[o / 4 + 1] = smw[u].y;
         }
         __syncthreads();
     }
-    const uint8_t *sm_lds = reinterpret_cast<const uint8_t *>(sm_tile);
-    // 4 escapes per thread in flight: their stream entries, then their sm
-    // bytes, then the stores
-    for (uint64_t rb = r0; rb < r1; rb += 4 * kThreads) {
-        int64_t idx[4];
-        uint32_t evv[4], smv[4];
+    const uint8_t *sm_lds = reinterpret_cast<const uint8_t *>(tile_buf);
+#ifndef SPLITZIP_DEC_PATCH
+#define SPLITZIP_DEC_PATCH 4
+#endif
+    constexpr int kPatch = SPLITZIP_DEC_PATCH;
+    // kPatch escapes per thread in flight: their stream entries, then their
+    // sm bytes, then the stores
+    for (uint64_t rb = r0; rb < r1; rb += kPatch * kThreads) {
+        int64_t idx[kPatch];
+        uint32_t evv[kPatch], smv[kPatch];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < kPatch; ++q) {
             const uint64_t r = rb + q * kThreads + tid;
             idx[q] = -1;
             evv[q] = 0;
@@ -1064,10 +1109,10 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
             }
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < kPatch; ++q)
             smv[q] = idx[q] < 0 ? 0u : (staged ? sm_lds[idx[q] - (int64_t)base] : sm[idx[q]]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < kPatch; ++q)
             if (idx[q] >= 0) I.out[idx[q]] = (uint16_t)join16(smv[q], evv[q]);
     }
 }
