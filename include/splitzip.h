@@ -242,7 +242,8 @@ int splitzip_decode_slot(uint8_t *d_slot, uint64_t slot_bytes, const splitzip_me
                          uint64_t stash_bytes, int32_t *d_status, void *stream);
 
 /* In-place decode of a group of slots (page "SplitZip in DDO -- VMM routes",
- * "Files added": the staging route decodes a group of slots at a time): the
+ * "Route B (fallback)": the staging route expands the slots of an execution
+ * group after their upload, on the upload stream): the
  * same result as splitzip_decode_slot on every item in order, with up to 32
  * items sharing each pair of launches.  Each item needs its own stash; no
  * slot or stash may overlap another item's buffers.  d_status (optional)
