@@ -253,8 +253,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this codec build runs on exactly one GPU; --gpus %d is not supported "
-              "(the multi-GPU sharding is described in DESIGN.md)" % args.gpus, file=sys.stderr)
+        print("bench.py: the benchmark runs on exactly one GPU; --gpus %d is not supported "
+              "(the codec shards across GPUs by tensor or by chunk range; that path is not built)"
+              % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
