@@ -10,11 +10,12 @@ Host-side policy helpers around the C ABI (no codec arithmetic):
   along under their own keys; a reader of the pages' format ignores them.
 * The coverage gate of the page "SplitZip in DDO -- VMM routes" ("Build the
   cache"; "Invariants common to both routes", item 3): a tensor whose top-16
-  coverage is below 0.99 is left uncompressed, because the size model no
-  longer holds and broad exponent distributions can expand.
+  coverage is below 0.99 is left uncompressed: the payload-size estimate no
+  longer holds there, and tensors with widely spread exponents can come out
+  larger than the raw data.
 
-A payload is useless without its dec_lut (same page, invariant 2): keep the
-codebook JSON next to every stored payload.
+A payload cannot be decoded without its codebook's dec_lut (same page,
+invariant 2): keep the codebook JSON next to every stored payload.
 """
 from __future__ import annotations
 

@@ -11,7 +11,7 @@
  * for diffusers-dynamic-offloader" (page 1: module docstring "Method" and
  * "Payload layout", functions calibrate_codebook, assemble_payload,
  * encode_torch, decode_torch), and the page "SplitZip in DDO -- VMM routes"
- * (page 2: "Invariants common to both routes", item 1, frozen wire format).
+ * (page 2: "Invariants common to both routes", item 1, the fixed wire format).
  *
  * Readings where the pages are silent or ambiguous (each one is listed in the
  * design notes of the repository as well):

@@ -44,7 +44,7 @@ def test_ratio_kv_like(o):
 
 
 def test_escape_heavy_expands(o):
-    # page 2, invariant 3: broad exponent distributions can expand the data
+    # page 2, invariant 3: data whose exponents are widely spread can grow
     r, cb, meta = _ratio(o, W.log_uniform_stress(1 << 18, seed=3, stream=0))
     assert r > 1.17, r
     assert meta.n_esc > (1 << 18) // 2
