@@ -231,13 +231,20 @@ int orc_encode(const uint16_t *x, uint64_t n, const uint8_t marked[256], uint32_
  * increasing, chunk-local positions must be < chunk and the offsets must equal
  * the layout rule.
  * ------------------------------------------------------------------------- */
+/* count items of width bytes starting at byte off lie inside buf[0, buf_len)
+ * (written so that no sum or product can wrap around) */
+static int section_fits(uint64_t off, uint64_t count, uint64_t width, uint64_t buf_len) {
+    return off <= buf_len && count <= (buf_len - off) / width;
+}
+
 int orc_decode(const uint8_t *buf, uint64_t buf_len, uint64_t n, uint64_t n_esc,
                uint32_t chunk, const uint64_t off[5], const uint8_t dec[16], uint16_t *out,
                int validate) {
     if (chunk == 0 || chunk > 65536u) return ORC_EINVAL;
     uint64_t n_pairs = (n + 1) / 2;
-    if (off[0] + n_pairs > buf_len || off[1] + n > buf_len || off[2] + 4 * n_esc > buf_len ||
-        off[3] + 2 * n_esc > buf_len || off[4] + n_esc > buf_len)
+    if (!section_fits(off[0], n_pairs, 1, buf_len) || !section_fits(off[1], n, 1, buf_len) ||
+        !section_fits(off[2], n_esc, 4, buf_len) || !section_fits(off[3], n_esc, 2, buf_len) ||
+        !section_fits(off[4], n_esc, 1, buf_len))
         return ORC_ECORRUPT;
     if (validate) {
         uint64_t want[5], total;
