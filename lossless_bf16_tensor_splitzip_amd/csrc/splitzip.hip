@@ -99,6 +99,8 @@ constexpr int kSuperTiles = 256;              // tiles per second-level count su
 constexpr uint64_t kTailDirect = SPLITZIP_TAIL_DIRECT;
 constexpr uint32_t kMaxChunk = 65536;         // chunk-local positions are uint16
 constexpr int kDecUnits = 4;                  // decode: units per thread per tile (8192 elements)
+constexpr uint32_t kStageDirect = 256;        // encode: escapes per tile written directly
+constexpr uint32_t kStageLds = 2048;          // ... beyond that, ranks per LDS round
 
 // Workspace layout (bytes).  kMaxBatch calibrate slots, each with its
 // counters on separate cache lines and its histogram copies (all of which
@@ -452,6 +454,7 @@ __device__ inline void encode_unit(const u32x4 q, const uint8_t *lut, uint32_t &
 __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
     __shared__ uint8_t lut[256];
     __shared__ uint32_t wtot[kEncUnits][4];
+    __shared__ uint32_t stg[kStageLds];       // staged escapes of a dense tile
 
     const uint64_t gt = blockIdx.x;
     const uint32_t item = find_item(a.tile_start, a.count, gt);
@@ -562,8 +565,9 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
         }
     }
     if (tid == 0) a.tile_count[gt] = tile_total;
-    if (tile_total) {
-        uint32_t *stage = a.stage + gt * kEncTile;
+    uint32_t *stage = a.stage + gt * kEncTile;
+    if (tile_total <= kStageDirect) {
+        // few escapes: every thread writes its own at their ranks
 #pragma unroll
         for (int u = 0; u < kEncUnits; ++u) {
             uint32_t f = flags[u];
@@ -576,6 +580,32 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
                 const uint32_t ex = (j & 1) ? exp_hi(w) : exp_lo(w);
                 stage[r++] = ((l0 + j) << 8) | ex;
             }
+        }
+    } else {
+        // many: ranks [lo, lo + kStageLds) at a time through LDS, so the
+        // staging stores are contiguous across the workgroup
+        for (uint32_t lo = 0; lo < tile_total; lo += kStageLds) {
+            const uint32_t hi = lo + kStageLds < tile_total ? lo + kStageLds : tile_total;
+#pragma unroll
+            for (int u = 0; u < kEncUnits; ++u) {
+                uint32_t f = flags[u];
+                uint32_t r = ubase[u] + pre[u];
+                if (r >= hi || r + __builtin_popcount(f) <= lo) continue;
+                const uint32_t l0 = (uint32_t)u * (kThreads * kUnit) + tid * kUnit;
+                while (f) {
+                    const int j = __builtin_ctz(f);
+                    f &= f - 1;
+                    if (r >= lo && r < hi) {
+                        const uint32_t w = word_of(q[u], j >> 1);
+                        const uint32_t ex = (j & 1) ? exp_hi(w) : exp_lo(w);
+                        stg[r - lo] = ((l0 + j) << 8) | ex;
+                    }
+                    ++r;
+                }
+            }
+            __syncthreads();
+            for (uint32_t k = tid; k < hi - lo; k += kThreads) stage[lo + k] = stg[k];
+            __syncthreads();
         }
     }
 }
