@@ -65,10 +65,10 @@ namespace {
 #define SPLITZIP_ENC_UNITS 4        // encode: 8-element units per thread per tile
 #endif
 #ifndef SPLITZIP_TAIL_MIN_TILES
-#define SPLITZIP_TAIL_MIN_TILES 8   // escape placement: fewest tiles per workgroup
+#define SPLITZIP_TAIL_MIN_TILES 4   // escape placement: fewest tiles per workgroup
 #endif
 #ifndef SPLITZIP_TAIL_TARGET_WGS
-#define SPLITZIP_TAIL_TARGET_WGS 2048   // ... and the workgroup count it aims at
+#define SPLITZIP_TAIL_TARGET_WGS 1024   // ... and the workgroup count it aims at
 #endif
 #ifndef SPLITZIP_TAIL_DIRECT
 #define SPLITZIP_TAIL_DIRECT 1024   // tiles per tensor up to which no count sums run
