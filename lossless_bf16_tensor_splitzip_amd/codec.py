@@ -98,8 +98,12 @@ def decode(payload: torch.Tensor, meta: torch.Tensor, cb_or_dec_lut: torch.Tenso
            out: torch.Tensor | None = None, status: torch.Tensor | None = None,
            stream=None) -> torch.Tensor:
     """Decode to a flat bfloat16 tensor of n elements (``out`` when given).
-    ``cb_or_dec_lut`` is a device codebook or a 16-byte dec_lut tensor."""
-    dev = payload.device
+    ``cb_or_dec_lut`` is a device codebook or a 16-byte dec_lut tensor.  The
+    payload may also sit in pinned host memory: the kernel then reads it over
+    the host link while it decodes (no separate copy)."""
+    dev = _gpu_of(out, meta, cb_or_dec_lut, payload)
+    if payload.device.type != "cuda" and not payload.is_pinned():
+        raise ValueError("the payload must be on the GPU or in pinned host memory")
     if out is None:
         out = torch.empty(n, dtype=torch.bfloat16, device=dev)
     if out.dtype is not torch.bfloat16 or not out.is_contiguous() or out.numel() != n:
@@ -110,6 +114,13 @@ def decode(payload: torch.Tensor, meta: torch.Tensor, cb_or_dec_lut: torch.Tenso
                 _abi.splitzip_decode(payload.data_ptr(), payload.numel(), meta.data_ptr(),
                                      lut_ptr, out.data_ptr(), n, st_ptr, _stream(stream, dev)))
     return out
+
+
+def _gpu_of(*tensors) -> torch.device:
+    for t in tensors:
+        if t is not None and t.device.type == "cuda":
+            return t.device
+    raise ValueError("decode needs its output, metadata or codebook on the GPU")
 
 
 def _lut_ptr(cb_or_dec_lut: torch.Tensor) -> int:

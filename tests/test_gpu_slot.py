@@ -235,3 +235,22 @@ def test_slot_batch_matches_inputs_across_launches():
     assert int(st.item()) == 0
     for k, (out, w) in enumerate(zip(outs, want)):
         assert np.array_equal(host_bits(out.cpu()), w), k
+
+
+@pytest.mark.parametrize("make,n", [(W.gaussian_weight, 1_000_003), (W.log_uniform_stress, 77_777),
+                                    (W.gaussian_weight, 8 * 32768 * 128)])
+def test_decode_straight_from_pinned_host_memory(make, n):
+    """The payload stays in pinned host memory and the decode kernel reads it
+    over the host link (no copy, no slot): same output as from HBM."""
+    x = make(n, seed=1800).reshape(-1)
+    xs, ocb, opay, om = oracle_case(x)
+    host = torch.empty(len(opay) + 16, dtype=torch.uint8, pin_memory=True)
+    host[: len(opay)] = torch.frombuffer(bytearray(opay), dtype=torch.uint8)
+    lut = torch.tensor(np.asarray(ocb.dec_lut, np.uint8)).to(DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = S.decode(host[: len(opay)], meta_to_device(om), lut, n, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(host_bits(out.cpu()), xs)
+    with pytest.raises(ValueError):
+        S.decode(torch.zeros(len(opay), dtype=torch.uint8), meta_to_device(om), lut, n)
