@@ -69,6 +69,7 @@ def calibrate(x: torch.Tensor, ws: Workspace, cb: torch.Tensor | None = None,
     xb = _bits(x)
     if cb is None:
         cb = new_codebook(x.device)
+    _device_or_pinned(cb, "codebook")
     _abi._check("splitzip_calibrate",
                 _abi.splitzip_calibrate(xb.data_ptr(), xb.numel(), cb.data_ptr(), ws.ptr(),
                                         ws.nbytes, _stream(stream, x.device)))
@@ -78,14 +79,18 @@ def calibrate(x: torch.Tensor, ws: Workspace, cb: torch.Tensor | None = None,
 def encode(x: torch.Tensor, cb: torch.Tensor, ws: Workspace, payload: torch.Tensor | None = None,
            meta: torch.Tensor | None = None, stream=None, chunk_size: int = CHUNK):
     """Encode into ``payload`` (allocated for the worst case when None).
-    Returns (payload, meta) as device uint8 tensors; the payload occupies the
-    first meta.comp_bytes bytes."""
+    Returns (payload, meta) as uint8 tensors; the payload occupies the first
+    meta.comp_bytes bytes.  ``payload`` may be pinned host memory: the kernels
+    then write it over the host link (an offload without a separate copy)."""
     xb = _bits(x)
     n = xb.numel()
     if payload is None:
         payload = torch.empty(max(payload_size(n, n), 16), dtype=torch.uint8, device=x.device)
+    _device_or_pinned(payload, "payload")
     if meta is None:
         meta = new_meta(x.device)
+    _device_or_pinned(cb, "codebook")
+    _device_or_pinned(meta, "metadata")
     _abi._check("splitzip_encode_chunked",
                 _abi.splitzip_encode_chunked(xb.data_ptr(), n, cb.data_ptr(), chunk_size,
                                              payload.data_ptr(), payload.numel(),
@@ -102,18 +107,26 @@ def decode(payload: torch.Tensor, meta: torch.Tensor, cb_or_dec_lut: torch.Tenso
     payload may also sit in pinned host memory: the kernel then reads it over
     the host link while it decodes (no separate copy)."""
     dev = _gpu_of(out, meta, cb_or_dec_lut, payload)
-    if payload.device.type != "cuda" and not payload.is_pinned():
-        raise ValueError("the payload must be on the GPU or in pinned host memory")
+    _device_or_pinned(payload, "payload")
     if out is None:
         out = torch.empty(n, dtype=torch.bfloat16, device=dev)
     if out.dtype is not torch.bfloat16 or not out.is_contiguous() or out.numel() != n:
         raise ValueError("out must be a contiguous bfloat16 tensor of n elements")
+    for t, what in ((meta, "metadata"), (cb_or_dec_lut, "codebook"), (out, "output")) + \
+            (() if status is None else ((status, "status word"),)):
+        _device_or_pinned(t, what)
     lut_ptr = _lut_ptr(cb_or_dec_lut)
     st_ptr = 0 if status is None else status.data_ptr()
     _abi._check("splitzip_decode",
                 _abi.splitzip_decode(payload.data_ptr(), payload.numel(), meta.data_ptr(),
                                      lut_ptr, out.data_ptr(), n, st_ptr, _stream(stream, dev)))
     return out
+
+
+def _device_or_pinned(t: torch.Tensor, what: str) -> None:
+    # a kernel may only touch pageable host memory by faulting
+    if t.device.type != "cuda" and not t.is_pinned():
+        raise ValueError("the %s must be on the GPU or in pinned host memory" % what)
 
 
 def _gpu_of(*tensors) -> torch.device:
@@ -143,6 +156,10 @@ def decode_slot(slot: torch.Tensor, meta: torch.Tensor, cb_or_dec_lut: torch.Ten
         # page 1, decode_slot_into: the slot must be contiguous
         raise ValueError("the slot tensor must be contiguous")
     raw = slot.reshape(-1).view(torch.uint8)
+    for t, what in ((raw, "slot"), (stash, "stash"), (meta, "metadata"),
+                    (cb_or_dec_lut, "codebook")) + \
+            (() if status is None else ((status, "status word"),)):
+        _device_or_pinned(t, what)
     st_ptr = 0 if status is None else status.data_ptr()
     _abi._check("splitzip_decode_slot",
                 _abi.splitzip_decode_slot(raw.data_ptr(), raw.numel(), meta.data_ptr(),
@@ -165,14 +182,19 @@ def decode_slots(slots, metas, cbs_or_luts, ns, stashes, status: torch.Tensor | 
         if not slots[k].is_contiguous():
             raise ValueError("the slot tensors must be contiguous")
         raw = slots[k].reshape(-1).view(torch.uint8)
+        for t, what in ((raw, "slot"), (stashes[k], "stash"), (metas[k], "metadata"),
+                        (cbs_or_luts[k], "codebook")):
+            _device_or_pinned(t, what)
         raws.append(raw)
         it = items[k]
         it.slot, it.slot_bytes = raw.data_ptr(), raw.numel()
         it.meta, it.dec_lut, it.n = metas[k].data_ptr(), _lut_ptr(cbs_or_luts[k]), ns[k]
         it.stash = stashes[k].data_ptr()
         it.stash_bytes = stashes[k].numel() * stashes[k].element_size()
+    if status is not None:
+        _device_or_pinned(status, "status word")
     st_ptr = 0 if status is None else status.data_ptr()
-    dev = slots[0].device if count else torch.device("cuda")
+    dev = _gpu_of(*slots, *metas) if count else torch.device("cuda")
     _abi._check("splitzip_decode_slot_batch",
                 _abi.splitzip_decode_slot_batch(items, count, st_ptr, _stream(stream, dev)))
     return [raw[: 2 * n].view(torch.bfloat16) for raw, n in zip(raws, ns)]

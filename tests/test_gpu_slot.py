@@ -254,3 +254,23 @@ def test_decode_straight_from_pinned_host_memory(make, n):
     assert np.array_equal(host_bits(out.cpu()), xs)
     with pytest.raises(ValueError):
         S.decode(torch.zeros(len(opay), dtype=torch.uint8), meta_to_device(om), lut, n)
+
+
+@pytest.mark.parametrize("make,n", [(W.gaussian_weight, 1_000_003), (W.log_uniform_stress, 77_777),
+                                    (W.gaussian_weight, 8 * 32768 * 128)])
+def test_encode_straight_into_pinned_host_memory(make, n):
+    """The kernels write the payload over the host link into pinned host
+    memory (an offload without a separate copy): the oracle's bytes."""
+    x = make(n, seed=1900).reshape(-1)
+    xs, ocb, opay, om = oracle_case(x)
+    xd = x.to(DEV)
+    ws = workspace(n)
+    cb = S.calibrate(xd, ws)
+    host = torch.empty(S.payload_size(n, n), dtype=torch.uint8, pin_memory=True)
+    payload, meta = S.encode(xd, cb, ws, payload=host)
+    torch.cuda.synchronize()
+    m = S.read_meta(meta)
+    assert m.status == 0 and m.comp_bytes == om.comp_bytes
+    assert host[: m.comp_bytes].numpy().tobytes() == opay
+    with pytest.raises(ValueError):
+        S.encode(xd, cb, ws, payload=torch.empty(16, dtype=torch.uint8))
