@@ -31,7 +31,9 @@
  *     found by the device (capacity overflow, corrupt escape stream) are
  *     written to the status field / word named by the function.
  *   - Device pointers ("d_") may also be pinned host memory mapped into the
- *     device address space.
+ *     device address space (hipHostMalloc): a decode then reads its payload,
+ *     or an encode writes it, over the host link with no separate copy.
+ *     Never pageable host memory: a kernel access to it faults.
  *   - Tensor and payload buffers must be 16-byte aligned.
  *   - n is limited to SPLITZIP_MAX_N elements.
  */
