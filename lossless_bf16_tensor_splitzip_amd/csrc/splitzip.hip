@@ -53,6 +53,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -1206,19 +1207,22 @@ __global__ void k_fill_zero(uint32_t *p, uint64_t words) {
 // Host side
 // ---------------------------------------------------------------------------
 
+// Compute units of the current device, cached per device (host threads may
+// race to fill an entry; they all store the same value).
 constexpr int kMaxDevices = 64;
-int g_cu_count[kMaxDevices];
+std::atomic<int> g_cu_count[kMaxDevices];
 
 bool cu_count(int &cus) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
-    if (g_cu_count[dev] == 0) {
-        int c = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+    int c = dev < kMaxDevices ? g_cu_count[dev].load(std::memory_order_relaxed) : 0;
+    if (c == 0) {
         if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return false;
-        g_cu_count[dev] = c > 0 ? c : 1;
+        if (c <= 0) c = 1;
+        if (dev < kMaxDevices) g_cu_count[dev].store(c, std::memory_order_relaxed);
     }
-    cus = g_cu_count[dev];
+    cus = c;
     return true;
 }
 
