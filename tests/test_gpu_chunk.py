@@ -89,3 +89,68 @@ def test_large_single_tensor_summed_placement():
     got = payload[: m.comp_bytes].cpu().numpy().tobytes()
     assert got == opay
     assert torch.equal(out.view(torch.int16), x.view(torch.int16))
+
+
+def test_two_billion_element_tensor_sampled_against_oracle():
+    """n = 2^31 + 5 (4 GiB of bf16, element indices past int32) in one call:
+    the codebook equals the oracle's over the whole tensor, the escape count
+    and payload size obey their identities, the decode round-trips, and four
+    2^20-element windows of the payload (chunk aligned, the last one near the
+    end) equal what the oracle encodes for those windows with the same
+    codebook: the dense bytes at their offsets and the escapes with chunk ids
+    shifted by the window start."""
+    n = (1 << 31) + 5
+    _say("2G tensor n=%d" % n)
+    x = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    step = 1 << 27
+    for s0 in range(0, n, step):   # N(0, 0.02), generated in slices to bound memory
+        m0 = min(step, n - s0)
+        x[s0: s0 + m0] = W.to_bf16(0.02 * W.normal(m0, 610, 0, DEV, start=s0))
+    xv = x.view(torch.int16)
+    k = torch.arange(0, n, 4099, device=DEV)
+    xv[k] = ((((k >> 3) % 40) + 150) << 7).to(torch.int16)     # planted escapes
+    xv[n - 4] = 200 << 7                                          # and past index 2^31
+    xv[n - 1] = -(0x8000 - (201 << 7) - 5)                        # sign set, mantissa 5
+    del k
+    torch.cuda.empty_cache()
+    ws = S.Workspace(n, DEV)
+    cb = S.calibrate(x, ws)
+    cap = S.payload_size(n, n // 1000)
+    payload, meta = S.encode(x, cb, ws, payload=torch.empty(cap, dtype=torch.uint8, device=DEV))
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = S.decode(payload, meta, cb, n, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(out.view(torch.int16), xv)
+    del out, ws
+    m = S.read_meta(meta)
+    c = S.read_codebook(cb)
+    assert m.status == 0 and m.n_esc == n - c.covered and m.n_esc > 500_000
+    assert m.comp_bytes == S.payload_size(n, m.n_esc)
+    xs = xv.cpu().numpy().view(np.uint16)
+    ocb = oracle.calibrate(xs)
+    check_codebook(c, ocb)
+    off = [int(v) for v in m.offsets]
+    e = m.n_esc
+    esc_cid = payload[off[2]: off[2] + 4 * e].cpu().numpy().view("<i4").astype(np.int64)
+    esc_pos = payload[off[3]: off[3] + 2 * e].cpu().numpy().view("<u2").astype(np.int64)
+    esc_ev = payload[off[4]: off[4] + e].cpu().numpy()
+    esc_idx = esc_cid * 1024 + esc_pos
+    assert np.all(np.diff(esc_idx) > 0)
+    assert esc_idx[-1] == n - 1 and esc_idx[-2] == n - 4
+    win = 1 << 20
+    for start, end in ((0, win), (1 << 30, (1 << 30) + win),
+                       (1024 * 1_900_001, 1024 * 1_900_001 + win), ((1 << 31) - win, n)):
+        _say("2G tensor window [%d, %d)" % (start, end))
+        opay, om = oracle.encode(xs[start: end], ocb)
+        assert payload[start // 2: (end + 1) // 2].cpu().numpy().tobytes() == \
+            opay[: om.n_pairs]
+        assert payload[off[1] + start: off[1] + end].cpu().numpy().tobytes() == \
+            opay[om.offsets[1]: om.offsets[1] + end - start]
+        sel = (esc_idx >= start) & (esc_idx < end)
+        ocid = np.frombuffer(opay, "<i4", om.n_esc, om.offsets[2]).astype(np.int64)
+        opos = np.frombuffer(opay, "<u2", om.n_esc, om.offsets[3]).astype(np.int64)
+        oev = np.frombuffer(opay, np.uint8, om.n_esc, om.offsets[4])
+        assert int(sel.sum()) == om.n_esc > 0
+        assert np.array_equal(esc_idx[sel] - start, ocid * 1024 + opos)
+        assert np.array_equal(esc_ev[sel], oev)
