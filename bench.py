@@ -9,8 +9,9 @@ kernels are launched on.
 
 Prints ONE JSON line.  ``value`` is the end-to-end raw-BF16 throughput of the
 step (4 GiB / step time); the line also carries per-phase throughput, the
-compression ratio, the roofline of the dominant call and the CPU oracle timed
-on a bounded sample of the same workload.
+compression ratio, the roofline of the dominant call, the rate of a
+reference stream with each phase's access pattern (its practical ceiling) and
+the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -49,8 +50,8 @@ def parse():
 
 
 def d2d_copy(x_all, stream):
-    """Device-to-device copy of the 4 GiB workload (torch's copy kernel): the
-    practical streaming ceiling next to the codec's rates."""
+    """Device-to-device copy of the 4 GiB workload with torch's copy kernel
+    (a library reference; the access-pattern ceilings are pattern_ceilings)."""
     import torch
 
     dst = torch.empty_like(x_all)
@@ -66,6 +67,58 @@ def d2d_copy(x_all, stream):
     del dst
     return {"ms": round(ms, 4), "bytes_moved": moved, "GBps": round(moved / ms / 1e6, 1),
             "hbm_frac": round(moved / ms / 1e6 / HBM_PEAK_GBPS, 4), "kernel": "torch copy_"}
+
+
+def pattern_ceilings(S, x_all, phases, stream, reps):
+    """The reference memory streams (the codec kernels' loads and stores with
+    XORs for the coding) over the bytes of one batched launch of each phase:
+    the ceiling of each access pattern, timed in the same run, and each
+    phase's algorithmic rate as a fraction of it."""
+    import torch
+
+    lib = S._abi.ceiling_lib()
+    sh = int(stream.cuda_stream)
+    n = x_all[:32].numel()                       # elements of one 32-tensor launch
+    x = x_all[:32].reshape(-1)
+    scratch = torch.empty(n // 2 + n + 2 * n, dtype=torch.uint8, device=x_all.device)
+    pk, sm = scratch[: n // 2], scratch[n // 2: n // 2 + n]
+    out = scratch[n // 2 + n:]
+    sink = torch.zeros(1, dtype=torch.int32, device=x_all.device)
+
+    def ok(rc):
+        if rc:
+            raise S._abi.SplitZipError("reference stream", rc)
+
+    runs = {
+        "calibrate": ("k_read_shape", 2 * n,
+                      lambda: ok(lib.splitzip_ceiling_read(x.data_ptr(), 2 * n, 0,
+                                                           sink.data_ptr(), sh))),
+        "encode": ("k_encode_shape", 2 * n + n // 2 + n,
+                   lambda: ok(lib.splitzip_ceiling_encode_shape(x.data_ptr(), n, pk.data_ptr(),
+                                                                sm.data_ptr(), sh))),
+        "decode": ("k_decode_shape", n // 2 + n + 2 * n,
+                   lambda: ok(lib.splitzip_ceiling_decode_shape(pk.data_ptr(), sm.data_ptr(),
+                                                                out.data_ptr(), n, sh))),
+    }
+    res = {}
+    for phase, (kernel, moved, fn) in runs.items():
+        fn()
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        rate = moved / ms / 1e6
+        res[phase] = {"kernel": kernel, "bytes_per_launch": moved, "ms_per_launch": round(ms, 4),
+                      "GBps": round(rate, 1), "hbm_frac": round(rate / HBM_PEAK_GBPS, 4),
+                      "phase_frac_of_ceiling": round(phases[phase]["alg_GBps"] / rate, 4)}
+    del scratch
+    res["note"] = ("same loads, stores, workgroup shapes and data map as the codec kernel, "
+                   "XORs in place of the coding; 2^30 elements per launch, mean of %d" % reps)
+    return res
 
 
 def small_configs(S, W, dev, stream):
@@ -454,6 +507,7 @@ def main():
 
     slot = slot_decode_phase(S, batch, metas_h, x_all, stream, max(2, args.steps // 2))
     copy = d2d_copy(x_all, stream)
+    ceilings = pattern_ceilings(S, x_all, phases, stream, max(3, args.steps))
     small = None if args.no_small else small_configs(S, W, dev, stream)
     h2d = None if args.no_h2d else h2d_pipeline(S, batch, metas_h, x_all, dev, args.h2d_tensors)
     if h2d:
@@ -493,6 +547,7 @@ def main():
         "phases": phases,
         "per_call_phases": per_call,
         "d2d_copy": copy,
+        "pattern_ceilings": ceilings,
         "slot_decode": slot,
         "small_configs": small,
         "h2d_pipeline": h2d,

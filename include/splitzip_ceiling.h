@@ -1,0 +1,63 @@
+/*
+ * Reference memory streams for measuring the SplitZip kernels
+ * (libsplitzip_ceiling.so; not part of the codec).
+ *
+ * Each call moves the same bytes with the same access pattern as one codec
+ * kernel of libsplitzip.so -- load and store widths, cache hints, workgroup
+ * shape and the map from workgroups to data -- but replaces the coding with
+ * a few XORs.  Its rate is therefore the ceiling of that access pattern on
+ * the GPU it runs on, which is what a codec kernel can at best approach:
+ *
+ *   splitzip_ceiling_read           the calibrate histogram pass (reads 2n B)
+ *   splitzip_ceiling_encode_shape   the dense encode (reads 2n B, writes
+ *                                   n/2 B of nibbles and n B of bytes)
+ *   splitzip_ceiling_decode_shape   the dense decode (reads n/2 + n B,
+ *                                   writes 2n B)
+ *
+ * Conventions: every pointer is a device (or pinned host) address the
+ * caller owns and keeps alive until the stream has run the call; calls are
+ * asynchronous on `stream` (0 = the null stream); the output bytes are
+ * meaningless, only the traffic matters.  Return values are the SPLITZIP_OK
+ * / SPLITZIP_ERR_INVALID / SPLITZIP_ERR_HIP codes of splitzip.h.
+ */
+#ifndef SPLITZIP_CEILING_H
+#define SPLITZIP_CEILING_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Reads `bytes` bytes at d_x (16-byte aligned, bytes a multiple of 16) as
+ * 1024-thread workgroups, each streaming one contiguous range with 4 16-byte
+ * non-temporal loads in flight per thread.  `grid` workgroups (0: two per
+ * compute unit).  d_sink: 4 device bytes that receive a value only in the
+ * unlikely case that the XOR of a workgroup's data hits a fixed constant (it
+ * keeps the loads alive).  INVALID for a bad pointer, alignment or size. */
+int splitzip_ceiling_read(const void *d_x, uint64_t bytes, uint32_t grid, uint32_t *d_sink,
+                          hipStream_t stream);
+
+/* The encode pattern over n elements (n a positive multiple of 8192): one
+ * 8192-element tile per 256-thread workgroup; per 8 elements a 16-byte
+ * non-temporal load of d_x, a 4-byte non-temporal store to d_pk + i/2 and an
+ * 8-byte non-temporal store to d_sm + i.  d_x, d_pk, d_sm 16-byte aligned;
+ * d_pk holds n/2 bytes, d_sm n bytes.  INVALID otherwise. */
+int splitzip_ceiling_encode_shape(const uint16_t *d_x, uint64_t n, uint8_t *d_pk, uint8_t *d_sm,
+                                  hipStream_t stream);
+
+/* The decode pattern over n elements (n a positive multiple of 8192): one
+ * 8192-element tile per 256-thread workgroup; per 8 elements a 4-byte
+ * non-temporal load of d_pk + i/2, an 8-byte non-temporal load of d_sm + i
+ * and a 16-byte plain store to d_out + i.  Pointers 16-byte aligned; d_pk
+ * holds n/2 bytes, d_sm n bytes, d_out 2n bytes.  INVALID otherwise. */
+int splitzip_ceiling_decode_shape(const uint8_t *d_pk, const uint8_t *d_sm, uint16_t *d_out,
+                                  uint64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLITZIP_CEILING_H */

@@ -10,7 +10,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-from ._build import LIB_PATH
+from ._build import CEILING_LIB_PATH, LIB_PATH
 
 CHUNK = 1024
 MAX_N = 1 << 36
@@ -114,6 +114,32 @@ SIGNATURES = {
 }
 
 _lib = None
+
+
+CEILING_SIGNATURES = {
+    "splitzip_ceiling_read": (ctypes.c_int, [_P, ctypes.c_uint64, ctypes.c_uint32, _P, _P]),
+    "splitzip_ceiling_encode_shape": (ctypes.c_int, [_P, ctypes.c_uint64, _P, _P, _P]),
+    "splitzip_ceiling_decode_shape": (ctypes.c_int, [_P, _P, _P, ctypes.c_uint64, _P]),
+}
+
+_ceiling = None
+
+
+def ceiling_lib():
+    """Load the reference-stream library (measurement only; raises if it has
+    not been built)."""
+    global _ceiling
+    if _ceiling is not None:
+        return _ceiling
+    if not os.path.exists(CEILING_LIB_PATH):
+        raise RuntimeError("reference-stream library not built (%s missing)" % CEILING_LIB_PATH)
+    handle = ctypes.CDLL(CEILING_LIB_PATH)
+    for name, (res, args) in CEILING_SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    _ceiling = handle
+    return handle
 
 
 def lib():

@@ -1,4 +1,6 @@
-"""Build of the HIP library ``_lib/libsplitzip.so`` (gfx950 only)."""
+"""Build of the HIP libraries (gfx950 only): ``_lib/libsplitzip.so``, the
+codec, and ``_lib/libsplitzip_ceiling.so``, the reference memory streams its
+kernels are measured against."""
 from __future__ import annotations
 
 import os
@@ -10,6 +12,8 @@ SRC = os.path.join(PKG, "csrc", "splitzip.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libsplitzip.so")
+CEILING_SRC = os.path.join(PKG, "csrc", "ceiling.hip")
+CEILING_LIB_PATH = os.path.join(LIB_DIR, "libsplitzip_ceiling.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -29,11 +33,10 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile csrc/splitzip.hip into _lib/libsplitzip.so (always recompiles)."""
+def _compile(src: str, lib_path: str, verbose: bool) -> str:
     os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, SRC, "-o", tmp]
+    tmp = lib_path + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, src, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
@@ -41,8 +44,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
+def build(verbose: bool = False) -> str:
+    """Compile both libraries (always recompiles); returns the codec's path."""
+    _compile(CEILING_SRC, CEILING_LIB_PATH, verbose)
+    return _compile(SRC, LIB_PATH, verbose)
 
 
 if __name__ == "__main__":

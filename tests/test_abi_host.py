@@ -1,7 +1,8 @@
 """The C-ABI library loads on a machine without a GPU, exports every function
 include/splitzip.h declares, agrees with the binding's struct mirrors, and its
 host-side functions (layout size, workspace size, argument checks) behave.
-No device work is launched here."""
+The reference-stream library exports what include/splitzip_ceiling.h
+declares.  No device work is launched here."""
 import ctypes
 import os
 import re
@@ -16,8 +17,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "splitzip.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(splitzip_\w+)\s*\(", text)))
 
@@ -30,6 +31,21 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(lib, name), name
         assert name in _abi.SIGNATURES, name
     assert set(_abi.SIGNATURES) == set(names)
+
+
+def test_reference_stream_symbols_and_argument_errors():
+    lib = _abi.ceiling_lib()
+    names = declared_functions(os.path.join(ROOT, "include", "splitzip_ceiling.h"))
+    assert names == sorted(_abi.CEILING_SIGNATURES), names
+    for name in names:
+        assert hasattr(lib, name), name
+    # sizes that are not whole tiles, null or misaligned pointers: no launch
+    assert lib.splitzip_ceiling_read(0, 1 << 20, 0, 0x1000, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_read(0x1000, 24, 0, 0x1000, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_encode_shape(0x1000, 8191, 0x2000, 0x3000, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_encode_shape(0x1008, 8192, 0x2000, 0x3000, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_decode_shape(0x1000, 0x2000, 0x3000, 0, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_decode_shape(0x1000, 0, 0x3000, 8192, 0) == _abi.ERR_INVALID
 
 
 def test_struct_layout_matches_header():
