@@ -32,7 +32,7 @@
 //                 to each other.
 //   k_encode_sums (large tensors only) escapes per block of tiles and per
 //                 256-tile superblock, so escape placement needs few loads.
-//   k_encode_tail every workgroup takes a block of 8-64 tiles, finds the rank
+//   k_encode_tail every workgroup takes a block of 4-64 tiles, finds the rank
 //                 of its first escape and the tensor's escape count, and
 //                 writes chunk id, chunk-local position and raw exponent of
 //                 each of its escapes at its final rank; the tensor's first
