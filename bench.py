@@ -121,12 +121,13 @@ def pattern_ceilings(S, x_all, phases, stream, reps):
     return res
 
 
-def small_configs(S, W, dev, stream):
+def small_configs(S, W, dev, stream, host_inputs=None):
     """The smaller single-tensor workloads: one call per phase, median GPU
     time of 20 calls (100 decodes into one output buffer for the linear
     weight), warm (after 3 warm-up calls; they fit the 256 MB last-level
     cache) and cold (a 512 MiB buffer is written before each call).  No
-    roofline claim is made for these."""
+    roofline claim is made for these.  With ``host_inputs`` (a dict), each
+    workload's bits are also copied to it for the oracle."""
     import statistics
 
     import torch
@@ -185,8 +186,47 @@ def small_configs(S, W, dev, stream):
         rec["payload_over_raw"] = round(comp / (2 * rec["elements"]), 6)
         rec["escape_fraction"] = round(esc / rec["elements"], 6)
         out[name] = rec
+        if host_inputs is not None:
+            host_inputs[name] = [x.reshape(-1).view(torch.int16).cpu() for x in xs]
     del scrub
     return out
+
+
+def cpu_small_configs(host_inputs):
+    """The oracle (one core) on each smaller workload, per phase: the median
+    of 3 runs of each tensor's calibrate, encode and decode."""
+    import statistics
+
+    import numpy as np
+
+    import oracle
+
+    o = oracle.default()
+    res = {}
+    for name, xs in host_inputs.items():
+        ms = {"calibrate": 0.0, "encode": 0.0, "decode": 0.0}
+        elems = 0
+        for xt in xs:
+            a = xt.numpy().view(np.uint16)
+            elems += a.size
+            ts = {k: [] for k in ms}
+            for _ in range(3):
+                t0 = time.perf_counter()
+                cb = o.calibrate(a)
+                t1 = time.perf_counter()
+                payload, meta = o.encode(a, cb)
+                t2 = time.perf_counter()
+                back = o.decode(payload, meta, cb.dec_lut)
+                t3 = time.perf_counter()
+                for k, dt in zip(ms, (t1 - t0, t2 - t1, t3 - t2)):
+                    ts[k].append(dt * 1e3)
+            if not np.array_equal(back, a):
+                raise AssertionError("oracle round trip failed on " + name)
+            for k in ms:
+                ms[k] += statistics.median(ts[k])
+        res[name] = {k: {"ms": round(v, 3), "raw_GBps": round(2 * elems / v / 1e6, 3)}
+                     for k, v in ms.items()}
+    return res
 
 
 def slot_decode_phase(S, batch, metas_h, x_all, stream, passes):
@@ -508,7 +548,8 @@ def main():
     slot = slot_decode_phase(S, batch, metas_h, x_all, stream, max(2, args.steps // 2))
     copy = d2d_copy(x_all, stream)
     ceilings = pattern_ceilings(S, x_all, phases, stream, max(3, args.steps))
-    small = None if args.no_small else small_configs(S, W, dev, stream)
+    small_inputs = None if args.no_cpu_baseline else {}
+    small = None if args.no_small else small_configs(S, W, dev, stream, small_inputs)
     h2d = None if args.no_h2d else h2d_pipeline(S, batch, metas_h, x_all, dev, args.h2d_tensors)
     if h2d:
         # the decode must outrun the link it sits behind (raw bytes per second)
@@ -517,6 +558,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x_all, args.cpu_seconds)
+        if small_inputs:
+            cpu["small_configs"] = cpu_small_configs(small_inputs)
 
     line = {
         "metric": METRIC,
