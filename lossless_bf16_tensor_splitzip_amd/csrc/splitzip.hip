@@ -30,7 +30,7 @@
 //                 ballots to rank the tile's escapes, which are staged in the
 //                 workspace with the tile's escape count.  Tiles never talk
 //                 to each other.
-//   k_encode_sums (large tensors only) escapes per block of tiles and per
+//   k_encode_sums (large launches only) escapes per block of tiles and per
 //                 256-tile superblock, so escape placement needs few loads.
 //   k_encode_tail every workgroup takes a block of 4-64 tiles, finds the rank
 //                 of its first escape and the tensor's escape count, and
@@ -72,7 +72,7 @@ namespace {
 #define SPLITZIP_TAIL_TARGET_WGS 1024   // ... and the workgroup count it aims at
 #endif
 #ifndef SPLITZIP_TAIL_DIRECT
-#define SPLITZIP_TAIL_DIRECT 1024   // tiles per tensor up to which no count sums run
+#define SPLITZIP_TAIL_DIRECT (1u << 22)   // tile counts the tail launch may read without sums
 #endif
 #ifndef SPLITZIP_TAIL_THREADS
 #define SPLITZIP_TAIL_THREADS 256   // escape placement workgroup size
@@ -1303,17 +1303,14 @@ int launch_encode(const EncItem *items, uint32_t count, const WsPlan &P, uint8_t
     a.count = count;
     a.tile_count = reinterpret_cast<uint32_t *>(ws + P.off_count);
     a.stage = reinterpret_cast<uint32_t *>(ws + P.off_stage);
-    uint64_t tiles = 0, most = 0;
-    for (uint32_t k = 0; k < count; ++k) {
-        const uint64_t t = enc_tiles(items[k].n);
-        tiles += t;
-        if (t > most) most = t;
-    }
+    uint64_t tiles = 0;
+    for (uint32_t k = 0; k < count; ++k) tiles += enc_tiles(items[k].n);
     uint32_t tt = kTailMinTiles;
     while (tt < (uint32_t)kTailMaxTiles && tiles / (2 * tt) >= kTailTargetWgs) tt *= 2;
     a.tail_tiles = tt;
     tiles = 0;
     uint32_t blks = 0, sups = 0;
+    uint64_t direct_loads = 0;   // tile counts read by the tail launch without sums
     for (uint32_t k = 0; k < count; ++k) {
         a.it[k] = items[k];
         a.tile_start[k] = tiles;
@@ -1324,6 +1321,7 @@ int launch_encode(const EncItem *items, uint32_t count, const WsPlan &P, uint8_t
         const uint64_t b = ceil_div(t, tt);
         blks += (uint32_t)(b ? b : 1);   // an empty tensor still gets its metadata
         sups += (uint32_t)ceil_div(t, kSuperTiles);
+        direct_loads += t * b;
     }
     a.tile_start[count] = tiles;
     a.blk_start[count] = blks;
@@ -1333,10 +1331,13 @@ int launch_encode(const EncItem *items, uint32_t count, const WsPlan &P, uint8_t
         k_encode<<<(unsigned)tiles, kThreads, 0, s>>>(a);
         if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     }
-    // Past kTailDirect tiles per tensor, one more launch that sums the counts
-    // per tail block and per superblock is cheaper than every tail workgroup
-    // reading all of a tensor's counts.
-    if (most > kTailDirect) {
+    // When every tail workgroup reading all of its tensor's tile counts adds
+    // up to more than kTailDirect loads (16 MB at the default, about the cost
+    // of a launch), one more launch first sums the counts per tail block and
+    // per superblock.  A single call on a 64 MiB tensor stays below it
+    // (measured: 3 us less on the GPU and one launch fewer per call); a batch
+    // of 32 such tensors is above it (2.5 us less with the sums).
+    if (direct_loads > kTailDirect) {
         a.blk_sum = reinterpret_cast<uint32_t *>(ws + P.off_bsum);
         a.sup_sum = reinterpret_cast<uint32_t *>(ws + P.off_ssum);
         k_encode_sums<<<sups, kThreads, 0, s>>>(a);

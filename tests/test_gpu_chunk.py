@@ -64,9 +64,10 @@ def test_chunk_sizes_weight(chunk):
 
 
 def test_large_single_tensor_summed_placement():
-    """2^28 + 5 elements: 32,769 encode tiles, 129 placement workgroups, so
-    the placement first sums the counts per workgroup.  Escapes are planted
-    every 997 elements on top of N(0, 0.02) values."""
+    """2^28 + 5 elements: 32,769 encode tiles, 1,025 placement workgroups of
+    32 tiles, so the placement first sums the counts per workgroup and per
+    superblock (read directly, the counts would cost 33.6M loads).  Escapes
+    are planted every 997 elements on top of N(0, 0.02) values."""
     n = (1 << 28) + 5
     b = host_bits(W.gaussian_weight(n, seed=602)).copy()
     k = np.arange(0, n, 997)
