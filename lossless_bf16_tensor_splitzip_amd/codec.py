@@ -69,7 +69,8 @@ def calibrate(x: torch.Tensor, ws: Workspace, cb: torch.Tensor | None = None,
     xb = _bits(x)
     if cb is None:
         cb = new_codebook(x.device)
-    _device_or_pinned(cb, "codebook")
+    _buf(cb, CODEBOOK_BYTES, "codebook")
+    _same_gpu(x.device, ws.buf)
     _abi._check("splitzip_calibrate",
                 _abi.splitzip_calibrate(xb.data_ptr(), xb.numel(), cb.data_ptr(), ws.ptr(),
                                         ws.nbytes, _stream(stream, x.device)))
@@ -86,14 +87,15 @@ def encode(x: torch.Tensor, cb: torch.Tensor, ws: Workspace, payload: torch.Tens
     n = xb.numel()
     if payload is None:
         payload = torch.empty(max(payload_size(n, n), 16), dtype=torch.uint8, device=x.device)
-    _device_or_pinned(payload, "payload")
+    capacity = _buf(payload, 0, "payload")
     if meta is None:
         meta = new_meta(x.device)
-    _device_or_pinned(cb, "codebook")
-    _device_or_pinned(meta, "metadata")
+    _buf(cb, CODEBOOK_BYTES, "codebook")
+    _buf(meta, META_BYTES, "metadata")
+    _same_gpu(x.device, ws.buf, payload, cb, meta)
     _abi._check("splitzip_encode_chunked",
                 _abi.splitzip_encode_chunked(xb.data_ptr(), n, cb.data_ptr(), chunk_size,
-                                             payload.data_ptr(), payload.numel(),
+                                             payload.data_ptr(), capacity,
                                              meta.data_ptr(), ws.ptr(), ws.nbytes,
                                              _stream(stream, x.device)))
     return payload, meta
@@ -107,18 +109,18 @@ def decode(payload: torch.Tensor, meta: torch.Tensor, cb_or_dec_lut: torch.Tenso
     payload may also sit in pinned host memory: the kernel then reads it over
     the host link while it decodes (no separate copy)."""
     dev = _gpu_of(out, meta, cb_or_dec_lut, payload)
-    _device_or_pinned(payload, "payload")
+    payload_bytes = _buf(payload, 0, "payload")
     if out is None:
         out = torch.empty(n, dtype=torch.bfloat16, device=dev)
     if out.dtype is not torch.bfloat16 or not out.is_contiguous() or out.numel() != n:
         raise ValueError("out must be a contiguous bfloat16 tensor of n elements")
-    for t, what in ((meta, "metadata"), (cb_or_dec_lut, "codebook"), (out, "output")) + \
-            (() if status is None else ((status, "status word"),)):
-        _device_or_pinned(t, what)
+    _device_or_pinned(out, "output")
+    _buf(meta, META_BYTES, "metadata")
+    st_ptr = _status_ptr(status)
+    _same_gpu(dev, payload, meta, cb_or_dec_lut, out, status)
     lut_ptr = _lut_ptr(cb_or_dec_lut)
-    st_ptr = 0 if status is None else status.data_ptr()
     _abi._check("splitzip_decode",
-                _abi.splitzip_decode(payload.data_ptr(), payload.numel(), meta.data_ptr(),
+                _abi.splitzip_decode(payload.data_ptr(), payload_bytes, meta.data_ptr(),
                                      lut_ptr, out.data_ptr(), n, st_ptr, _stream(stream, dev)))
     return out
 
@@ -129,6 +131,34 @@ def _device_or_pinned(t: torch.Tensor, what: str) -> None:
         raise ValueError("the %s must be on the GPU or in pinned host memory" % what)
 
 
+def _buf(t: torch.Tensor, nbytes: int, what: str) -> int:
+    """Checks a raw buffer handed to the kernels (device or pinned host,
+    contiguous, at least ``nbytes`` bytes) and returns its size in bytes."""
+    _device_or_pinned(t, what)
+    if not t.is_contiguous():
+        raise ValueError("the %s must be a contiguous tensor" % what)
+    size = t.numel() * t.element_size()
+    if size < nbytes:
+        raise ValueError("the %s needs at least %d bytes, got %d" % (what, nbytes, size))
+    return size
+
+
+def _status_ptr(status: torch.Tensor | None) -> int:
+    if status is None:
+        return 0
+    if status.dtype is not torch.int32:
+        raise ValueError("the status word must be an int32 tensor")
+    _buf(status, 4, "status word")
+    return status.data_ptr()
+
+
+def _same_gpu(dev: torch.device, *tensors) -> None:
+    # every device buffer of one call lives on the GPU the call runs on
+    for t in tensors:
+        if t is not None and t.device.type == "cuda" and t.device != dev:
+            raise ValueError("all device buffers of a call must be on %s, got %s" % (dev, t.device))
+
+
 def _gpu_of(*tensors) -> torch.device:
     for t in tensors:
         if t is not None and t.device.type == "cuda":
@@ -137,10 +167,12 @@ def _gpu_of(*tensors) -> torch.device:
 
 
 def _lut_ptr(cb_or_dec_lut: torch.Tensor) -> int:
-    if cb_or_dec_lut.numel() == CODEBOOK_BYTES:
+    size = _buf(cb_or_dec_lut, 0, "codebook")
+    if size == CODEBOOK_BYTES:
         return cb_or_dec_lut.data_ptr() + _abi.DEC_LUT_OFFSET
-    if cb_or_dec_lut.numel() != 16:
-        raise ValueError("expected a codebook or a 16-entry dec_lut")
+    if size != 16:
+        raise ValueError("expected a codebook (%d bytes) or a 16-byte dec_lut, got %d bytes"
+                         % (CODEBOOK_BYTES, size))
     return cb_or_dec_lut.data_ptr()
 
 
@@ -156,16 +188,15 @@ def decode_slot(slot: torch.Tensor, meta: torch.Tensor, cb_or_dec_lut: torch.Ten
         # page 1, decode_slot_into: the slot must be contiguous
         raise ValueError("the slot tensor must be contiguous")
     raw = slot.reshape(-1).view(torch.uint8)
-    for t, what in ((raw, "slot"), (stash, "stash"), (meta, "metadata"),
-                    (cb_or_dec_lut, "codebook")) + \
-            (() if status is None else ((status, "status word"),)):
-        _device_or_pinned(t, what)
-    st_ptr = 0 if status is None else status.data_ptr()
+    _device_or_pinned(raw, "slot")
+    stash_bytes = _buf(stash, 0, "stash")
+    _buf(meta, META_BYTES, "metadata")
+    st_ptr = _status_ptr(status)
+    _same_gpu(slot.device, stash, meta, cb_or_dec_lut, status)
     _abi._check("splitzip_decode_slot",
                 _abi.splitzip_decode_slot(raw.data_ptr(), raw.numel(), meta.data_ptr(),
                                           _lut_ptr(cb_or_dec_lut), n, stash.data_ptr(),
-                                          stash.numel() * stash.element_size(), st_ptr,
-                                          _stream(stream, slot.device)))
+                                          stash_bytes, st_ptr, _stream(stream, slot.device)))
     return raw[: 2 * n].view(torch.bfloat16)
 
 
@@ -182,19 +213,17 @@ def decode_slots(slots, metas, cbs_or_luts, ns, stashes, status: torch.Tensor | 
         if not slots[k].is_contiguous():
             raise ValueError("the slot tensors must be contiguous")
         raw = slots[k].reshape(-1).view(torch.uint8)
-        for t, what in ((raw, "slot"), (stashes[k], "stash"), (metas[k], "metadata"),
-                        (cbs_or_luts[k], "codebook")):
-            _device_or_pinned(t, what)
+        _device_or_pinned(raw, "slot")
+        _buf(metas[k], META_BYTES, "metadata")
         raws.append(raw)
         it = items[k]
         it.slot, it.slot_bytes = raw.data_ptr(), raw.numel()
         it.meta, it.dec_lut, it.n = metas[k].data_ptr(), _lut_ptr(cbs_or_luts[k]), ns[k]
         it.stash = stashes[k].data_ptr()
-        it.stash_bytes = stashes[k].numel() * stashes[k].element_size()
-    if status is not None:
-        _device_or_pinned(status, "status word")
-    st_ptr = 0 if status is None else status.data_ptr()
+        it.stash_bytes = _buf(stashes[k], 0, "stash")
+    st_ptr = _status_ptr(status)
     dev = _gpu_of(*slots, *metas) if count else torch.device("cuda")
+    _same_gpu(dev, *slots, *stashes, *metas, *cbs_or_luts, status)
     _abi._check("splitzip_decode_slot_batch",
                 _abi.splitzip_decode_slot_batch(items, count, st_ptr, _stream(stream, dev)))
     return [raw[: 2 * n].view(torch.bfloat16) for raw, n in zip(raws, ns)]
@@ -244,7 +273,7 @@ class Batch:
                                                _stream(stream, self.device)))
 
     def decode(self, status: torch.Tensor | None = None, stream=None):
-        st_ptr = 0 if status is None else status.data_ptr()
+        st_ptr = _status_ptr(status)
         _abi._check("splitzip_decode_batch",
                     _abi.splitzip_decode_batch(self.items, self.count, st_ptr,
                                                _stream(stream, self.device)))
