@@ -78,6 +78,8 @@ def pattern_ceilings(S, x_all, phases, stream, reps):
 
     lib = S._abi.ceiling_lib()
     sh = int(stream.cuda_stream)
+    # the batched calibrate launch of this size runs one workgroup per compute unit
+    cus = torch.cuda.get_device_properties(x_all.device).multi_processor_count
     n = x_all[:32].numel()                       # elements of one 32-tensor launch
     x = x_all[:32].reshape(-1)
     scratch = torch.empty(n // 2 + n + 2 * n, dtype=torch.uint8, device=x_all.device)
@@ -91,7 +93,7 @@ def pattern_ceilings(S, x_all, phases, stream, reps):
 
     runs = {
         "calibrate": ("k_read_shape", 2 * n,
-                      lambda: ok(lib.splitzip_ceiling_read(x.data_ptr(), 2 * n, 0,
+                      lambda: ok(lib.splitzip_ceiling_read(x.data_ptr(), 2 * n, cus,
                                                            sink.data_ptr(), sh))),
         "encode": ("k_encode_shape", 2 * n + n // 2 + n,
                    lambda: ok(lib.splitzip_ceiling_encode_shape(x.data_ptr(), n, pk.data_ptr(),
