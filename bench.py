@@ -534,9 +534,10 @@ def main():
                      "hbm_frac": round(gbps(alg[k], ms) / HBM_PEAK_GBPS, 4)}
     per_call = {k: {"ms": round(v, 4), "raw_GBps": round(gbps(raw_bytes, v), 1),
                     "alg_GBps": round(gbps(alg[k], v), 1)} for k, v in per_call_ms.items()}
-    # Roofline of the dominant kernel: the decode kernel is the longest single
-    # kernel of the step (the encode phase is three launches: main, count
-    # sums, escape placement), and its phase time is that kernel's time.
+    # Roofline of the dominant kernel: the decode kernel and the main encode
+    # kernel are the two longest of the step, about equally long; the decode
+    # phase is that one kernel, so its event time is the kernel's time (the
+    # encode phase is three launches: main, count sums, escape placement).
     dom = "decode"
     achieved = gbps(alg[dom], phase_ms[dom])
     roofline = {"bound": "hbm", "kernel": "k_decode<4>", "phase": dom,

@@ -51,7 +51,7 @@ int splitzip_ceiling_encode_shape(const uint16_t *d_x, uint64_t n, uint8_t *d_pk
 /* The decode pattern over n elements (n a positive multiple of 8192): one
  * 8192-element tile per 256-thread workgroup; per 8 elements a 4-byte
  * non-temporal load of d_pk + i/2, an 8-byte non-temporal load of d_sm + i
- * and a 16-byte plain store to d_out + i.  Pointers 16-byte aligned; d_pk
+ * and a 16-byte non-temporal store to d_out + i.  Pointers 16-byte aligned; d_pk
  * holds n/2 bytes, d_sm n bytes, d_out 2n bytes.  INVALID otherwise. */
 int splitzip_ceiling_decode_shape(const uint8_t *d_pk, const uint8_t *d_sm, uint16_t *d_out,
                                   uint64_t n, hipStream_t stream);

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_shape(const uint8_t *pk, co
     for (int u = 0; u < kUnits; ++u) {
         const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
         const u32x4 o = {p[u] ^ s[u].x, p[u] ^ s[u].y, s[u].x ^ 0x5A5A5A5Au, s[u].y ^ 0xA5A5A5A5u};
-        *reinterpret_cast<u32x4 *>(out + i0) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(out + i0));
     }
 }
 

@@ -100,7 +100,15 @@ constexpr int kTailThreads = SPLITZIP_TAIL_THREADS;
 constexpr int kSuperTiles = 256;              // tiles per second-level count sum
 constexpr uint64_t kTailDirect = SPLITZIP_TAIL_DIRECT;
 constexpr uint32_t kMaxChunk = 65536;         // chunk-local positions are uint16
-constexpr int kDecUnits = 4;                  // decode: units per thread per tile (8192 elements)
+#ifndef SPLITZIP_DEC_THREADS
+#define SPLITZIP_DEC_THREADS 256    // decode workgroup
+#endif
+#ifndef SPLITZIP_DEC_UNITS
+#define SPLITZIP_DEC_UNITS 4        // decode: 8-element units per thread per tile
+#endif
+constexpr int kDecThreads = SPLITZIP_DEC_THREADS;
+constexpr int kDecUnits = SPLITZIP_DEC_UNITS;
+constexpr int kDecStaged = 512;               // decode: escapes per tile above which sm goes to LDS
 constexpr uint32_t kStageDirect = 256;        // encode: escapes per tile written directly
 constexpr uint32_t kStageLds = 2048;          // ... beyond that, ranks per LDS round
 
@@ -920,10 +928,9 @@ __device__ inline uint64_t lower_bound_wave(const int32_t *cid, uint64_t lo, uin
     return lo + __popcll(__ballot(v < key));
 }
 
-template <int kUnits, int kMode>
+template <int kTh, int kUnits, int kMode>
 __device__ __forceinline__ void decode_tile(const DecArgs &a) {
-    constexpr int kDecUnits = kUnits;
-    constexpr int kDecTile = kThreads * kUnit * kDecUnits;
+    constexpr int kDecTile = kTh * kUnit * kUnits;
     __shared__ uint32_t pair_lut[256];      // pk byte -> (even exponent, odd exponent << 16)
     __shared__ uint64_t range[2];
     // Output tile of a tensor with dense escapes, or the sm bytes of a tile
@@ -943,19 +950,19 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     const Layout L0 = layout_of(I.n, 0);
     const uint8_t *pk = I.payload;
     const uint8_t *sm = I.payload + L0.off_sm;
-    uint32_t pkw[kDecUnits];
-    u32x2 smw[kDecUnits];
+    uint32_t pkw[kUnits];
+    u32x2 smw[kUnits];
     // second slot pass: tiles before the dense sections' end are certainly stashed
     const bool early = full && (kMode != kSlotFinish || tile < L0.total / (2 * kDecTile));
     if (early) {
 #pragma unroll
-        for (int u = 0; u < kDecUnits; ++u) {
-            const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+        for (int u = 0; u < kUnits; ++u) {
+            const uint64_t i0 = base + (uint64_t)u * (kTh * kUnit) + tid * kUnit;
             pkw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(pk + i0 / 2));
             smw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4 *>(sm + i0));
         }
     }
-    const uint32_t lut_entry = (uint32_t)I.dec_lut[tid >> 4] | ((uint32_t)I.dec_lut[tid & 15] << 16);
+    const uint32_t lut_entry = tid < 256 ? ((uint32_t)I.dec_lut[(tid >> 4) & 15] | ((uint32_t)I.dec_lut[tid & 15] << 16)) : 0u;
     Layout L;
     if (!meta_ok(I, L) || (kMode != kPlain && L.total > I.other_bytes)) {
         // nothing is written for inconsistent metadata
@@ -972,8 +979,8 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
             const uint64_t esc_bytes = L.total - L.off_cid;
             const uint32_t *src = reinterpret_cast<const uint32_t *>(I.payload + L.off_cid);
             uint32_t *dst = reinterpret_cast<uint32_t *>(I.stash + L.off_cid);
-            const uint64_t stride = tiles * kThreads;
-            for (uint64_t w = tile * kThreads + tid; w < esc_bytes / 4; w += stride) dst[w] = src[w];
+            const uint64_t stride = tiles * kTh;
+            for (uint64_t w = tile * kTh + tid; w < esc_bytes / 4; w += stride) dst[w] = src[w];
             if (tile == 0 && tid < (int)(esc_bytes & 3)) {
                 const uint64_t b = L.off_cid + (esc_bytes & ~uint64_t(3)) + tid;
                 I.stash[b] = I.payload[b];
@@ -981,15 +988,15 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
             if (tile < t_split) {   // output overlaps the payload: stash the inputs
                 if (full) {
 #pragma unroll
-                    for (int u = 0; u < kDecUnits; ++u) {
-                        const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+                    for (int u = 0; u < kUnits; ++u) {
+                        const uint64_t i0 = base + (uint64_t)u * (kTh * kUnit) + tid * kUnit;
                         *reinterpret_cast<uint32_t *>(I.stash + i0 / 2) = pkw[u];
                         *reinterpret_cast<u32x2_a4 *>(I.stash + L0.off_sm + i0) = smw[u];
                     }
                 } else {
-                    for (uint64_t b = base / 2 + tid; b < L0.n_pairs; b += kThreads)
+                    for (uint64_t b = base / 2 + tid; b < L0.n_pairs; b += kTh)
                         I.stash[b] = pk[b];
-                    for (uint64_t i = base + tid; i < I.n; i += kThreads)
+                    for (uint64_t i = base + tid; i < I.n; i += kTh)
                         I.stash[L0.off_sm + i] = sm[i];
                 }
                 return;
@@ -998,8 +1005,8 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
             if (tile >= t_split) return;   // decoded by the first pass
             if (full && !early) {
 #pragma unroll
-                for (int u = 0; u < kDecUnits; ++u) {
-                    const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+                for (int u = 0; u < kUnits; ++u) {
+                    const uint64_t i0 = base + (uint64_t)u * (kTh * kUnit) + tid * kUnit;
                     pkw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(pk + i0 / 2));
                     smw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4 *>(sm + i0));
                 }
@@ -1011,7 +1018,8 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     const uint16_t *lpos = reinterpret_cast<const uint16_t *>(I.payload + L.off_lpos);
     const uint8_t *ev = I.payload + L.off_ev;
 
-    pair_lut[tid] = lut_entry;
+    static_assert(kTh >= 256, "one pair-table entry per thread");
+    if (tid < 256) pair_lut[tid] = lut_entry;
     // A tensor whose escapes average more than 512 per tile is decoded tile
     // by tile in LDS (dense values, the patch, then one coalesced store):
     // scattering thousands of 2-byte stores per tile to memory costs more
@@ -1022,8 +1030,8 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     // Dense part first: every element through the pair table, 16-byte stores.
     if (full) {
 #pragma unroll
-        for (int u = 0; u < kDecUnits; ++u) {
-            const int l0 = u * (kThreads * kUnit) + tid * kUnit;
+        for (int u = 0; u < kUnits; ++u) {
+            const int l0 = u * (kTh * kUnit) + tid * kUnit;
             u32x4 o;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -1033,11 +1041,11 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
             }
             if (in_lds)
                 *reinterpret_cast<u32x4 *>(tile_buf + l0 / 2) = o;
-            else   // plain stores: measured faster than non-temporal ones for this stream
-                *reinterpret_cast<u32x4 *>(I.out + base + l0) = o;
+            else   // non-temporal: 5 % faster than plain stores for this stream
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(I.out + base + l0));
         }
     } else {
-        for (uint64_t i = base + tid; i < I.n; i += kThreads) {
+        for (uint64_t i = base + tid; i < I.n; i += kTh) {
             const uint32_t byte = pk[i / 2];
             const uint32_t code = (i & 1) ? (byte & 15u) : (byte >> 4);
             I.out[i] = (uint16_t)join16(sm[i], pair_lut[code << 4] & 0xFFu);
@@ -1077,12 +1085,12 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     if (in_lds) {
         // the decoded value already holds the sign and mantissa
         uint16_t *t16 = reinterpret_cast<uint16_t *>(tile_buf);
-        for (uint64_t rb = r0; rb < r1; rb += 8 * kThreads) {
+        for (uint64_t rb = r0; rb < r1; rb += 8 * kTh) {
             int32_t l8[8];
             uint32_t e8[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const uint64_t r = rb + q * kThreads + tid;
+                const uint64_t r = rb + q * kTh + tid;
                 l8[q] = -1;
                 e8[q] = 0;
                 if (r < r1) {
@@ -1098,21 +1106,21 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
         }
         __syncthreads();
 #pragma unroll
-        for (int u = 0; u < kDecUnits; ++u) {
-            const int l0 = u * (kThreads * kUnit) + tid * kUnit;
-            *reinterpret_cast<u32x4 *>(I.out + base + l0) =
-                *reinterpret_cast<const u32x4 *>(tile_buf + l0 / 2);
+        for (int u = 0; u < kUnits; ++u) {
+            const int l0 = u * (kTh * kUnit) + tid * kUnit;
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(tile_buf + l0 / 2),
+                                        reinterpret_cast<u32x4 *>(I.out + base + l0));
         }
         return;
     }
     // A tile with many escapes in a sparse tensor keeps its sm bytes (still
     // in registers) in LDS for the patch, instead of reading each one back
     // from memory.
-    const bool staged = full && r1 - r0 > 2 * kThreads;
+    const bool staged = full && r1 - r0 > kDecStaged;
     if (staged) {
 #pragma unroll
-        for (int u = 0; u < kDecUnits; ++u) {
-            const int o = u * (kThreads * kUnit) + tid * kUnit;
+        for (int u = 0; u < kUnits; ++u) {
+            const int o = u * (kTh * kUnit) + tid * kUnit;
             tile_buf[o / 4] = smw[u].x;
             tile_buf[o / 4 + 1] = smw[u].y;
         }
@@ -1125,12 +1133,12 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     constexpr int kPatch = SPLITZIP_DEC_PATCH;
     // kPatch escapes per thread in flight: their stream entries, then their
     // sm bytes, then the stores
-    for (uint64_t rb = r0; rb < r1; rb += kPatch * kThreads) {
+    for (uint64_t rb = r0; rb < r1; rb += kPatch * kTh) {
         int64_t idx[kPatch];
         uint32_t evv[kPatch], smv[kPatch];
 #pragma unroll
         for (int q = 0; q < kPatch; ++q) {
-            const uint64_t r = rb + q * kThreads + tid;
+            const uint64_t r = rb + q * kTh + tid;
             idx[q] = -1;
             evv[q] = 0;
             if (r < r1) {
@@ -1150,14 +1158,16 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
 }
 
 template <int kUnits>
-__global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) { decode_tile<kUnits, kPlain>(a); }
-
-__global__ __launch_bounds__(kThreads) void k_decode_slot_stage(DecArgs a) {
-    decode_tile<kDecUnits, kSlotStage>(a);
+__global__ __launch_bounds__(kDecThreads) void k_decode(DecArgs a) {
+    decode_tile<kDecThreads, kUnits, kPlain>(a);
 }
 
-__global__ __launch_bounds__(kThreads) void k_decode_slot_finish(DecArgs a) {
-    decode_tile<kDecUnits, kSlotFinish>(a);
+__global__ __launch_bounds__(kDecThreads) void k_decode_slot_stage(DecArgs a) {
+    decode_tile<kDecThreads, kDecUnits, kSlotStage>(a);
+}
+
+__global__ __launch_bounds__(kDecThreads) void k_decode_slot_finish(DecArgs a) {
+    decode_tile<kDecThreads, kDecUnits, kSlotFinish>(a);
 }
 
 // Validation (and order-independent re-application) of every escape.  The
@@ -1364,11 +1374,11 @@ int launch_decode(const DecItem *items, uint32_t count, int32_t *status, hipStre
     for (uint32_t k = 0; k < count; ++k) {
         a.it[k] = items[k];
         a.tile_start[k] = tiles;
-        tiles += ceil_div(items[k].n, (uint64_t)kDecUnits * kThreads * kUnit);
+        tiles += ceil_div(items[k].n, (uint64_t)kDecUnits * kDecThreads * kUnit);
     }
     a.tile_start[count] = tiles;
     if (tiles) {
-        k_decode<kDecUnits><<<(unsigned)tiles, kThreads, 0, s>>>(a);
+        k_decode<kDecUnits><<<(unsigned)tiles, kDecThreads, 0, s>>>(a);
         if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     }
     if (status) {
@@ -1388,7 +1398,7 @@ int launch_decode(const DecItem *items, uint32_t count, int32_t *status, hipStre
 // stashed tiles over the payload.
 int launch_decode_slot(const splitzip_slot_item *items, uint32_t count, int32_t *status,
                        hipStream_t s) {
-    constexpr uint64_t kTile = (uint64_t)kDecUnits * kThreads * kUnit;
+    constexpr uint64_t kTile = (uint64_t)kDecUnits * kDecThreads * kUnit;
     DecArgs a{};
     a.count = count;
     a.status = status;
@@ -1403,7 +1413,7 @@ int launch_decode_slot(const splitzip_slot_item *items, uint32_t count, int32_t 
     }
     a.tile_start[count] = tiles;
     if (tiles == 0) return SPLITZIP_OK;
-    k_decode_slot_stage<<<(unsigned)tiles, kThreads, 0, s>>>(a);
+    k_decode_slot_stage<<<(unsigned)tiles, kDecThreads, 0, s>>>(a);
     if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     for (uint32_t k = 0; k < count; ++k) {
         a.it[k].payload = items[k].stash;
@@ -1411,7 +1421,7 @@ int launch_decode_slot(const splitzip_slot_item *items, uint32_t count, int32_t 
         a.it[k].stash = nullptr;
         a.it[k].other_bytes = items[k].slot_bytes;
     }
-    k_decode_slot_finish<<<(unsigned)tiles, kThreads, 0, s>>>(a);
+    k_decode_slot_finish<<<(unsigned)tiles, kDecThreads, 0, s>>>(a);
     if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     if (status) {
         uint64_t cgrid = ceil_div(n_all, 16 * kThreads);
