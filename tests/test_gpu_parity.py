@@ -202,6 +202,34 @@ def test_escapes_at_chunk_and_tile_edges():
     assert om.n_esc == len(edges)
 
 
+def test_decode_patch_paths():
+    """Each way the decode applies escapes, byte for byte: scattered from
+    registers (a tile with few), through the tile's sign/mantissa bytes staged
+    in LDS (a tile with more than 512 while the tensor averages fewer), and
+    with the whole tile built in LDS (more than 512 per tile on average)."""
+    src = torch.ones(8, dtype=torch.bfloat16)          # codes exponent 127 only
+    n = 6 * 8192 + 100
+    b = np.full(n, 0x3F80, np.uint16)
+    j = np.arange(100)
+    few = 8192 + 37 * j                                 # tile 1: 100 escapes
+    b[few] = ((j % 2) << 15) | (((j % 120) + 1) << 7) | (j & 0x7F)
+    j = np.arange(2048)
+    many = 2 * 8192 + 4 * j                             # tile 2: 2048 escapes
+    b[many] = ((j % 3 == 0) << 15) | ((130 + j % 100) << 7) | ((j * 7) & 0x7F)
+    b[[n - 1, n - 2, 5 * 8192]] = [0x0001, 0xFF80, 0x8000]
+    x = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+    _, om = full_parity(x, cb_source=src, name="patch paths")
+    assert om.n_esc == 100 + 2048 + 3 and om.n_esc * 8192 <= 512 * n
+    # more than 512 per tile on average: every third element escapes
+    n = 4 * 8192 + 333
+    b = np.full(n, 0x3F80, np.uint16)
+    k = np.arange(0, n, 3)
+    b[k] = ((k & 1) << 15) | ((k % 126) << 7) | (k & 0x7F)
+    x = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+    _, om = full_parity(x, cb_source=src, name="tile in LDS")
+    assert om.n_esc == len(k) and om.n_esc * 8192 > 512 * n
+
+
 def test_determinism_and_workspace_reuse():
     big = W.log_uniform_stress(1 << 20, seed=14)
     small = W.gaussian_weight(5_001, seed=15)
