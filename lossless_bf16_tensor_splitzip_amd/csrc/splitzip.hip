@@ -447,8 +447,8 @@ __device__ inline void encode_unit(const u32x4 q, const uint8_t *lut, uint32_t &
         const uint32_t w = q[k];
         const uint32_t m_even = lut[exp_lo(w)];
         const uint32_t m_odd = lut[exp_hi(w)];
-        // marked code: 0..15, or 16 for an escape, whose nibble is 16 & 15 = 0;
-        // the even element takes the high nibble
+        // table entry: nibble | (escape << 4), at most 31 (normalised when the
+        // table is loaded); the even element takes the high nibble
         const uint32_t byte = ((m_even & 15u) << 4) | (m_odd & 15u);
         pk |= byte << (8 * k);
         flags |= ((m_even >> 4) | ((m_odd >> 4) << 1)) << (2 * k);
@@ -487,7 +487,14 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
             q[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(I.x + i0));
         }
     }
-    lut[tid] = I.cb->enc_lut_marked[tid];
+    {
+        // Page 1, encode_torch: an exponent escapes when its marked code is
+        // above 15, and its nibble is the marked code's low 4 bits, whatever
+        // byte the caller's table holds.  Stored as nibble | (escape << 4), so
+        // that m >> 4 is exactly one flag bit below.
+        const uint32_t v = I.cb->enc_lut_marked[tid];
+        lut[tid] = (uint8_t)((v & 15u) | (v > 15u ? 16u : 0u));
+    }
     __syncthreads();
 
     uint32_t flags[kEncUnits];

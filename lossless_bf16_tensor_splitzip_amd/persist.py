@@ -64,6 +64,10 @@ def codebook_from_json(d: dict) -> Codebook:
         raw = base64.b64decode(d[name])
         if len(raw) != sizes[name]:
             raise ValueError("%s must hold %d bytes, got %d" % (name, sizes[name], len(raw)))
+        if name == "enc_lut_marked" and max(raw) > 16:
+            # page 1, calibrate_codebook: a marked table holds codes 0..15
+            # and 16 for an escape; anything else is not such a table
+            raise ValueError("enc_lut_marked holds a value above 16")
         ctypes.memmove(ctypes.addressof(getattr(cb, name)), raw, len(raw))
     cb.n_codes = int(d["n_codes"]) if "n_codes" in d else sum(bytes(cb.common_lut))
     cb.covered = int(d.get("covered", 0))
@@ -173,7 +177,18 @@ def unpack(entry: dict, blob, out=None, stream=None):
     m = meta_from_json(entry["meta"])
     if m.n != n:
         raise ValueError("manifest shape and metadata disagree")
+    if out is not None and not out.is_contiguous():
+        # a reshape of a strided tensor would be a copy, and the decode would
+        # land there instead of in `out`
+        raise ValueError("out must be a contiguous tensor")
     flat = None if out is None else out.reshape(-1)
+    # The validating decode: metadata from storage may describe an escape
+    # stream this library did not write (any order, or damaged bytes).
+    status = torch.zeros(1, dtype=torch.int32, device=blob.device)
     res = codec.decode(blob, to_device(m, blob.device), to_device(cb, blob.device), n, out=flat,
-                       stream=stream)
+                       status=status, stream=stream)
+    bad = int(status.item())
+    if bad:
+        raise ValueError("stored payload of %s is corrupt (decode status %d)"
+                         % (entry.get("name", "?"), bad))
     return res.reshape(shape) if out is None else out

@@ -62,3 +62,27 @@ def test_pack_unpack(make, n, compressed):
     torch.cuda.synchronize()
     assert back.shape == (1, n)
     assert torch.equal(back.reshape(-1).view(torch.int16), x.view(torch.int16))
+
+
+def test_unpack_into_out_and_refusals():
+    n = 200_003
+    x = W.gaussian_weight(n, seed=92).reshape(-1).to(DEV)
+    ws = S.Workspace(n, DEV)
+    entry, blob = persist.pack("w", x.reshape(1, -1), ws)
+    # into a caller buffer: the same buffer comes back, filled
+    out = torch.empty(1, n, dtype=torch.bfloat16, device=DEV)
+    res = persist.unpack(entry, blob, out=out)
+    torch.cuda.synchronize()
+    assert res is out and torch.equal(out.reshape(-1).view(torch.int16), x.view(torch.int16))
+    # a strided output would be decoded into a copy: refused
+    wide = torch.empty(n, 2, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        persist.unpack(entry, blob, out=wide[:, :1].t())
+    # a damaged escape stream is reported, not silently decoded
+    e = entry["meta"]["n_esc"]
+    assert e > 0
+    bad = blob.clone()
+    off_cid = entry["meta"]["offsets"][2]
+    bad[off_cid: off_cid + 4] = torch.tensor([0xFF, 0xFF, 0xFF, 0x7F], dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        persist.unpack(entry, bad)

@@ -93,3 +93,18 @@ def test_manifest_entry_format():
     assert e["meta"]["comp_bytes"] == om.comp_bytes
     r = persist.manifest_entry("w", (3,), None, None)
     assert r["raw"] is True and "codebook" not in r
+
+
+def test_codebook_json_rejects_marked_values_above_16():
+    x = W.bits(W.gaussian_weight(5_001, seed=85)).numpy().view(np.uint16)
+    _, cb = oracle_codebook(x)
+    d = persist.codebook_to_json(cb)
+    raw = bytearray(base64.b64decode(d["enc_lut_marked"]))
+    raw[7] = 17
+    d["enc_lut_marked"] = base64.b64encode(bytes(raw)).decode()
+    try:
+        persist.codebook_from_json(d)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a marked table with 17 was accepted")
