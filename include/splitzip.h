@@ -136,9 +136,10 @@ const char *splitzip_status_string(int status);
 uint64_t splitzip_payload_size(uint64_t n, uint64_t n_esc);
 
 /* Bytes of device workspace needed by calibrate and encode for tensors of up
- * to n elements (host function): about 4n bytes plus a fixed ~1.2 MB, since
- * encode stages every escape of a tile (all of them, at worst) until their
- * final ranks are known.  A workspace of S bytes serves every n with
+ * to n elements (host function): about n/4 bytes plus a fixed ~1.2 MB.  Encode
+ * keeps one escape count per 8192-element tile and stages up to 512 escapes
+ * per tile until their final ranks are known; a tile with more has them
+ * derived from the input again.  A workspace of S bytes serves every n with
  * splitzip_workspace_size(n) <= S. */
 size_t splitzip_workspace_size(uint64_t n);
 

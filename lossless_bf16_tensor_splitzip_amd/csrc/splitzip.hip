@@ -27,16 +27,17 @@
 //                 runs the top-16 select.
 //   k_encode      one 8192-element tile per workgroup: 16-byte loads, code
 //                 table in LDS, nibble packing, sign/mantissa bytes, wave
-//                 ballots to rank the tile's escapes, which are staged in the
-//                 workspace with the tile's escape count.  Tiles never talk
-//                 to each other.
+//                 ballots to rank the tile's escapes; the escape count goes
+//                 to the workspace, and so do the escapes themselves when
+//                 there are at most 512.  Tiles never talk to each other.
 //   k_encode_sums (large launches only) escapes per block of tiles and per
 //                 256-tile superblock, so escape placement needs few loads.
-//   k_encode_tail every workgroup takes a block of 4-64 tiles, finds the rank
+//   k_encode_tail every workgroup takes a block of 1-64 tiles, finds the rank
 //                 of its first escape and the tensor's escape count, and
 //                 writes chunk id, chunk-local position and raw exponent of
-//                 each of its escapes at its final rank; the tensor's first
-//                 workgroup writes the padding and the metadata.
+//                 each of its escapes at its final rank (staged ones copied,
+//                 the others derived from the input again); the tensor's
+//                 first workgroup writes the padding and the metadata.
 //   k_decode      one 8192-element tile per workgroup:
 //                 pk + sm -> bf16 through a 256-entry pair table in LDS and
 //                 16-byte stores; meanwhile one wave finds the tile's escapes
@@ -66,7 +67,7 @@ namespace {
 #define SPLITZIP_ENC_UNITS 4        // encode: 8-element units per thread per tile
 #endif
 #ifndef SPLITZIP_TAIL_MIN_TILES
-#define SPLITZIP_TAIL_MIN_TILES 4   // escape placement: fewest tiles per workgroup
+#define SPLITZIP_TAIL_MIN_TILES 1   // escape placement: fewest tiles per workgroup
 #endif
 #ifndef SPLITZIP_TAIL_TARGET_WGS
 #define SPLITZIP_TAIL_TARGET_WGS 1024   // ... and the workgroup count it aims at
@@ -109,8 +110,10 @@ constexpr uint32_t kMaxChunk = 65536;         // chunk-local positions are uint1
 constexpr int kDecThreads = SPLITZIP_DEC_THREADS;
 constexpr int kDecUnits = SPLITZIP_DEC_UNITS;
 constexpr int kDecStaged = 512;               // decode: escapes per tile above which sm goes to LDS
-constexpr uint32_t kStageDirect = 256;        // encode: escapes per tile written directly
-constexpr uint32_t kStageLds = 2048;          // ... beyond that, ranks per LDS round
+// Encode: a tile stages at most kStageCap escapes in the workspace; the
+// placement kernel derives the escapes of a tile with more from the input
+// again (16 KB read instead of 8 bytes staged and read back per escape).
+constexpr uint32_t kStageCap = 512;
 
 // Workspace layout (bytes).  kMaxBatch calibrate slots, each with its
 // counters on separate cache lines and its histogram copies (all of which
@@ -126,7 +129,7 @@ constexpr size_t kWsSlack = 64;
 static_assert(kWsTiles % 256 == 0, "alignment");
 static_assert(kSuperTiles == kThreads && kTailMaxTiles <= 64 && kTailMaxTiles <= kTailThreads &&
                   kTailThreads % 64 == 0 && (kTailMinTiles & (kTailMinTiles - 1)) == 0 &&
-                  kTailMinTiles <= kTailMaxTiles,
+                  kTailMinTiles <= kTailMaxTiles && kSuperTiles / kTailMinTiles <= kTailThreads,
               "count sums: one tile per thread, whole tail blocks per superblock");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -158,11 +161,14 @@ struct WsPlan {
     uint64_t off_count;   // uint32[t_max] escapes per tile
     uint64_t off_bsum;    // uint32[t_max / kTailMinTiles + 64] escapes per tail workgroup
     uint64_t off_ssum;    // uint32[t_max / kSuperTiles + 64] escapes per kSuperTiles tiles
-    uint64_t off_stage;   // uint32[t_max * kEncTile] staged escapes
+    uint64_t off_stage;   // uint32[t_max * kStageCap] staged escapes
 };
 
-constexpr uint64_t kWsPerTile = 8 + 4 * (uint64_t)kEncTile;   // count, count sums, stage
+// per tile: its count, its share of the block and superblock sums, its stage
+constexpr uint64_t kWsPerTile =
+    4 + 4 / kTailMinTiles + 1 + 4 * (uint64_t)kStageCap;
 constexpr uint64_t kWsFixed = kWsTiles + kWsSlack + 4 * 128;
+static_assert(kTailMinTiles <= 4, "block sums fit the per-tile budget");
 
 __host__ inline WsPlan ws_plan(size_t ws_bytes) {
     WsPlan P{0, 0, 0, 0, 0};
@@ -433,7 +439,7 @@ struct EncArgs {
     uint32_t *blk_sum;                    // escapes per tail workgroup, or null
     uint32_t *sup_sum;                    // escapes per superblock, or null
     uint32_t tail_tiles;                  // tiles per tail workgroup (power of two)
-    uint32_t *stage;                      // per tile: (position << 8) | raw exponent
+    uint32_t *stage;                      // per tile, up to kStageCap: (position << 8) | raw exponent
 };
 
 // One 8-element unit: codes -> 4 pk bytes, sign/mantissa -> 8 sm bytes,
@@ -459,12 +465,73 @@ __device__ inline void encode_unit(const u32x4 q, const uint8_t *lut, uint32_t &
           (sm_of16(q[3] >> 16) << 24);
 }
 
-// Dense sections of one tile plus the tile's escapes, staged in element
-// order; no communication between tiles.
+// Marked-code table of a codebook in LDS (one entry per thread of the first
+// 256).  Page 1, encode_torch: an exponent escapes when its marked code is
+// above 15, and its nibble is the marked code's low 4 bits, whatever byte the
+// caller's table holds.  Stored as nibble | (escape << 4), so that m >> 4 is
+// exactly one flag bit.
+__device__ inline void load_marked_table(const splitzip_codebook *cb, uint8_t *lut) {
+    const int tid = threadIdx.x;
+    if (tid < 256) {
+        const uint32_t v = cb->enc_lut_marked[tid];
+        lut[tid] = (uint8_t)((v & 15u) | (v > 15u ? 16u : 0u));
+    }
+}
+
+// Escape mask of one 8-element unit (bit j: element j escapes).
+__device__ inline uint32_t unit_flags(const u32x4 q, const uint8_t *lut) {
+    uint32_t f = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        f |= ((uint32_t)(lut[exp_lo(q[k])] >> 4) | ((uint32_t)(lut[exp_hi(q[k])] >> 4) << 1)) << (2 * k);
+    return f;
+}
+
+// Ranks of a tile's escapes in element order (unit, thread, element of the
+// unit), from every thread's per-unit escape masks: first[u] is the rank of
+// this thread's first escape in unit u; returns the tile's escape count.
+// One workgroup barrier (after the per-wave totals are in `wtot`); the caller
+// orders a later reuse of `wtot` behind another barrier.
+__device__ inline uint32_t tile_ranks(const uint32_t *flags, uint32_t (*wtot)[4], uint32_t *first) {
+    static_assert(kThreads == 256 && kTailThreads == 256, "four waves per tile workgroup");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t pre[kEncUnits];
+#pragma unroll
+    for (int u = 0; u < kEncUnits; ++u) {
+        const uint32_t c = __builtin_popcount(flags[u]);   // 0..8: four bits
+        const uint64_t any = __ballot(c != 0);
+        uint32_t p = 0, tot = 0;
+        if (any) {
+#pragma unroll
+            for (int bit = 0; bit < 4; ++bit) {
+                const uint64_t m = __ballot((c >> bit) & 1u);
+                p += lanes_below(m) << bit;
+                tot += (uint32_t)__popcll(m) << bit;
+            }
+        }
+        pre[u] = p;
+        if (lane == 0) wtot[u][wave] = tot;
+    }
+    __syncthreads();
+    uint32_t total = 0;
+#pragma unroll
+    for (int u = 0; u < kEncUnits; ++u) {
+        uint32_t b = total;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            b += (w < wave) ? wtot[u][w] : 0u;
+            total += wtot[u][w];
+        }
+        first[u] = b + pre[u];
+    }
+    return total;
+}
+
+// Dense sections of one tile, its escape count, and (up to kStageCap) its
+// escapes staged in element order; no communication between tiles.
 __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
     __shared__ uint8_t lut[256];
     __shared__ uint32_t wtot[kEncUnits][4];
-    __shared__ uint32_t stg[kStageLds];       // staged escapes of a dense tile
 
     const uint64_t gt = blockIdx.x;
     const uint32_t item = find_item(a.tile_start, a.count, gt);
@@ -474,8 +541,6 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
     const Layout L0 = layout_of(I.n, 0);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
     const uint64_t base = t * kEncTile;
     const bool full = base + kEncTile <= I.n;
 
@@ -487,14 +552,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
             q[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(I.x + i0));
         }
     }
-    {
-        // Page 1, encode_torch: an exponent escapes when its marked code is
-        // above 15, and its nibble is the marked code's low 4 bits, whatever
-        // byte the caller's table holds.  Stored as nibble | (escape << 4), so
-        // that m >> 4 is exactly one flag bit below.
-        const uint32_t v = I.cb->enc_lut_marked[tid];
-        lut[tid] = (uint8_t)((v & 15u) | (v > 15u ? 16u : 0u));
-    }
+    load_marked_table(I.cb, lut);
     __syncthreads();
 
     uint32_t flags[kEncUnits];
@@ -550,79 +608,23 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
         for (uint64_t b = L0.off_sm + I.n; b < L0.off_cid; ++b) I.payload[b] = 0;
     }
 
-    // Escape ranks inside the tile, in element order (unit, thread, j).
-    uint32_t pre[kEncUnits];
-#pragma unroll
-    for (int u = 0; u < kEncUnits; ++u) {
-        const uint32_t c = __builtin_popcount(flags[u]);
-        const uint64_t any = __ballot(c != 0);
-        uint32_t p = 0, tot = 0;
-        if (any) {
-#pragma unroll
-            for (int bit = 0; bit < 4; ++bit) {
-                const uint64_t m = __ballot((c >> bit) & 1u);
-                p += lanes_below(m) << bit;
-                tot += (uint32_t)__popcll(m) << bit;
-            }
-        }
-        pre[u] = p;
-        if (lane == 0) wtot[u][wave] = tot;
-    }
-    __syncthreads();
-
-    uint32_t tile_total = 0;
-    uint32_t ubase[kEncUnits];
-#pragma unroll
-    for (int u = 0; u < kEncUnits; ++u) {
-        ubase[u] = tile_total;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            ubase[u] += (w < wave) ? wtot[u][w] : 0u;
-            tile_total += wtot[u][w];
-        }
-    }
+    uint32_t first[kEncUnits];
+    const uint32_t tile_total = tile_ranks(flags, wtot, first);
     if (tid == 0) a.tile_count[gt] = tile_total;
-    uint32_t *stage = a.stage + gt * kEncTile;
-    if (tile_total <= kStageDirect) {
-        // few escapes: every thread writes its own at their ranks
+    if (tile_total > kStageCap) return;   // placement derives them from the input again
+    // every thread writes its own escapes at their ranks
+    uint32_t *stage = a.stage + gt * kStageCap;
 #pragma unroll
-        for (int u = 0; u < kEncUnits; ++u) {
-            uint32_t f = flags[u];
-            uint32_t r = ubase[u] + pre[u];
-            const uint32_t l0 = (uint32_t)u * (kThreads * kUnit) + tid * kUnit;
-            while (f) {
-                const int j = __builtin_ctz(f);
-                f &= f - 1;
-                const uint32_t w = word_of(q[u], j >> 1);
-                const uint32_t ex = (j & 1) ? exp_hi(w) : exp_lo(w);
-                stage[r++] = ((l0 + j) << 8) | ex;
-            }
-        }
-    } else {
-        // many: ranks [lo, lo + kStageLds) at a time through LDS, so the
-        // staging stores are contiguous across the workgroup
-        for (uint32_t lo = 0; lo < tile_total; lo += kStageLds) {
-            const uint32_t hi = lo + kStageLds < tile_total ? lo + kStageLds : tile_total;
-#pragma unroll
-            for (int u = 0; u < kEncUnits; ++u) {
-                uint32_t f = flags[u];
-                uint32_t r = ubase[u] + pre[u];
-                if (r >= hi || r + __builtin_popcount(f) <= lo) continue;
-                const uint32_t l0 = (uint32_t)u * (kThreads * kUnit) + tid * kUnit;
-                while (f) {
-                    const int j = __builtin_ctz(f);
-                    f &= f - 1;
-                    if (r >= lo && r < hi) {
-                        const uint32_t w = word_of(q[u], j >> 1);
-                        const uint32_t ex = (j & 1) ? exp_hi(w) : exp_lo(w);
-                        stg[r - lo] = ((l0 + j) << 8) | ex;
-                    }
-                    ++r;
-                }
-            }
-            __syncthreads();
-            for (uint32_t k = tid; k < hi - lo; k += kThreads) stage[lo + k] = stg[k];
-            __syncthreads();
+    for (int u = 0; u < kEncUnits; ++u) {
+        uint32_t f = flags[u];
+        uint32_t r = first[u];
+        const uint32_t l0 = (uint32_t)u * (kThreads * kUnit) + tid * kUnit;
+        while (f) {
+            const int j = __builtin_ctz(f);
+            f &= f - 1;
+            const uint32_t w = word_of(q[u], j >> 1);
+            const uint32_t ex = (j & 1) ? exp_hi(w) : exp_lo(w);
+            stage[r++] = ((l0 + j) << 8) | ex;
         }
     }
 }
@@ -712,16 +714,149 @@ __device__ inline void place_escape(const EncItem &I, const Layout &L, bool fits
     }
 }
 
+// One 8-element unit of bf16 bits at element i0 (zeros past n): a 16-byte
+// load when the whole tile is in range, else element by element.
+__device__ inline u32x4 load_unit(const uint16_t *x, uint64_t n, uint64_t i0, bool full) {
+    if (full) return *reinterpret_cast<const u32x4 *>(x + i0);
+    // last tile only: one element at a time keeps the register count down
+    uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+#pragma unroll 1
+    for (int j = 0; j < kUnit; ++j) {
+        const uint32_t v = (i0 + j < n ? (uint32_t)x[i0 + j] : 0u) << (16 * (j & 1));
+        const int k = j >> 1;
+        w0 |= k == 0 ? v : 0u;
+        w1 |= k == 1 ? v : 0u;
+        w2 |= k == 2 ? v : 0u;
+        w3 |= k == 3 ? v : 0u;
+    }
+    return u32x4{w0, w1, w2, w3};
+}
+
+// The kEncUnits units of this thread in the tile at element tb.
+__device__ inline void load_tile(const EncItem &I, uint64_t tb, u32x4 *qt) {
+    const bool full = tb + kEncTile <= I.n;
+#pragma unroll
+    for (int u = 0; u < kEncUnits; ++u)
+        qt[u] = load_unit(I.x, I.n, tb + (uint64_t)u * (kThreads * kUnit) + threadIdx.x * kUnit, full);
+}
+
+// Escapes of one encode tile whose count exceeded the staging cap, derived
+// from the input again (its values qt, loaded by the caller; the same table
+// and the same ranks as k_encode) and written at ranks rank0 + r.  Every
+// thread puts the position in tile and the raw exponent of each of its
+// escapes into LDS by rank, shifted so that 16-byte blocks of LDS line up
+// with 16-byte blocks of the position and exponent sections; the workgroup
+// then writes the three sections 16 bytes per lane (4 chunk ids, 8
+// positions, 16 exponents), the few ranks outside whole blocks one by one.
+__device__ void rederive_tile(const EncItem &I, const Layout &L, bool fits, const uint8_t *lut,
+                              uint32_t (*wtot)[4], uint16_t *rpos, uint8_t *rex, uint64_t tb,
+                              uint64_t rank0, const u32x4 *qt) {
+    const uint32_t tid = threadIdx.x;
+    uint32_t flags[kEncUnits];
+#pragma unroll
+    for (int u = 0; u < kEncUnits; ++u) {
+        const uint64_t i0 = tb + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+        const uint32_t valid = i0 + kUnit <= I.n ? 0xFFu : (i0 < I.n ? (1u << (I.n - i0)) - 1u : 0u);
+        flags[u] = unit_flags(qt[u], lut) & valid;
+        // one unit's table reads at a time: hoisting all of them costs occupancy
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    uint32_t first[kEncUnits];
+    const uint32_t total = tile_ranks(flags, wtot, first);
+    // byte addresses of rank 0 in the three sections and their offsets in a
+    // 16-byte block (positions: in units of 2 bytes)
+    uint8_t *dc = I.payload + L.off_cid + 4 * rank0;
+    uint8_t *dl = I.payload + L.off_lpos + 2 * rank0;
+    uint8_t *de = I.payload + L.off_ev + rank0;
+    const uint32_t al = (uint32_t)((uintptr_t)dl & 15u) >> 1;
+    const uint32_t ae = (uint32_t)((uintptr_t)de & 15u);
+#pragma unroll
+    for (int u = 0; u < kEncUnits; ++u) {
+        uint32_t f = flags[u];
+        uint32_t r = first[u];
+        const uint32_t l0 = (uint32_t)u * (kThreads * kUnit) + tid * kUnit;
+        while (f) {
+            const int j = __builtin_ctz(f);
+            f &= f - 1;
+            const uint32_t w = word_of(qt[u], j >> 1);
+            rpos[al + r] = (uint16_t)(l0 + j);
+            rex[ae + r] = (uint8_t)((j & 1) ? exp_hi(w) : exp_lo(w));
+            ++r;
+        }
+    }
+    __syncthreads();
+    // Chunk ids in 32-bit arithmetic when the chunk size is a power of two
+    // that divides the tile (then the tile starts a chunk).
+    const uint32_t chunk = I.chunk;
+    const bool pow2 = (chunk & (chunk - 1)) == 0 && chunk <= (uint32_t)kEncTile;
+    if (fits && pow2) {
+        const int sh = __builtin_ctz(chunk);
+        const uint32_t cbase = (uint32_t)(tb >> sh), msk = chunk - 1u;
+        const uint32_t nth = kTailThreads;
+        {   // chunk ids: 4 ranks per 16-byte block
+            uint32_t *d32 = reinterpret_cast<uint32_t *>(dc);
+            uint32_t h = ((16u - (uint32_t)((uintptr_t)dc & 15u)) & 15u) >> 2;
+            h = h < total ? h : total;
+            const uint32_t nb = (total - h) >> 2;
+            u32x4 *dv = reinterpret_cast<u32x4 *>(d32 + h);
+            for (uint32_t c = tid; c < nb; c += nth) {
+                const uint16_t *p = rpos + al + h + 4 * c;
+                dv[c] = u32x4{cbase + ((uint32_t)p[0] >> sh), cbase + ((uint32_t)p[1] >> sh),
+                              cbase + ((uint32_t)p[2] >> sh), cbase + ((uint32_t)p[3] >> sh)};
+            }
+            // fewer than 4 ranks before the blocks and after them
+            const uint32_t k = tid < h ? tid : h + 4 * nb + (tid - h);
+            if (tid < h + 4 && k < total) d32[k] = cbase + ((uint32_t)rpos[al + k] >> sh);
+        }
+        {   // positions: 8 ranks per block, LDS blocks aligned with them
+            uint16_t *d16 = reinterpret_cast<uint16_t *>(dl);
+            uint32_t h = (8u - al) & 7u;
+            h = h < total ? h : total;
+            const uint32_t nb = (total - h) >> 3;
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(rpos + al + h);
+            u32x4 *dv = reinterpret_cast<u32x4 *>(d16 + h);
+            const uint32_t m2 = msk | (msk << 16);
+            for (uint32_t c = tid; c < nb; c += nth) {
+                const u32x4 v = src[c];
+                dv[c] = u32x4{v.x & m2, v.y & m2, v.z & m2, v.w & m2};
+            }
+            const uint32_t k = tid < h ? tid : h + 8 * nb + (tid - h);
+            if (tid < h + 8 && k < total) d16[k] = (uint16_t)((uint32_t)rpos[al + k] & msk);
+        }
+        {   // raw exponents: 16 ranks per block, LDS blocks aligned with them
+            uint32_t h = (16u - ae) & 15u;
+            h = h < total ? h : total;
+            const uint32_t nb = (total - h) >> 4;
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(rex + ae + h);
+            u32x4 *dv = reinterpret_cast<u32x4 *>(de + h);
+            for (uint32_t c = tid; c < nb; c += nth) dv[c] = src[c];
+            const uint32_t k = tid < h ? tid : h + 16 * nb + (tid - h);
+            if (tid < h + 16 && k < total) de[k] = rex[ae + k];
+        }
+    } else {
+#pragma unroll 1
+        for (uint32_t k = tid; k < total; k += kTailThreads)
+            place_escape(I, L, fits, tb, ((uint32_t)rpos[al + k] << 8) | rex[ae + k], rank0 + k);
+    }
+    __syncthreads();   // before the next tile reuses rpos and rex
+}
+
 // Escape placement: every workgroup takes tail_tiles tiles of one tensor,
 // finds the rank of its first escape and the tensor's escape count (from the
 // tile counts, or for large tensors from the superblock and block sums),
-// then copies each tile's staged escapes to their final ranks as chunk id,
-// chunk-local position and raw exponent.  The tensor's first tail workgroup
-// writes the padding and the metadata.
+// then writes each tile's escapes at their final ranks as chunk id,
+// chunk-local position and raw exponent: copied from the staging area, or
+// for a tile above the staging cap derived from the input again.  The
+// tensor's first tail workgroup writes the padding and the metadata.
 __global__ __launch_bounds__(kTailThreads) void k_encode_tail(EncArgs a) {
     __shared__ uint64_t red[2][kTailThreads / 64];
     __shared__ uint32_t waves[kTailThreads / 64];
     __shared__ uint32_t scan[kTailMaxTiles + 1];
+    __shared__ uint8_t lut[256];
+    __shared__ uint32_t wtot[kEncUnits][4];
+    // a re-derived tile's escapes by rank: position in tile, raw exponent
+    __shared__ __attribute__((aligned(16))) uint16_t rpos[kEncTile + 8];
+    __shared__ __attribute__((aligned(16))) uint8_t rex[kEncTile + 16];
     const uint32_t item = find_item(a.blk_start, a.count, blockIdx.x);
     const EncItem I = a.it[item];
     const uint32_t blk = blockIdx.x - a.blk_start[item];
@@ -759,7 +894,8 @@ __global__ __launch_bounds__(kTailThreads) void k_encode_tail(EncArgs a) {
     const uint32_t incl = block_scan_incl(mine_c, waves);
     if ((uint32_t)tid < tt) scan[tid + 1] = incl;
     if (tid == 0) scan[0] = 0;
-    __syncthreads();
+    // a tile above the staging cap has to be derived from the input again
+    const bool rederive = __syncthreads_or(mine_c > kStageCap) != 0;
     uint64_t P = 0, e = 0;
 #pragma unroll
     for (int w = 0; w < kTailThreads / 64; ++w) {
@@ -771,7 +907,7 @@ __global__ __launch_bounds__(kTailThreads) void k_encode_tail(EncArgs a) {
 
     const uint32_t nt = (uint32_t)(t1 - t0);
     const uint32_t total = scan[nt];
-    if (total <= 8 * kTailThreads) {
+    if (!rederive && total <= 8 * kTailThreads) {
         // few escapes: one pass over all of them, the tile of escape k found
         // in the block's scan, 8 staged loads in flight
         uint32_t w8[8], j8[8];
@@ -786,7 +922,7 @@ __global__ __launch_bounds__(kTailThreads) void k_encode_tail(EncArgs a) {
                     const uint32_t mid = (lo + hi) >> 1;
                     if (scan[mid] <= k) lo = mid; else hi = mid;
                 }
-                w8[q] = a.stage[(tfirst + t0 + lo) * kEncTile + (k - scan[lo])];
+                w8[q] = a.stage[(tfirst + t0 + lo) * kStageCap + (k - scan[lo])];
             }
             j8[q] = lo;
         }
@@ -797,11 +933,32 @@ __global__ __launch_bounds__(kTailThreads) void k_encode_tail(EncArgs a) {
             place_escape(I, L, fits, (t0 + j8[q]) * kEncTile, w8[q], P + k);
         }
     } else {
-        // many: tile by tile, every thread takes every kTailThreads-th escape
-        // of the tile, 8 staged loads in flight
+        // first tile above the cap (nt when none); the values of the next
+        // one are loaded while a tile is worked on
+        uint32_t jd = 0;
+        while (jd < nt && scan[jd + 1] - scan[jd] <= kStageCap) ++jd;
+        u32x4 qt[kEncUnits];
+        if (rederive) {
+            load_tile(I, (t0 + jd) * kEncTile, qt);
+            load_marked_table(I.cb, lut);
+            __syncthreads();
+        }
+        // tile by tile: staged escapes with every kTailThreads-th one per
+        // thread, 8 staged loads in flight; tiles above the cap re-derived
         for (uint32_t j = 0; j < nt; ++j) {
             const uint32_t k_first = scan[j], c = scan[j + 1] - k_first;
-            const uint32_t *st = a.stage + (tfirst + t0 + j) * kEncTile;
+            const uint64_t tb = (t0 + j) * kEncTile;
+            if (c > kStageCap) {
+                uint32_t jn = j + 1;
+                while (jn < nt && scan[jn + 1] - scan[jn] <= kStageCap) ++jn;
+                u32x4 qn[kEncUnits];
+                if (jn < nt) load_tile(I, (t0 + jn) * kEncTile, qn);
+                rederive_tile(I, L, fits, lut, wtot, rpos, rex, tb, P + k_first, qt);
+#pragma unroll
+                for (int u = 0; u < kEncUnits; ++u) qt[u] = qn[u];
+                continue;
+            }
+            const uint32_t *st = a.stage + (tfirst + t0 + j) * kStageCap;
             for (uint32_t k0 = 0; k0 < c; k0 += 8 * kTailThreads) {
                 uint32_t w8[8];
 #pragma unroll
@@ -813,7 +970,7 @@ __global__ __launch_bounds__(kTailThreads) void k_encode_tail(EncArgs a) {
                 for (int q = 0; q < 8; ++q) {
                     const uint32_t k = k0 + q * kTailThreads + tid;
                     if (k >= c) break;
-                    place_escape(I, L, fits, (t0 + j) * kEncTile, w8[q], P + k_first + k);
+                    place_escape(I, L, fits, tb, w8[q], P + k_first + k);
                 }
             }
         }

@@ -202,6 +202,33 @@ def test_escapes_at_chunk_and_tile_edges():
     assert om.n_esc == len(edges)
 
 
+@pytest.mark.parametrize("counts", [
+    # escapes per 8192-element encode tile around the staging cap of 512
+    [0, 1, 511, 512, 513, 2048, 8191, 8192, 700],
+    [513, 0, 0, 0, 5, 512, 0, 8192, 1],
+    [8192] * 5 + [3000],
+])
+def test_staging_cap_edges(counts):
+    """Tiles whose escapes are staged (at most 512) and tiles whose escapes
+    the placement derives from the input again (more than 512), mixed in one
+    placement block and across blocks; the last tile is partial."""
+    src = torch.ones(8, dtype=torch.bfloat16)          # codes exponent 127 only
+    tail = 4321
+    n = (len(counts) - 1) * 8192 + tail
+    rng = np.random.default_rng(sum(counts))
+    b = np.full(n, 0x3F80, np.uint16)
+    for t, c in enumerate(counts):
+        size = 8192 if t < len(counts) - 1 else tail
+        c = min(c, size)
+        pos = t * 8192 + rng.choice(size, c, replace=False)
+        b[pos] = (rng.integers(0, 2, c) << 15) | (rng.integers(128, 256, c) << 7) | \
+            rng.integers(0, 128, c)
+    x = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+    g, om = full_parity(x, cb_source=src, name="staging-cap")
+    assert om.n_esc == sum(min(c, 8192 if t < len(counts) - 1 else tail)
+                           for t, c in enumerate(counts))
+
+
 def test_decode_patch_paths():
     """Each way the decode applies escapes, byte for byte: scattered from
     registers (a tile with few), through the tile's sign/mantissa bytes staged
@@ -241,13 +268,20 @@ def test_determinism_and_workspace_reuse():
     assert runs[1]["payload"] == opay
 
 
-def test_capacity_overflow():
-    x = W.log_uniform_stress(20_001, seed=16).to(DEV)
-    ws = workspace(20_001)
+@pytest.mark.parametrize("make,extra", [
+    (W.log_uniform_stress, 0),      # escape-dense tiles: derived again by the placement
+    (W.log_uniform_stress, 2),      # capacity not a whole number of chunk ids
+    (W.log_uniform_stress, 3),
+    (W.gaussian_weight, 0),         # few escapes: staged ones placed by the tail
+])
+def test_capacity_overflow(make, extra):
+    n = 20_001 if make is W.log_uniform_stress else 600_001
+    x = make(n, seed=16).to(DEV)
+    ws = workspace(n)
     cb = S.calibrate(x, ws)
     xs = host_bits(x)
-    _, om = oracle.encode(xs, oracle.calibrate(xs))
-    cap = om.offsets[2] + 4 * (om.n_esc // 2)   # room for half of the chunk ids only
+    opay, om = oracle.encode(xs, oracle.calibrate(xs))
+    cap = om.offsets[2] + 4 * (om.n_esc // 2) + extra   # room for half of the chunk ids
     guard = 64
     buf = torch.full((cap + guard,), 0xA5, dtype=torch.uint8, device=DEV)
     meta = torch.zeros(S.codec.META_BYTES, dtype=torch.uint8, device=DEV)
@@ -258,7 +292,12 @@ def test_capacity_overflow():
     torch.cuda.synchronize()
     m = S.read_meta(meta)
     assert m.status == _abi.ERR_CAPACITY and m.comp_bytes == om.comp_bytes
-    assert bool((buf[cap:] == 0xA5).all())          # nothing written past capacity
+    host = buf.cpu().numpy()
+    assert bool((host[cap:] == 0xA5).all())          # nothing written past capacity
+    # the dense sections and every chunk id that fits whole are the oracle's
+    whole = om.offsets[2] + 4 * ((cap - om.offsets[2]) // 4)
+    assert host[:whole].tobytes() == opay[:whole]
+    assert bool((host[whole:cap] == 0xA5).all())
     # synchronous check: below the dense size
     rc = _abi.splitzip_encode(x.view(torch.int16).data_ptr(), x.numel(), cb.data_ptr(),
                               buf.data_ptr(), om.offsets[2] - 1, meta.data_ptr(), ws.ptr(),
