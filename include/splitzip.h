@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SPLITZIP_ABI_VERSION 1
+#define SPLITZIP_ABI_VERSION 2
 #define SPLITZIP_CHUNK 1024u
 #define SPLITZIP_MAX_N (1ull << 36)
 
@@ -89,8 +89,15 @@ typedef struct splitzip_meta {
     uint64_t covered;    /* copied from the codebook used                     */
     uint64_t total;
     int32_t status;      /* SPLITZIP_OK or SPLITZIP_ERR_CAPACITY / _INTERNAL  */
-    uint32_t reserved;
+    uint32_t flags;      /* SPLITZIP_META_* bits                              */
 } splitzip_meta;
+
+/* splitzip_meta.flags: the escape stream is in strictly ascending element
+ * order.  splitzip_encode sets it (its escapes always are); metadata from
+ * elsewhere (page 1, PayloadMeta: no such field) leaves it clear, and then
+ * every decode applies the escapes in an order-independent pass of its own,
+ * as page 1, decode_torch does. */
+#define SPLITZIP_META_ASCENDING 1u
 
 /* One tensor of a batched call.  The array of items lives in host memory;
  * the pointers in it are device pointers.  Each batched call reads only the
@@ -193,7 +200,10 @@ int splitzip_encode_chunked(const uint16_t *d_x, uint64_t n, const splitzip_code
                             splitzip_meta *d_meta, void *d_ws, size_t ws_bytes, void *stream);
 
 /* Decode a payload back to BF16 bit patterns (page 1, decode_torch): dense
- * 16-entry table lookup plus the escape patch.
+ * 16-entry table lookup plus the escape patch.  Escapes are applied in any
+ * order: a stream marked SPLITZIP_META_ASCENDING (every payload of
+ * splitzip_encode) is patched tile by tile in the dense pass; any other
+ * stream by a second pass that applies each escape at its index.
  *   d_payload  payload laid out as d_meta describes (device, 16-byte aligned),
  *              payload_bytes readable bytes; a buffer shorter than the dense
  *              sections of n elements (splitzip_payload_size(n, 0)) is an
@@ -239,8 +249,10 @@ int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const spli
  *               there first (about three quarters of the payload)
  *   d_status    optional, as for splitzip_decode (escapes are re-applied from
  *               the decoded sign and mantissa)
- * Two kernels (three with d_status) on `stream`; calls that share a stash
- * must be ordered on one stream.
+ * Three kernels on `stream` (stash and direct decode, stashed tiles, then the
+ * order-independent escape pass, which does nothing for a stream marked
+ * SPLITZIP_META_ASCENDING without d_status); calls that share a stash must be
+ * ordered on one stream.
  * Synchronous errors: INVALID (also for overlapping slot and stash), HIP. */
 int splitzip_decode_slot(uint8_t *d_slot, uint64_t slot_bytes, const splitzip_meta *d_meta,
                          const uint8_t *d_dec_lut, uint64_t n, uint8_t *d_stash,

@@ -23,6 +23,9 @@ ERR_HIP = 4
 ERR_WORKSPACE = 5
 ERR_INTERNAL = 6
 
+# splitzip_meta.flags
+META_ASCENDING = 1
+
 # decode status bits
 DEC_BAD_META = 1
 DEC_ESC_OUT_OF_RANGE = 2
@@ -57,7 +60,7 @@ class Meta(ctypes.Structure):
         ("covered", ctypes.c_uint64),
         ("total", ctypes.c_uint64),
         ("status", ctypes.c_int32),
-        ("reserved", ctypes.c_uint32),
+        ("flags", ctypes.c_uint32),
     ]
 
 

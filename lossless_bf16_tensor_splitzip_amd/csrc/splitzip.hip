@@ -42,10 +42,11 @@
 //                 pk + sm -> bf16 through a 256-entry pair table in LDS and
 //                 16-byte stores; meanwhile one wave finds the tile's escapes
 //                 by a search of the sorted chunk ids, and after a workgroup
-//                 barrier they are patched over the dense output.
-//   k_decode_check  (only when a status word is requested) validates every
-//                 escape and re-applies it by scatter, which also makes the
-//                 decode correct for escape streams that are not sorted.
+//                 barrier they are patched over the dense output (only for
+//                 streams the metadata marks ascending).
+//   k_decode_check  after every decode: applies the escapes of streams not
+//                 marked ascending by scatter, in any order; with a status
+//                 word it validates every escape and re-applies it.
 //   k_decode_slot_stage / k_decode_slot_finish  in-place decode of payloads
 //                 that sit at the head of their own output buffers: the first
 //                 pass stashes the inputs of the tiles whose output overlaps
@@ -992,7 +993,7 @@ __global__ __launch_bounds__(kTailThreads) void k_encode_tail(EncArgs a) {
         m->covered = I.cb->covered;
         m->total = I.cb->total;
         m->status = fits ? SPLITZIP_OK : SPLITZIP_ERR_CAPACITY;
-        m->reserved = 0;
+        m->flags = SPLITZIP_META_ASCENDING;   // ranks follow element order
     }
 }
 
@@ -1020,7 +1021,33 @@ struct DecArgs {
     uint64_t tile_start[kMaxBatch + 1];   // first decode tile of each tensor
     DecItem it[kMaxBatch];
     int32_t *status;
+    uint64_t *order_sync;                 // this device's arrival counters (below)
+    uint64_t order_ticket;                // this call's first counter, and its tag
 };
+
+// Arrival counters of the order-independent escape pass (streams not marked
+// ascending): tensor k of a call uses counter (ticket + k) mod kOrderSlots,
+// tagged (ticket + k + 1) in its high half, so a counter needs no clearing
+// between calls and a stale or foreign value is simply replaced.  Library
+// state on every device that runs a decode, kept until the process ends;
+// calls that run at the same time use different counters unless 65,536
+// tensors' decodes are issued while one of them waits to run.
+constexpr uint32_t kOrderSlots = 65536;
+__device__ __align__(256) uint64_t g_order_sync[kOrderSlots];
+
+// Epoch-tagged arrival on a 64-bit counter (tag << 32 | arrivals): the first
+// arrival of a call replaces a value with another tag by (tag << 32); later
+// arrivals see the tag and only add.  Returns the arrivals before this one.
+__device__ inline uint32_t tagged_arrive(uint64_t *c, uint32_t tag) {
+    uint64_t cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // a failed exchange leaves the current value in cur: normally another
+    // arrival's claim, so the loop ends; bounded regardless
+    for (int k = 0; k < 64 && (uint32_t)(cur >> 32) != tag; ++k)
+        if (__hip_atomic_compare_exchange_strong(c, &cur, (uint64_t)tag << 32, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            break;
+    return (uint32_t)__hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Metadata must describe exactly the layout of (n, n_esc) and fit the buffer.
 __device__ inline bool meta_ok(const DecItem &I, Layout &L) {
@@ -1092,11 +1119,47 @@ __device__ inline uint64_t lower_bound_wave(const int32_t *cid, uint64_t lo, uin
     return lo + __popcll(__ballot(v < key));
 }
 
+// Order-independent escape pass (page 1, decode_torch applies the escapes
+// by index, in any order) for a tensor whose stream is not marked ascending:
+// every workgroup of the tensor releases its dense stores and arrives; the
+// last to arrive applies all escapes.  The sign and mantissa come from the
+// payload, or after an in-place decode from the decoded value.
+template <bool kFromOut>
+__device__ void order_pass(const DecArgs &a, const DecItem &I, uint32_t item, const Layout &L,
+                           uint32_t *last) {
+    __threadfence();   // this wave's dense stores before the arrival
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint64_t t = a.order_ticket + item;
+        const uint64_t ntiles = a.tile_start[item + 1] - a.tile_start[item];
+        const uint32_t prev = tagged_arrive(a.order_sync + (t & (kOrderSlots - 1)), (uint32_t)t + 1u);
+        *last = (uint64_t)prev + 1 == ntiles;
+    }
+    __syncthreads();
+    if (!*last) return;
+    __threadfence();   // every other workgroup's dense stores before the patches
+    const uint64_t e = I.meta->n_esc;
+    const uint64_t chunk = I.meta->chunk_size;
+    const uint8_t *sm = I.payload + L.off_sm;
+    const int32_t *cid = reinterpret_cast<const int32_t *>(I.payload + L.off_cid);
+    const uint16_t *lpos = reinterpret_cast<const uint16_t *>(I.payload + L.off_lpos);
+    const uint8_t *ev = I.payload + L.off_ev;
+    for (uint64_t r = threadIdx.x; r < e; r += blockDim.x) {
+        const int32_t c = cid[r];
+        if (c < 0) continue;
+        const uint64_t idx = (uint64_t)c * chunk + lpos[r];
+        if (idx >= I.n) continue;
+        const uint32_t keep = kFromOut ? sm_of16(I.out[idx]) : sm[idx];
+        I.out[idx] = (uint16_t)join16(keep, ev[r]);
+    }
+}
+
 template <int kTh, int kUnits, int kMode>
 __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     constexpr int kDecTile = kTh * kUnit * kUnits;
     __shared__ uint32_t pair_lut[256];      // pk byte -> (even exponent, odd exponent << 16)
     __shared__ uint64_t range[2];
+    __shared__ uint32_t last_arrival;
     // Output tile of a tensor with dense escapes, or the sm bytes of a tile
     // with many escapes in an otherwise sparse tensor.
     __shared__ uint32_t tile_buf[kDecTile / 2];
@@ -1166,7 +1229,11 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
                 return;
             }
         } else {
-            if (tile >= t_split) return;   // decoded by the first pass
+            if (tile >= t_split) {   // decoded by the first pass
+                if (I.meta->n_esc && !(I.meta->flags & SPLITZIP_META_ASCENDING))
+                    order_pass<true>(a, I, item, L, &last_arrival);
+                return;
+            }
             if (full && !early) {
 #pragma unroll
                 for (int u = 0; u < kUnits; ++u) {
@@ -1188,7 +1255,11 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     // by tile in LDS (dense values, the patch, then one coalesced store):
     // scattering thousands of 2-byte stores per tile to memory costs more
     // than writing the tile twice.
-    const bool in_lds = full && e * (uint64_t)kDecTile > 512 * I.n;
+    // An escape stream not known to be ascending cannot be searched per
+    // tile: after the dense part the last workgroup of the tensor applies
+    // every escape.
+    const bool ascending = (I.meta->flags & SPLITZIP_META_ASCENDING) != 0;
+    const bool in_lds = ascending && full && e * (uint64_t)kDecTile > 512 * I.n;
     __syncthreads();
 
     // Dense part first: every element through the pair table, 16-byte stores.
@@ -1216,6 +1287,10 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
         }
     }
     if (e == 0) return;
+    if (!ascending) {
+        if (kMode != kSlotStage) order_pass<kMode == kSlotFinish>(a, I, item, L, &last_arrival);
+        return;
+    }
 
     // Escape patch: the tile's escapes are among those with chunk ids in
     // [c0, c1) of the sorted stream (exactly those when tiles and chunks
@@ -1334,9 +1409,10 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_slot_finish(DecArgs a) {
     decode_tile<kDecThreads, kDecUnits, kSlotFinish>(a);
 }
 
-// Validation (and order-independent re-application) of every escape.  The
-// sign and mantissa come from the payload, or, after a slot decode (whose
-// stash holds only part of the sm section), from the decoded output itself.
+// Validation (and order-independent re-application) of every escape, only
+// when a status word is requested.  The sign and mantissa come from the
+// payload, or, after a slot decode (whose stash holds only part of the sm
+// section), from the decoded output itself.
 template <bool kFromOut>
 __global__ __launch_bounds__(kThreads) void k_decode_check(DecArgs a) {
     const uint64_t gs = (uint64_t)gridDim.x * kThreads;
@@ -1402,6 +1478,26 @@ bool cu_count(int &cus) {
 }
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// The current device's address of g_order_sync (each device holds its own
+// copy), cached per device, and the next decode call's first counter.
+std::atomic<uint64_t *> g_order_pool[kMaxDevices];
+std::atomic<uint64_t> g_order_ticket{0};
+
+bool order_counters(DecArgs &a, uint32_t count) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+    uint64_t *p = dev < kMaxDevices ? g_order_pool[dev].load(std::memory_order_relaxed) : nullptr;
+    if (!p) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(g_order_sync)) != hipSuccess || !q) return false;
+        p = static_cast<uint64_t *>(q);
+        if (dev < kMaxDevices) g_order_pool[dev].store(p, std::memory_order_relaxed);
+    }
+    a.order_sync = p;
+    a.order_ticket = g_order_ticket.fetch_add(count, std::memory_order_relaxed);
+    return true;
+}
 
 inline uint64_t enc_tiles(uint64_t n) { return (n + kEncTile - 1) / kEncTile; }
 
@@ -1534,6 +1630,7 @@ int launch_decode(const DecItem *items, uint32_t count, int32_t *status, hipStre
     DecArgs a{};
     a.count = count;
     a.status = status;
+    if (!order_counters(a, count)) return SPLITZIP_ERR_HIP;
     uint64_t tiles = 0;
     for (uint32_t k = 0; k < count; ++k) {
         a.it[k] = items[k];
@@ -1566,6 +1663,7 @@ int launch_decode_slot(const splitzip_slot_item *items, uint32_t count, int32_t 
     DecArgs a{};
     a.count = count;
     a.status = status;
+    if (!order_counters(a, count)) return SPLITZIP_ERR_HIP;
     uint64_t tiles = 0, n_all = 0;
     for (uint32_t k = 0; k < count; ++k) {
         const splitzip_slot_item &I = items[k];

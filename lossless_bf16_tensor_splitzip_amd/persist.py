@@ -22,7 +22,7 @@ from __future__ import annotations
 import base64
 import ctypes
 
-from ._abi import Codebook, Meta
+from ._abi import META_ASCENDING, Codebook, Meta
 
 COVERAGE_GATE = 0.99
 
@@ -92,6 +92,8 @@ def meta_to_json(m: Meta) -> dict:
         "coverage": 1.0 if m.total == 0 else m.covered / m.total,
         "covered": int(m.covered),
         "total": int(m.total),
+        # this library's flag: the escape stream is in ascending order
+        "ascending": bool(m.flags & META_ASCENDING),
     }
 
 
@@ -107,6 +109,9 @@ def meta_from_json(d: dict) -> Meta:
     m.covered = int(d.get("covered", 0))
     m.total = int(d.get("total", 0))
     m.status = 0
+    # page-format metadata says nothing about the escape order: left clear,
+    # so the decode applies the escapes in any order
+    m.flags = META_ASCENDING if d.get("ascending") is True else 0
     return m
 
 

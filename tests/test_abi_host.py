@@ -56,7 +56,8 @@ def test_struct_layout_matches_header():
     assert _abi.Codebook.dec_lut.offset == 512
     assert _abi.Meta.status.offset == 96
     assert ctypes.sizeof(_abi.SlotItem) == 56 and ctypes.sizeof(_abi.Item) == 56
-    assert S.lib().splitzip_abi_version() == 1
+    assert S.lib().splitzip_abi_version() == 2
+    assert _abi.Meta.flags.offset == 100
 
 
 def test_payload_size_matches_golden_layout():

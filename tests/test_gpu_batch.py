@@ -151,3 +151,42 @@ def test_workload_kv_stream_batched():
         m = S.read_meta(b.metas[k])
         check_meta(m, om, ocb)
         assert b.payloads[k][: m.comp_bytes].cpu().numpy().tobytes() == opay, k
+
+
+def test_batch_decode_streams_not_marked_ascending():
+    """A batched decode whose items mix streams marked ascending (patched per
+    tile) with streams whose metadata lacks the flag (applied by the last
+    workgroup of each tensor, in any order), one of them shuffled; no status
+    word; twice in a row (the arrival counters carry no state between
+    calls)."""
+    xs_cpu = [W.log_uniform_stress(8192 * 5 + 3, seed=61), W.gaussian_weight(200_003, seed=62),
+              W.log_uniform_stress(50_001, seed=63), W.kv_layer(seed=2, stream=0, seq=256),
+              W.log_uniform_stress(8192 * 9, seed=64)]
+    xs = [x.reshape(-1).to(DEV) for x in xs_cpu]
+    b = S.Batch(xs)
+    ws = S.Workspace(0, device=DEV, batch_ns=b.ns)
+    b.calibrate(ws)
+    b.encode(ws)
+    torch.cuda.synchronize()
+    flags_at = _abi.Meta.flags.offset
+    rng = np.random.default_rng(6)
+    for k in (1, 2, 4):
+        b.metas[k][flags_at: flags_at + 4] = 0
+    # item 2: escape stream in random order
+    m = S.read_meta(b.metas[2])
+    e = m.n_esc
+    assert e > 1000
+    pay = b.payloads[2][: m.comp_bytes].cpu().numpy().copy()
+    order = rng.permutation(e)
+    for sec, width in ((2, 4), (3, 2), (4, 1)):
+        at = m.offsets[sec]
+        items = pay[at: at + width * e].reshape(e, width)
+        pay[at: at + width * e] = items[order].reshape(-1)
+    b.payloads[2][: m.comp_bytes] = torch.from_numpy(pay).to(DEV)
+    for rep in range(2):
+        for o in b.outs:
+            o.fill_(0)
+        b.decode(status=None)
+        torch.cuda.synchronize()
+        for k, x in enumerate(xs):
+            assert torch.equal(b.outs[k].view(torch.int16), x.view(torch.int16)), (rep, k)

@@ -87,19 +87,22 @@ def check_meta(m, om, ocb_src):
     assert (m.covered, m.total) == (ocb_src.covered, ocb_src.total)
 
 
-def meta_to_device(om) -> torch.Tensor:
+def meta_to_device(om, ascending=False) -> torch.Tensor:
+    """Device metadata for an oracle payload: the page's fields only, unless
+    ``ascending`` marks the escape stream as sorted (this library's flag)."""
     m = _abi.Meta()
     m.n, m.n_pairs, m.chunk_size, m.n_esc, m.comp_bytes = (om.n, om.n_pairs, om.chunk_size,
                                                           om.n_esc, om.comp_bytes)
     for k in range(5):
         m.offsets[k] = om.offsets[k]
+    m.flags = _abi.META_ASCENDING if ascending else 0
     raw = bytes(m)
     return torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(DEV)
 
 
-def gpu_decode_bytes(payload: bytes, om, dec_lut, validate=True) -> tuple:
+def gpu_decode_bytes(payload: bytes, om, dec_lut, validate=True, ascending=False) -> tuple:
     pay = torch.frombuffer(bytearray(payload + b"\0" * 16), dtype=torch.uint8).to(DEV)
-    meta = meta_to_device(om)
+    meta = meta_to_device(om, ascending)
     lut = torch.tensor(np.asarray(dec_lut, np.uint8)).to(DEV)
     status = torch.zeros(1, dtype=torch.int32, device=DEV) if validate else None
     out = torch.empty(om.n, dtype=torch.bfloat16, device=DEV)
@@ -131,8 +134,13 @@ def full_parity(x_cpu, cb_source=None, name=""):
     assert np.array_equal(oracle.decode(g["payload"], om, ocb.dec_lut), xs)
     out2, st2 = gpu_decode_bytes(opay, om, ocb.dec_lut)
     assert st2 == 0 and np.array_equal(out2, xs)
+    # without a status word: page-format metadata (escapes applied in any
+    # order) and the same metadata marked ascending (patched per tile)
     out3, _ = gpu_decode_bytes(opay, om, ocb.dec_lut, validate=False)
     assert np.array_equal(out3, xs)
+    out4, _ = gpu_decode_bytes(opay, om, ocb.dec_lut, validate=False, ascending=True)
+    assert np.array_equal(out4, xs)
+    assert g["meta"].flags == _abi.META_ASCENDING
     return g, om
 
 
@@ -360,6 +368,50 @@ def test_unsorted_escape_stream_with_validation():
     out, st = gpu_decode_bytes(bytes(buf), om, ocb.dec_lut)
     assert st & _abi.DEC_NOT_INCREASING
     assert np.array_equal(out, xs)
+    # no status word: the metadata does not mark the stream ascending, so
+    # the escapes are applied by index in any order (page 1, decode_torch)
+    out, _ = gpu_decode_bytes(bytes(buf), om, ocb.dec_lut, validate=False)
+    assert np.array_equal(out, xs)
+
+
+def _shuffle_escapes(opay: bytes, om, rng) -> bytes:
+    buf = bytearray(opay)
+    e = om.n_esc
+    order = rng.permutation(e)
+    for sec, width in ((2, 4), (3, 2), (4, 1)):
+        at = om.offsets[sec]
+        items = np.frombuffer(bytes(buf[at: at + width * e]), np.uint8).reshape(e, width)
+        buf[at: at + width * e] = items[order].tobytes()
+    return bytes(buf)
+
+
+@pytest.mark.parametrize("make,n", [
+    (W.log_uniform_stress, 3 * 8192 + 77),      # dense escapes, all tiles
+    (W.gaussian_weight, 1_000_003),             # a few escapes
+    (W.log_uniform_stress, 100_003),
+])
+def test_shuffled_escape_stream_without_status(make, n):
+    """An escape stream in random order, with page-format metadata (no
+    ascending flag) and no status word, decodes bit for bit: plain, and in
+    place from the head of the output buffer."""
+    x = make(n, seed=77)
+    xs = host_bits(x)
+    ocb = oracle.calibrate(xs)
+    opay, om = oracle.encode(xs, ocb)
+    assert om.n_esc > 0
+    shuffled = _shuffle_escapes(opay, om, np.random.default_rng(n))
+    assert np.array_equal(oracle.decode(shuffled, om, ocb.dec_lut, validate=False), xs)
+    out, _ = gpu_decode_bytes(shuffled, om, ocb.dec_lut, validate=False)
+    assert np.array_equal(out, xs)
+    # in place
+    slot = torch.zeros(max(2 * n, om.comp_bytes), dtype=torch.uint8)
+    slot[: om.comp_bytes] = torch.frombuffer(bytearray(shuffled), dtype=torch.uint8)
+    slot = slot.to(DEV)
+    stash = torch.empty(om.comp_bytes, dtype=torch.uint8, device=DEV)
+    lut = torch.tensor(np.asarray(ocb.dec_lut, np.uint8)).to(DEV)
+    res = S.decode_slot(slot, meta_to_device(om), lut, n, stash)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.bits(res.cpu()).numpy().view(np.uint16), xs)
 
 
 @pytest.mark.parametrize("tiles", [255, 256, 257, 513])

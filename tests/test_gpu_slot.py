@@ -45,13 +45,13 @@ def oracle_case(x_cpu):
     return xs, ocb, opay, om
 
 
-def run_slot(opay, om, dec_lut, validate=True, extra=0, stash_extra=0):
+def run_slot(opay, om, dec_lut, validate=True, extra=0, stash_extra=0, ascending=False):
     n = om.n
     slot = slot_for(opay, n, extra)
     stash = stash_for(om.comp_bytes, stash_extra)
     lut = torch.tensor(np.asarray(dec_lut, np.uint8)).to(DEV)
     st = torch.zeros(1, dtype=torch.int32, device=DEV) if validate else None
-    out = S.decode_slot(slot, meta_to_device(om), lut, n, stash, status=st)
+    out = S.decode_slot(slot, meta_to_device(om, ascending), lut, n, stash, status=st)
     torch.cuda.synchronize()
     return slot, host_bits(out), (int(st.item()) if validate else 0)
 
@@ -60,8 +60,10 @@ def check_slot(x_cpu, name, extra=0):
     xs, ocb, opay, om = oracle_case(x_cpu)
     n = om.n
     _say("slot case %s n=%d e=%d comp=%d" % (name, n, om.n_esc, om.comp_bytes))
-    for validate in (False, True):
-        slot, out, st = run_slot(opay, om, ocb.dec_lut, validate, extra)
+    # the oracle's escapes are ascending: decoded with and without the flag
+    # that says so (per-tile patch, or the order-independent pass)
+    for validate, ascending in ((False, True), (False, False), (True, True)):
+        slot, out, st = run_slot(opay, om, ocb.dec_lut, validate, extra, ascending=ascending)
         assert st == 0
         assert np.array_equal(out, xs), name
         # bytes past the decoded tensor and past the payload are left alone

@@ -108,3 +108,16 @@ def test_codebook_json_rejects_marked_values_above_16():
         pass
     else:
         raise AssertionError("a marked table with 17 was accepted")
+
+
+def test_meta_json_ascending_flag():
+    m = S.Meta()
+    m.n, m.n_pairs, m.chunk_size = 10, 5, 1024
+    m.flags = 1
+    d = json.loads(json.dumps(persist.meta_to_json(m)))
+    assert d["ascending"] is True
+    assert persist.meta_from_json(d).flags == 1
+    # the pages' PayloadMeta keys say nothing about the order: flag clear
+    page = {k: d[k] for k in ("n", "n_pairs", "chunk_size", "n_esc", "comp_bytes", "offsets",
+                              "coverage")}
+    assert persist.meta_from_json(page).flags == 0
