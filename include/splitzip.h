@@ -155,9 +155,12 @@ size_t splitzip_workspace_size(uint64_t n);
  * of them. */
 size_t splitzip_workspace_size_batch(const uint64_t *n, uint32_t count);
 
-/* Prepare a workspace for first use (enqueues a zero-fill kernel).  The
- * library keeps it consistent afterwards; one workspace must not be used by
- * two calls that can run at the same time.
+/* Zero-fill the calibrate area of a workspace (enqueues a fill kernel).
+ * Optional: no call needs the workspace to hold any particular value
+ * beforehand (its arrival counters carry a tag per call, so a value left
+ * by an interrupted call, by another process or by a stray write is simply
+ * replaced).  One workspace must not be used by two calls that can run at
+ * the same time.
  * Errors: INVALID (null or unaligned d_ws, ws_bytes below the minimum), HIP. */
 int splitzip_workspace_init(void *d_ws, size_t ws_bytes, void *stream);
 

@@ -91,7 +91,8 @@ constexpr int kCalMaxGrid = 512;              // workgroups per tensor, at most
 constexpr int kCalTarget = 2;                 // resident 1024-thread workgroups per CU
 constexpr uint64_t kCalLongLoop = 32;         // ... one instead when each still loops this often
 constexpr int kCalGroup = 16;                 // arrivals per first-level counter
-constexpr int kCalCopies = 16;                // global histogram copies per tensor
+constexpr int kCalSingle = 32;                // one counter when a tensor has at most this many workgroups
+constexpr int kCalMaxWgs = 1024;              // workgroups per calibrate launch, at most
 // Encode tiles placed per tail workgroup: chosen per launch, a power of two
 // from kTailMinTiles (enough workgroups to spread dense escape streams over
 // the GPU) to kTailMaxTiles (fewer workgroups when the launch has many tiles).
@@ -116,18 +117,22 @@ constexpr int kDecStaged = 512;               // decode: escapes per tile above 
 // again (16 KB read instead of 8 bytes staged and read back per escape).
 constexpr uint32_t kStageCap = 512;
 
-// Workspace layout (bytes).  kMaxBatch calibrate slots, each with its
-// counters on separate cache lines and its histogram copies (all of which
-// return to zero at the end of every call), then the encode tile counts, the
-// count sums per tail block and per superblock, and the escape staging area,
-// whose sizes depend only on the workspace size.
-constexpr size_t kSlotTop = 0;                                           // uint32
-constexpr size_t kSlotLvl1 = 64;                                         // uint32, 64 B apart
-constexpr size_t kSlotHist = kSlotLvl1 + 64 * (kCalMaxGrid / kCalGroup); // uint64[16][256]
-constexpr size_t kCalSlot = (kSlotHist + 8 * 256 * kCalCopies + 255) & ~size_t(255);
-constexpr size_t kWsTiles = kCalSlot * kMaxBatch;                        // uint32[t_max], stage
+// Workspace layout (bytes).  The calibrate area: per tensor of a launch its
+// arrival counters (tagged, see tagged_arrive: no clearing between calls),
+// one histogram row per workgroup and one per group of workgroups; then the
+// encode tile counts, the count sums per tail block and per superblock, and
+// the escape staging area, whose sizes depend only on the workspace size.
+// Nothing in the workspace needs to hold any particular value before a call.
+constexpr size_t kCalCounters = 1 + kCalMaxGrid / kCalGroup;             // top + groups, 64 B apart
+constexpr size_t kCalRowsOff = 64 * kCalCounters * kMaxBatch;            // uint32[kCalMaxWgs][256]
+constexpr size_t kCalGroupRows = kCalMaxWgs / kCalGroup + kMaxBatch;
+constexpr size_t kCalGrowsOff = kCalRowsOff + 4 * 256 * (size_t)kCalMaxWgs;   // uint64[kCalGroupRows][256]
+constexpr size_t kWsTiles = (kCalGrowsOff + 8 * 256 * kCalGroupRows + 255) & ~size_t(255);
 constexpr size_t kWsSlack = 64;
 static_assert(kWsTiles % 256 == 0, "alignment");
+static_assert(kCalSingle % 4 == 0 && kCalGroup % 4 == 0 && (kCalMaxGrid / kCalGroup) % 4 == 0 &&
+                  kCalThreads == 1024,
+              "calibrate row sums: four quarters of 256 threads");
 static_assert(kSuperTiles == kThreads && kTailMaxTiles <= 64 && kTailMaxTiles <= kTailThreads &&
                   kTailThreads % 64 == 0 && (kTailMinTiles & (kTailMinTiles - 1)) == 0 &&
                   kTailMinTiles <= kTailMaxTiles && kSuperTiles / kTailMinTiles <= kTailThreads,
@@ -202,13 +207,6 @@ __host__ __device__ inline bool chunk_ok(uint64_t n, uint64_t chunk) {
     return chunk >= 1 && chunk <= kMaxChunk && (n + chunk - 1) / chunk <= (1ull << 31);
 }
 
-__device__ inline uint64_t ld_agent(const uint64_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void st_agent(uint64_t *p, uint64_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // popcount of the bits of m held by lanes below this one
 __device__ inline uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -223,6 +221,25 @@ __device__ inline uint64_t wave_sum_u64(uint64_t v) {
 // Wait until every vector memory operation this wave issued has completed
 // (for atomics: performed at the device coherence point).
 __device__ inline void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Tagged arrival on a 64-bit counter (tag << 32 | arrivals), for `total`
+// arrivals per call: the first arrival of a call replaces a value with
+// another tag by (tag << 32); later arrivals see the tag and only add; the
+// last one puts (tag << 32) back, so that a replay of a captured graph (the
+// same tag again) also starts from zero.  Returns true for the last arrival.
+__device__ inline bool tagged_arrive(uint64_t *c, uint32_t tag, uint64_t total) {
+    uint64_t cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // a failed exchange leaves the current value in cur: normally another
+    // arrival's claim, so the loop ends; bounded regardless
+    for (int k = 0; k < 64 && (uint32_t)(cur >> 32) != tag; ++k)
+        if (__hip_atomic_compare_exchange_strong(c, &cur, (uint64_t)tag << 32, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            break;
+    const uint64_t prev = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = (uint32_t)prev + 1ull == total;
+    if (last) __hip_atomic_store(c, (uint64_t)tag << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return last;
+}
 
 // Last k in [0, count) with start[k] <= g, for start[0] = 0 <= g < start[count].
 template <typename T>
@@ -263,9 +280,30 @@ struct CalItem {
 struct CalArgs {
     uint32_t count;
     uint32_t wg_start[kMaxBatch + 1];   // first workgroup of each tensor
+    uint32_t grp_start[kMaxBatch + 1];  // first group row of each tensor
     CalItem it[kMaxBatch];
-    uint8_t *ws;                        // calibrate slots
+    uint8_t *ws;                        // calibrate area
+    uint64_t ticket;                    // counter tags: ticket + tensor + 1
 };
+
+// Sum over rows q, q + 4, q + 8, ... < count (count <= 4 K) of row[bin],
+// every load issued before the first is used; agent-scope loads, so that
+// rows another XCD wrote are read from the coherence point.
+template <int K, typename T>
+__device__ inline uint64_t sum_rows(const T *rows, uint32_t count, int q, int bin) {
+    T v[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const uint32_t w = (uint32_t)q + 4u * k;
+        v[k] = w < count ? __hip_atomic_load(rows + (size_t)w * 256 + bin, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)
+                         : T(0);
+    }
+    uint64_t acc = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) acc += v[k];
+    return acc;
+}
 
 __global__ __launch_bounds__(kCalThreads) void k_calibrate(CalArgs a) {
     __shared__ uint32_t hist[256 * 64];   // [exponent][lane]
@@ -278,7 +316,6 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(CalArgs a) {
     const CalItem I = a.it[item];
     const uint32_t wg = blockIdx.x - a.wg_start[item];
     const uint32_t nwg = a.wg_start[item + 1] - a.wg_start[item];
-    uint8_t *slot = a.ws + (size_t)item * kCalSlot;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -331,60 +368,74 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(CalArgs a) {
         part[tid] = s;
     }
     __syncthreads();
-    // Merge into one of kCalCopies global histograms (few workgroups per
-    // address, so the device atomics do not queue up behind each other).
-    uint64_t *ghist = reinterpret_cast<uint64_t *>(slot + kSlotHist);
+    // This workgroup's histogram goes to its own row (write-through stores,
+    // so that a workgroup on another XCD reads it from the coherence point);
+    // nothing is accumulated into memory that an earlier call left behind.
+    uint32_t *rows = reinterpret_cast<uint32_t *>(a.ws + kCalRowsOff);
+    uint64_t *grows = reinterpret_cast<uint64_t *>(a.ws + kCalGrowsOff);
+    uint64_t *ctrs = reinterpret_cast<uint64_t *>(a.ws) + 8 * kCalCounters * item;
     if (tid < 256) {
         const uint32_t s = part[tid] + part[256 + tid] + part[512 + tid] + part[768 + tid];
-        if (s)
-            atomicAdd(reinterpret_cast<unsigned long long *>(ghist + (wg % kCalCopies) * 256 + tid),
-                      (unsigned long long)s);
+        __hip_atomic_store(rows + (size_t)blockIdx.x * 256 + tid, s, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
     wait_vector_memory();
     __syncthreads();
 
-    // Arrival: the last workgroup of each group of 16 reports to the top
-    // counter; the last group merges the copies and selects the codes.
-    const uint32_t g = wg / kCalGroup;
-    const uint32_t gsize = min((uint32_t)kCalGroup, nwg - g * kCalGroup);
-    const uint32_t ngroups = (nwg + kCalGroup - 1) / kCalGroup;
-    if (tid == 0) {
-        uint32_t *ctr = reinterpret_cast<uint32_t *>(slot + kSlotLvl1 + 64 * g);
-        const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t go = 0;
-        if (prev == gsize - 1) {
-            __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            uint32_t *top = reinterpret_cast<uint32_t *>(slot + kSlotTop);
-            const uint32_t p2 = __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-            if (p2 == ngroups - 1) {
-                __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                go = 1;
-            }
-        }
-        proceed = go;
-        covered = 0;
-    }
-    __syncthreads();
-    if (!proceed) return;
-
+    // Arrival: with few workgroups one counter, whose last arriver sums the
+    // rows; else the last arriver of each group of kCalGroup sums the
+    // group's rows into a group row and reports to the tensor's top counter,
+    // whose last arriver sums the group rows.
+    const uint32_t tag = (uint32_t)(a.ticket + item) + 1u;
+    const uint32_t row0 = a.wg_start[item];
+    const int bin = tid & 255, quarter = tid >> 8;
     uint64_t c = 0;
-    if (tid < 256) {
-        uint64_t copy[kCalCopies];
-#pragma unroll
-        for (int k = 0; k < kCalCopies; ++k) copy[k] = ld_agent(ghist + k * 256 + tid);
-#pragma unroll
-        for (int k = 0; k < kCalCopies; ++k) {
-            c += copy[k];
-            st_agent(ghist + k * 256 + tid, 0);   // clean for the next call
+    if (nwg <= (uint32_t)kCalSingle) {
+        if (tid == 0) proceed = tagged_arrive(ctrs, tag, nwg);
+        __syncthreads();
+        if (!proceed) return;
+        const uint64_t acc = sum_rows<kCalSingle / 4>(rows + (size_t)row0 * 256, nwg, quarter, bin);
+        reinterpret_cast<uint64_t *>(hist)[tid] = acc;   // the histogram copies are done with
+        __syncthreads();
+        if (tid < 256) {
+            const uint64_t *h = reinterpret_cast<const uint64_t *>(hist);
+            c = h[tid] + h[256 + tid] + h[512 + tid] + h[768 + tid];
         }
+    } else {
+        const uint32_t g = wg / kCalGroup;
+        const uint32_t gsize = min((uint32_t)kCalGroup, nwg - g * kCalGroup);
+        const uint32_t ngroups = (nwg + kCalGroup - 1) / kCalGroup;
+        if (tid == 0) proceed = tagged_arrive(ctrs + 8 * (1 + g), tag, gsize);
+        __syncthreads();
+        if (!proceed) return;
+        uint64_t acc = sum_rows<kCalGroup / 4>(rows + (size_t)(row0 + g * kCalGroup) * 256, gsize,
+                                               quarter, bin);
+        uint64_t *h = reinterpret_cast<uint64_t *>(hist);
+        h[tid] = acc;
+        __syncthreads();
+        uint64_t *grow = grows + (size_t)(a.grp_start[item] + g) * 256;
+        if (tid < 256)
+            __hip_atomic_store(grow + tid, h[tid] + h[256 + tid] + h[512 + tid] + h[768 + tid],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wait_vector_memory();
+        __syncthreads();
+        if (tid == 0) proceed = tagged_arrive(ctrs, tag, ngroups);
+        __syncthreads();
+        if (!proceed) return;
+        acc = sum_rows<(kCalMaxGrid / kCalGroup) / 4>(grows + (size_t)a.grp_start[item] * 256,
+                                                      ngroups, quarter, bin);
+        __syncthreads();
+        h[tid] = acc;
+        __syncthreads();
+        if (tid < 256) c = h[tid] + h[256 + tid] + h[512 + tid] + h[768 + tid];
+    }
+    if (tid == 0) covered = 0;
+    if (tid < 256) {
         // unique sort key: count first, then the smaller exponent value
         key[tid] = c ? ((c << 8) | (uint64_t)(255 - tid)) : 0;
     }
     __syncthreads();
     {   // rank = number of larger keys; 4 threads per exponent, 64 keys each
-        const int bin = tid & 255, quarter = tid >> 8;
         const uint64_t mine = key[bin];
         uint32_t r = 0;
         for (int u = quarter * 64; u < quarter * 64 + 64; ++u) r += key[u] > mine ? 1u : 0u;
@@ -1027,27 +1078,13 @@ struct DecArgs {
 
 // Arrival counters of the order-independent escape pass (streams not marked
 // ascending): tensor k of a call uses counter (ticket + k) mod kOrderSlots,
-// tagged (ticket + k + 1) in its high half, so a counter needs no clearing
-// between calls and a stale or foreign value is simply replaced.  Library
+// tagged (ticket + k + 1) in its high half (see tagged_arrive), so a
+// counter needs no clearing and a stale or foreign value is simply replaced.  Library
 // state on every device that runs a decode, kept until the process ends;
 // calls that run at the same time use different counters unless 65,536
 // tensors' decodes are issued while one of them waits to run.
 constexpr uint32_t kOrderSlots = 65536;
 __device__ __align__(256) uint64_t g_order_sync[kOrderSlots];
-
-// Epoch-tagged arrival on a 64-bit counter (tag << 32 | arrivals): the first
-// arrival of a call replaces a value with another tag by (tag << 32); later
-// arrivals see the tag and only add.  Returns the arrivals before this one.
-__device__ inline uint32_t tagged_arrive(uint64_t *c, uint32_t tag) {
-    uint64_t cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // a failed exchange leaves the current value in cur: normally another
-    // arrival's claim, so the loop ends; bounded regardless
-    for (int k = 0; k < 64 && (uint32_t)(cur >> 32) != tag; ++k)
-        if (__hip_atomic_compare_exchange_strong(c, &cur, (uint64_t)tag << 32, __ATOMIC_RELAXED,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-            break;
-    return (uint32_t)__hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Metadata must describe exactly the layout of (n, n_esc) and fit the buffer.
 __device__ inline bool meta_ok(const DecItem &I, Layout &L) {
@@ -1132,8 +1169,7 @@ __device__ void order_pass(const DecArgs &a, const DecItem &I, uint32_t item, co
     if (threadIdx.x == 0) {
         const uint64_t t = a.order_ticket + item;
         const uint64_t ntiles = a.tile_start[item + 1] - a.tile_start[item];
-        const uint32_t prev = tagged_arrive(a.order_sync + (t & (kOrderSlots - 1)), (uint32_t)t + 1u);
-        *last = (uint64_t)prev + 1 == ntiles;
+        *last = tagged_arrive(a.order_sync + (t & (kOrderSlots - 1)), (uint32_t)t + 1u, ntiles);
     }
     __syncthreads();
     if (!*last) return;
@@ -1480,9 +1516,11 @@ bool cu_count(int &cus) {
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // The current device's address of g_order_sync (each device holds its own
-// copy), cached per device, and the next decode call's first counter.
+// copy), cached per device.
 std::atomic<uint64_t *> g_order_pool[kMaxDevices];
-std::atomic<uint64_t> g_order_ticket{0};
+// Tags of the tagged arrival counters: each call takes as many as it has
+// tensors (shared by calibrate and decode; only uniqueness matters).
+std::atomic<uint64_t> g_ticket{0};
 
 bool order_counters(DecArgs &a, uint32_t count) {
     int dev = 0;
@@ -1495,7 +1533,7 @@ bool order_counters(DecArgs &a, uint32_t count) {
         if (dev < kMaxDevices) g_order_pool[dev].store(p, std::memory_order_relaxed);
     }
     a.order_sync = p;
-    a.order_ticket = g_order_ticket.fetch_add(count, std::memory_order_relaxed);
+    a.order_ticket = g_ticket.fetch_add(count, std::memory_order_relaxed);
     return true;
 }
 
@@ -1554,8 +1592,10 @@ int launch_calibrate(const CalItem *items, uint32_t count, uint8_t *ws, hipStrea
     // kCalLongLoop rounds of loads is faster with one (longer contiguous
     // ranges, half the merges: 2 % on 32 tensors of 32M elements).
     const uint64_t long_enough = kCalLongLoop * 4 * (uint64_t)kCalThreads * (uint64_t)cus;
-    const uint64_t target = (uint64_t)((total >> 3) >= long_enough ? 1 : kCalTarget) * cus;
-    uint32_t wg = 0;
+    uint64_t target = (uint64_t)((total >> 3) >= long_enough ? 1 : kCalTarget) * cus;
+    // every workgroup has a histogram row: at most kCalMaxWgs per launch
+    if (target > kCalMaxWgs - kMaxBatch) target = kCalMaxWgs - kMaxBatch;
+    uint32_t wg = 0, grp = 0;
     for (uint32_t k = 0; k < count; ++k) {
         a.it[k] = items[k];
         uint64_t g = total ? ceil_div(target * items[k].n, total) : 1;
@@ -1564,9 +1604,14 @@ int launch_calibrate(const CalItem *items, uint32_t count, uint8_t *ws, hipStrea
         if (g > kCalMaxGrid) g = kCalMaxGrid;
         if (g == 0) g = 1;
         a.wg_start[k] = wg;
+        a.grp_start[k] = grp;
         wg += (uint32_t)g;
+        if (g > (uint64_t)kCalSingle) grp += (uint32_t)ceil_div(g, kCalGroup);
     }
     a.wg_start[count] = wg;
+    a.grp_start[count] = grp;
+    if (wg > (uint32_t)kCalMaxWgs || grp > kCalGroupRows) return SPLITZIP_ERR_INTERNAL;
+    a.ticket = g_ticket.fetch_add(count, std::memory_order_relaxed);
     k_calibrate<<<wg, kCalThreads, 0, s>>>(a);
     return launched();
 }
