@@ -191,6 +191,24 @@ int splitzip_encode(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_
                     uint8_t *d_payload, uint64_t capacity, splitzip_meta *d_meta, void *d_ws,
                     size_t ws_bytes, void *stream);
 
+/* splitzip_encode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid it): the same
+ * computation and output, with no workspace argument.  Its scratch is a
+ * SPLITZIP_NOALLOC_SCRATCH_BYTES array in device memory the library owns
+ * (each device that runs the call holds its own copy until the process
+ * ends); no call allocates or frees memory.  Every call on one device shares
+ * that device's array: calls that may run at the same time on one device
+ * (on different streams, or a graph replay overlapping a call) race and
+ * must not be issued; calls ordered on one stream are fine, as nothing in
+ * the array needs any value before a call.
+ * Synchronous errors: as splitzip_encode, and WORKSPACE when n exceeds
+ * SPLITZIP_NOALLOC_MAX_N (16,312 encode tiles of 8192 elements). */
+#define SPLITZIP_NOALLOC_SCRATCH_BYTES (32ull << 20)
+#define SPLITZIP_NOALLOC_MAX_N 133627904ull
+int splitzip_encode_noalloc(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_cb,
+                            uint8_t *d_payload, uint64_t capacity, splitzip_meta *d_meta,
+                            void *stream);
+
 /* Encode with another escape-stream chunk size (page 1, encode, parameter
  * chunk_size): chunk id = element / chunk_size, local position = element %
  * chunk_size.  Only the escape sections and meta->chunk_size differ from

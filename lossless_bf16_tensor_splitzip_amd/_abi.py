@@ -14,6 +14,7 @@ from ._build import CEILING_LIB_PATH, LIB_PATH
 
 CHUNK = 1024
 MAX_N = 1 << 36
+NOALLOC_MAX_N = 133627904        # splitzip_encode_noalloc's limit
 
 OK = 0
 ERR_INVALID = 1
@@ -107,6 +108,7 @@ SIGNATURES = {
     "splitzip_encode": (ctypes.c_int, [_P, _U64, _P, _P, _U64, _P, _P, _SZ, _P]),
     "splitzip_encode_chunked": (ctypes.c_int, [_P, _U64, _P, ctypes.c_uint32, _P, _U64, _P, _P, _SZ,
                                                _P]),
+    "splitzip_encode_noalloc": (ctypes.c_int, [_P, _U64, _P, _P, _U64, _P, _P]),
     "splitzip_decode": (ctypes.c_int, [_P, _U64, _P, _P, _P, _U64, _P, _P]),
     "splitzip_decode_slot": (ctypes.c_int, [_P, _U64, _P, _P, _U64, _P, _U64, _P, _P]),
     "splitzip_decode_slot_batch": (ctypes.c_int, [_P, ctypes.c_uint32, _P, _P]),
@@ -215,6 +217,11 @@ def splitzip_encode_chunked(d_x: int, n: int, d_cb: int, chunk_size: int, d_payl
                             stream: int) -> int:
     return lib().splitzip_encode_chunked(d_x, n, d_cb, chunk_size, d_payload, capacity, d_meta,
                                          d_ws, ws_bytes, stream)
+
+
+def splitzip_encode_noalloc(d_x: int, n: int, d_cb: int, d_payload: int, capacity: int,
+                            d_meta: int, stream: int) -> int:
+    return lib().splitzip_encode_noalloc(d_x, n, d_cb, d_payload, capacity, d_meta, stream)
 
 
 def splitzip_decode(d_payload: int, payload_bytes: int, d_meta: int, d_dec_lut: int, d_out: int,

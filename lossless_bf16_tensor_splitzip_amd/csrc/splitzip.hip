@@ -142,8 +142,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef u32x2 u32x2_a4 __attribute__((aligned(4)));
 
-__host__ __device__ inline uint64_t align4(uint64_t v) { return (v + 3u) & ~uint64_t(3); }
-__host__ __device__ inline uint64_t align16(uint64_t v) { return (v + 15u) & ~uint64_t(15); }
+__host__ __device__ constexpr uint64_t align4(uint64_t v) { return (v + 3u) & ~uint64_t(3); }
+__host__ __device__ constexpr uint64_t align16(uint64_t v) { return (v + 15u) & ~uint64_t(15); }
 
 struct Layout {
     uint64_t n_pairs, off_sm, off_cid, off_lpos, off_ev, total;
@@ -176,16 +176,19 @@ constexpr uint64_t kWsPerTile =
 constexpr uint64_t kWsFixed = kWsTiles + kWsSlack + 4 * 128;
 static_assert(kTailMinTiles <= 4, "block sums fit the per-tile budget");
 
-__host__ inline WsPlan ws_plan(size_t ws_bytes) {
+// head: bytes before the encode area (the calibrate area of a workspace;
+// none in an encode-only buffer)
+__host__ constexpr WsPlan ws_plan(size_t ws_bytes, size_t head = kWsTiles) {
     WsPlan P{0, 0, 0, 0, 0};
-    if (ws_bytes < kWsFixed) return P;
-    P.t_max = (ws_bytes - kWsFixed) / kWsPerTile;
-    P.off_count = kWsTiles;
+    if (ws_bytes < head + kWsSlack + 4 * 128) return P;
+    P.t_max = (ws_bytes - head - kWsSlack - 4 * 128) / kWsPerTile;
+    P.off_count = head;
     P.off_bsum = align16(P.off_count + 4 * P.t_max);
     P.off_ssum = align16(P.off_bsum + 4 * (P.t_max / kTailMinTiles + 64));
     P.off_stage = align16(P.off_ssum + 4 * (P.t_max / kSuperTiles + 64));
     return P;
 }
+static_assert(kWsFixed == kWsTiles + kWsSlack + 4 * 128, "workspace plan");
 
 // Chunk id and chunk-local position of element i (shift and mask when the
 // chunk size is a power of two).
@@ -1518,6 +1521,31 @@ inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)
 // The current device's address of g_order_sync (each device holds its own
 // copy), cached per device.
 std::atomic<uint64_t *> g_order_pool[kMaxDevices];
+// Workspace of splitzip_encode_noalloc, for callers that cannot allocate:
+// an encode-only area (tile counts, count sums, staging) of fixed size in
+// device memory the library owns.  Each device holds its own copy until the
+// process ends; host code reaches it only through its per-device address.
+constexpr size_t kScratchBytes = SPLITZIP_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr WsPlan kScratchPlan = ws_plan(kScratchBytes, 0);
+static_assert(kScratchPlan.t_max * kEncTile == SPLITZIP_NOALLOC_MAX_N,
+              "the header's limit is the scratch plan's");
+std::atomic<uint8_t *> g_scratch[kMaxDevices];
+
+// Address of `scratch` on the current device, looked up on the first call
+// on that device.
+bool scratch_of_device(uint8_t *&p) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+    p = dev < kMaxDevices ? g_scratch[dev].load(std::memory_order_relaxed) : nullptr;
+    if (p) return true;
+    void *q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return false;
+    p = static_cast<uint8_t *>(q);
+    if (dev < kMaxDevices) g_scratch[dev].store(p, std::memory_order_relaxed);
+    return true;
+}
+
 // Tags of the tagged arrival counters: each call takes as many as it has
 // tensors (shared by calibrate and decode; only uniqueness matters).
 std::atomic<uint64_t> g_ticket{0};
@@ -1834,6 +1862,18 @@ int splitzip_encode(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_
                     size_t ws_bytes, void *stream) {
     return splitzip_encode_chunked(d_x, n, d_cb, kChunk, d_payload, capacity, d_meta, d_ws,
                                    ws_bytes, stream);
+}
+
+int splitzip_encode_noalloc(const uint16_t *d_x, uint64_t n, const splitzip_codebook *d_cb,
+                            uint8_t *d_payload, uint64_t capacity, splitzip_meta *d_meta,
+                            void *stream) {
+    const int rc = check_encode_item(d_x, n, d_cb, d_payload, capacity, d_meta);
+    if (rc) return rc;
+    if (enc_tiles(n) > kScratchPlan.t_max) return SPLITZIP_ERR_WORKSPACE;   // n > SPLITZIP_NOALLOC_MAX_N
+    uint8_t *ws = nullptr;
+    if (!scratch_of_device(ws)) return SPLITZIP_ERR_HIP;
+    const EncItem it{d_x, n, d_cb, d_payload, capacity, d_meta, kChunk};
+    return launch_encode(&it, 1, kScratchPlan, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
 int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const splitzip_meta *d_meta,
