@@ -92,7 +92,9 @@ constexpr int kCalTarget = 2;                 // resident 1024-thread workgroups
 constexpr uint64_t kCalLongLoop = 32;         // ... one instead when each still loops this often
 constexpr int kCalGroup = 16;                 // arrivals per first-level counter
 constexpr int kCalSingle = 32;                // one counter when a tensor has at most this many workgroups
-constexpr int kCalMaxWgs = 1024;              // workgroups per calibrate launch, at most
+constexpr int kCalCopies = 16;                // global histogram copies per tensor
+constexpr int kBinCountBits = 37;             // a copy's bin: tag << 37 | count (counts < 2^37)
+constexpr uint64_t kBinCountMask = (1ull << kBinCountBits) - 1;
 // Encode tiles placed per tail workgroup: chosen per launch, a power of two
 // from kTailMinTiles (enough workgroups to spread dense escape streams over
 // the GPU) to kTailMaxTiles (fewer workgroups when the launch has many tiles).
@@ -117,22 +119,22 @@ constexpr int kDecStaged = 512;               // decode: escapes per tile above 
 // again (16 KB read instead of 8 bytes staged and read back per escape).
 constexpr uint32_t kStageCap = 512;
 
-// Workspace layout (bytes).  The calibrate area: per tensor of a launch its
-// arrival counters (tagged, see tagged_arrive: no clearing between calls),
-// one histogram row per workgroup and one per group of workgroups; then the
-// encode tile counts, the count sums per tail block and per superblock, and
-// the escape staging area, whose sizes depend only on the workspace size.
-// Nothing in the workspace needs to hold any particular value before a call.
-constexpr size_t kCalCounters = 1 + kCalMaxGrid / kCalGroup;             // top + groups, 64 B apart
-constexpr size_t kCalRowsOff = 64 * kCalCounters * kMaxBatch;            // uint32[kCalMaxWgs][256]
-constexpr size_t kCalGroupRows = kCalMaxWgs / kCalGroup + kMaxBatch;
-constexpr size_t kCalGrowsOff = kCalRowsOff + 4 * 256 * (size_t)kCalMaxWgs;   // uint64[kCalGroupRows][256]
-constexpr size_t kWsTiles = (kCalGrowsOff + 8 * 256 * kCalGroupRows + 255) & ~size_t(255);
+// Workspace layout (bytes).  The calibrate area: per tensor of a launch a
+// slot with its arrival counters (64 bytes apart) and its global histogram
+// copies, all tagged per call (see tagged_arrive and k_calibrate), so that
+// nothing needs clearing between calls; then the encode tile counts, the
+// count sums per tail block and per superblock, and the escape staging area,
+// whose sizes depend only on the workspace size.  Nothing in the workspace
+// needs to hold any particular value before a call.
+constexpr size_t kCalCounters = 1 + kCalMaxGrid / kCalGroup;             // top + groups
+// generation word, counters, uint64 copies[16][256]
+constexpr size_t kCalSlot = 64 + 64 * kCalCounters + 8 * 256 * kCalCopies;
+constexpr size_t kWsTiles = (kCalSlot * kMaxBatch + 255) & ~size_t(255);
+static_assert(kCalSlot % 64 == 0, "copies start on a cache line");
 constexpr size_t kWsSlack = 64;
 static_assert(kWsTiles % 256 == 0, "alignment");
-static_assert(kCalSingle % 4 == 0 && kCalGroup % 4 == 0 && (kCalMaxGrid / kCalGroup) % 4 == 0 &&
-                  kCalThreads == 1024,
-              "calibrate row sums: four quarters of 256 threads");
+static_assert(kCalThreads >= 256 && ((uint64_t)SPLITZIP_MAX_N >> kBinCountBits) == 0,
+              "calibrate: a thread per bin, counts fit a copy's bin");
 static_assert(kSuperTiles == kThreads && kTailMaxTiles <= 64 && kTailMaxTiles <= kTailThreads &&
                   kTailThreads % 64 == 0 && (kTailMinTiles & (kTailMinTiles - 1)) == 0 &&
                   kTailMinTiles <= kTailMaxTiles && kSuperTiles / kTailMinTiles <= kTailThreads,
@@ -225,22 +227,36 @@ __device__ inline uint64_t wave_sum_u64(uint64_t v) {
 // (for atomics: performed at the device coherence point).
 __device__ inline void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Tagged arrival on a 64-bit counter (tag << 32 | arrivals), for `total`
-// arrivals per call: the first arrival of a call replaces a value with
-// another tag by (tag << 32); later arrivals see the tag and only add; the
-// last one puts (tag << 32) back, so that a replay of a captured graph (the
-// same tag again) also starts from zero.  Returns true for the last arrival.
-__device__ inline bool tagged_arrive(uint64_t *c, uint32_t tag, uint64_t total) {
-    uint64_t cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Tagged arrival counters: a 64-bit word (tag << 32 | arrivals), `total`
+// arrivals per call.  Every arriver (or, in a tree, a member that the
+// arriver's own arrival depends on) claims the word for the call's tag
+// before it arrives: a word with another tag (junk, an interrupted call,
+// the last call) is replaced by (tag << 32); a claim that finds the tag
+// leaves the word alone.  The last arrival puts (tag << 32) back, so that a
+// replay of a captured graph (the same tag again) also starts from zero.
+// `cur` is a value of *c read earlier in this call (or the word's value now).
+__device__ inline void tagged_claim(uint64_t *c, uint64_t cur, uint64_t want, uint64_t tag_mask) {
     // a failed exchange leaves the current value in cur: normally another
     // arrival's claim, so the loop ends; bounded regardless
-    for (int k = 0; k < 64 && (uint32_t)(cur >> 32) != tag; ++k)
-        if (__hip_atomic_compare_exchange_strong(c, &cur, (uint64_t)tag << 32, __ATOMIC_RELAXED,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+    for (int k = 0; k < 64 && (cur & tag_mask) != want; ++k)
+        if (__hip_atomic_compare_exchange_strong(c, &cur, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
             break;
+}
+__device__ inline uint64_t ld_agent(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void counter_claim(uint64_t *c, uint64_t cur, uint32_t tag) {
+    tagged_claim(c, cur, (uint64_t)tag << 32, ~0ull << 32);
+}
+// Returns true for the last of `total` arrivals of the call, which leaves
+// (reset_tag << 32) behind: the same tag for a replay of the same
+// arguments, or the next call's tag when it is known.
+__device__ inline bool tagged_arrive(uint64_t *c, uint64_t total, uint32_t reset_tag) {
     const uint64_t prev = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = (uint32_t)prev + 1ull == total;
-    if (last) __hip_atomic_store(c, (uint64_t)tag << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (last)
+        __hip_atomic_store(c, (uint64_t)reset_tag << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return last;
 }
 
@@ -283,32 +299,13 @@ struct CalItem {
 struct CalArgs {
     uint32_t count;
     uint32_t wg_start[kMaxBatch + 1];   // first workgroup of each tensor
-    uint32_t grp_start[kMaxBatch + 1];  // first group row of each tensor
     CalItem it[kMaxBatch];
-    uint8_t *ws;                        // calibrate area
+    uint8_t *ws;                        // calibrate slots
     uint64_t ticket;                    // counter tags: ticket + tensor + 1
 };
 
-// Sum over rows q, q + 4, q + 8, ... < count (count <= 4 K) of row[bin],
-// every load issued before the first is used; agent-scope loads, so that
-// rows another XCD wrote are read from the coherence point.
-template <int K, typename T>
-__device__ inline uint64_t sum_rows(const T *rows, uint32_t count, int q, int bin) {
-    T v[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const uint32_t w = (uint32_t)q + 4u * k;
-        v[k] = w < count ? __hip_atomic_load(rows + (size_t)w * 256 + bin, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT)
-                         : T(0);
-    }
-    uint64_t acc = 0;
-#pragma unroll
-    for (int k = 0; k < K; ++k) acc += v[k];
-    return acc;
-}
-
-__global__ __launch_bounds__(kCalThreads) void k_calibrate(CalArgs a) {
+// (8 waves per SIMD: two 1024-thread workgroups per compute unit fit)
+__global__ __launch_bounds__(kCalThreads, 8) void k_calibrate(CalArgs a) {
     __shared__ uint32_t hist[256 * 64];   // [exponent][lane]
     __shared__ uint32_t part[4 * 256];
     __shared__ uint64_t key[256];
@@ -322,6 +319,26 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(CalArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
+    // The tensor's slot: generation word, arrival counters, global copies.
+    // The call's tag is the generation the last call left behind, which
+    // already tags every counter and bin; a word that is not a generation
+    // (its low half is not the complement of its high half: junk, a fresh
+    // workspace) gives way to a tag from the host's ticket, and counters
+    // and bins with another tag are claimed for it (tagged_claim).  The
+    // values this workgroup needs are read now and used after the
+    // histogram, so in the common case nothing waits for them.
+    uint64_t *genp = reinterpret_cast<uint64_t *>(a.ws + (size_t)item * kCalSlot);
+    uint64_t *ctrs = genp + 8;
+    uint64_t *copies = ctrs + 8 * kCalCounters;
+    uint64_t *mine = copies + (wg % kCalCopies) * 256;
+    const bool single = nwg <= (uint32_t)kCalSingle;
+    uint64_t gw = 0, seen = 0, seen_top = 0, seen_grp = 0;
+    if (tid <= 256) gw = ld_agent(genp);
+    if (tid < 256) seen = ld_agent(mine + tid);
+    if (tid == 256) {
+        seen_top = ld_agent(ctrs);
+        if (!single) seen_grp = ld_agent(ctrs + 8 * (1 + wg / kCalGroup));
+    }
     for (int i = tid; i < 256 * 64; i += kCalThreads) hist[i] = 0;
     __syncthreads();
 
@@ -371,67 +388,61 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(CalArgs a) {
         part[tid] = s;
     }
     __syncthreads();
-    // This workgroup's histogram goes to its own row (write-through stores,
-    // so that a workgroup on another XCD reads it from the coherence point);
-    // nothing is accumulated into memory that an earlier call left behind.
-    uint32_t *rows = reinterpret_cast<uint32_t *>(a.ws + kCalRowsOff);
-    uint64_t *grows = reinterpret_cast<uint64_t *>(a.ws + kCalGrowsOff);
-    uint64_t *ctrs = reinterpret_cast<uint64_t *>(a.ws) + 8 * kCalCounters * item;
+    // Merge into one of kCalCopies global copies (few workgroups per
+    // address, so the device atomics do not queue up behind each other).  A
+    // bin holds tag << 37 | count: the first workgroup of a call to reach a
+    // bin with another tag (junk, an interrupted call, the last call)
+    // replaces it by the tag with count 0; adds leave the tag alone.
+    const bool gen_ok = (uint32_t)gw == ~(uint32_t)(gw >> 32);
+    const uint32_t tag = gen_ok ? (uint32_t)(gw >> 32) : (uint32_t)(a.ticket + item) + 1u;
+    const uint32_t next = tag + 1u;
+    const uint64_t btag = (uint64_t)tag << kBinCountBits;    // the tag's low 27 bits
     if (tid < 256) {
+        tagged_claim(mine + tid, seen, btag, ~kBinCountMask);
         const uint32_t s = part[tid] + part[256 + tid] + part[512 + tid] + part[768 + tid];
-        __hip_atomic_store(rows + (size_t)blockIdx.x * 256 + tid, s, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        if (s) __hip_atomic_fetch_add(mine + tid, (uint64_t)s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     wait_vector_memory();
     __syncthreads();
 
-    // Arrival: with few workgroups one counter, whose last arriver sums the
-    // rows; else the last arriver of each group of kCalGroup sums the
-    // group's rows into a group row and reports to the tensor's top counter,
-    // whose last arriver sums the group rows.
-    const uint32_t tag = (uint32_t)(a.ticket + item) + 1u;
-    const uint32_t row0 = a.wg_start[item];
-    const int bin = tid & 255, quarter = tid >> 8;
-    uint64_t c = 0;
-    if (nwg <= (uint32_t)kCalSingle) {
-        if (tid == 0) proceed = tagged_arrive(ctrs, tag, nwg);
-        __syncthreads();
-        if (!proceed) return;
-        const uint64_t acc = sum_rows<kCalSingle / 4>(rows + (size_t)row0 * 256, nwg, quarter, bin);
-        reinterpret_cast<uint64_t *>(hist)[tid] = acc;   // the histogram copies are done with
-        __syncthreads();
-        if (tid < 256) {
-            const uint64_t *h = reinterpret_cast<const uint64_t *>(hist);
-            c = h[tid] + h[256 + tid] + h[512 + tid] + h[768 + tid];
+    // Arrival: with few workgroups one counter; else the last arriver of
+    // each group of kCalGroup reports to the tensor's top counter (claimed
+    // by the first workgroup of each group, whose arrival precedes the
+    // group's report).  The last arriver of all sums the copies' bins that
+    // carry this call's tag, then tags counters, bins and the generation
+    // word for the next call.
+    if (tid == 256) {
+        bool go;
+        if (single) {
+            counter_claim(ctrs, seen_top, tag);
+            go = tagged_arrive(ctrs, nwg, next);
+        } else {
+            const uint32_t g = wg / kCalGroup;
+            const uint32_t gsize = min((uint32_t)kCalGroup, nwg - g * kCalGroup);
+            if (wg % kCalGroup == 0) counter_claim(ctrs, seen_top, tag);
+            counter_claim(ctrs + 8 * (1 + g), seen_grp, tag);
+            go = tagged_arrive(ctrs + 8 * (1 + g), gsize, next) &&
+                 tagged_arrive(ctrs, (nwg + kCalGroup - 1) / kCalGroup, next);
         }
-    } else {
-        const uint32_t g = wg / kCalGroup;
-        const uint32_t gsize = min((uint32_t)kCalGroup, nwg - g * kCalGroup);
-        const uint32_t ngroups = (nwg + kCalGroup - 1) / kCalGroup;
-        if (tid == 0) proceed = tagged_arrive(ctrs + 8 * (1 + g), tag, gsize);
-        __syncthreads();
-        if (!proceed) return;
-        uint64_t acc = sum_rows<kCalGroup / 4>(rows + (size_t)(row0 + g * kCalGroup) * 256, gsize,
-                                               quarter, bin);
-        uint64_t *h = reinterpret_cast<uint64_t *>(hist);
-        h[tid] = acc;
-        __syncthreads();
-        uint64_t *grow = grows + (size_t)(a.grp_start[item] + g) * 256;
-        if (tid < 256)
-            __hip_atomic_store(grow + tid, h[tid] + h[256 + tid] + h[512 + tid] + h[768 + tid],
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        wait_vector_memory();
-        __syncthreads();
-        if (tid == 0) proceed = tagged_arrive(ctrs, tag, ngroups);
-        __syncthreads();
-        if (!proceed) return;
-        acc = sum_rows<(kCalMaxGrid / kCalGroup) / 4>(grows + (size_t)a.grp_start[item] * 256,
-                                                      ngroups, quarter, bin);
-        __syncthreads();
-        h[tid] = acc;
-        __syncthreads();
-        if (tid < 256) c = h[tid] + h[256 + tid] + h[512 + tid] + h[768 + tid];
+        proceed = go;
     }
+    __syncthreads();
+    if (!proceed) return;
+    uint64_t c = 0;
+    if (tid < 256) {
+        uint64_t copy[kCalCopies];
+#pragma unroll
+        for (int k = 0; k < kCalCopies; ++k) copy[k] = ld_agent(copies + k * 256 + tid);
+        const uint64_t nbtag = (uint64_t)next << kBinCountBits;
+#pragma unroll
+        for (int k = 0; k < kCalCopies; ++k) {
+            c += (copy[k] & ~kBinCountMask) == btag ? (copy[k] & kBinCountMask) : 0;
+            __hip_atomic_store(copies + k * 256 + tid, nbtag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (tid == 0)
+        __hip_atomic_store(genp, ((uint64_t)next << 32) | (uint64_t)~next, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     if (tid == 0) covered = 0;
     if (tid < 256) {
         // unique sort key: count first, then the smaller exponent value
@@ -439,9 +450,10 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(CalArgs a) {
     }
     __syncthreads();
     {   // rank = number of larger keys; 4 threads per exponent, 64 keys each
-        const uint64_t mine = key[bin];
+        const int bin = tid & 255, quarter = tid >> 8;
+        const uint64_t own = key[bin];
         uint32_t r = 0;
-        for (int u = quarter * 64; u < quarter * 64 + 64; ++u) r += key[u] > mine ? 1u : 0u;
+        for (int u = quarter * 64; u < quarter * 64 + 64; ++u) r += key[u] > own ? 1u : 0u;
         part[tid] = r;
     }
     __syncthreads();
@@ -730,23 +742,25 @@ __global__ __launch_bounds__(kThreads) void k_encode_sums(EncArgs a) {
     }
 }
 
-// Sum of src[0, n) and of src[0, split), 8 loads in flight per thread,
-// reduced over the workgroup (results in red[0] / red[1] after a barrier).
+// Sum of src[0, n) and of src[0, split) for this thread's share (every
+// kTailThreads-th entry), 16 loads in flight per thread: a single round
+// trip up to 4096 entries (the tile counts of a 2^25-element tensor).
 __device__ inline void sum_prefix(const uint32_t *src, uint64_t n, uint64_t split,
                                   uint64_t &before, uint64_t &all) {
     const int tid = threadIdx.x;
-    for (uint64_t k0 = 0; k0 < n; k0 += 8 * kTailThreads) {
-        uint32_t c8[8];
+    constexpr int kIn = 16;
+    for (uint64_t k0 = 0; k0 < n; k0 += kIn * kTailThreads) {
+        uint32_t c[kIn];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kIn; ++j) {
             const uint64_t k = k0 + j * kTailThreads + tid;
-            c8[j] = k < n ? src[k] : 0u;
+            c[j] = k < n ? src[k] : 0u;
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kIn; ++j) {
             const uint64_t k = k0 + j * kTailThreads + tid;
-            all += c8[j];
-            before += k < split ? c8[j] : 0u;
+            all += c[j];
+            before += k < split ? c[j] : 0u;
         }
     }
 }
@@ -1172,7 +1186,9 @@ __device__ void order_pass(const DecArgs &a, const DecItem &I, uint32_t item, co
     if (threadIdx.x == 0) {
         const uint64_t t = a.order_ticket + item;
         const uint64_t ntiles = a.tile_start[item + 1] - a.tile_start[item];
-        *last = tagged_arrive(a.order_sync + (t & (kOrderSlots - 1)), (uint32_t)t + 1u, ntiles);
+        uint64_t *c = a.order_sync + (t & (kOrderSlots - 1));
+        counter_claim(c, ld_agent(c), (uint32_t)t + 1u);   // a rare path: not hidden
+        *last = tagged_arrive(c, ntiles, (uint32_t)t + 1u);
     }
     __syncthreads();
     if (!*last) return;
@@ -1620,10 +1636,8 @@ int launch_calibrate(const CalItem *items, uint32_t count, uint8_t *ws, hipStrea
     // kCalLongLoop rounds of loads is faster with one (longer contiguous
     // ranges, half the merges: 2 % on 32 tensors of 32M elements).
     const uint64_t long_enough = kCalLongLoop * 4 * (uint64_t)kCalThreads * (uint64_t)cus;
-    uint64_t target = (uint64_t)((total >> 3) >= long_enough ? 1 : kCalTarget) * cus;
-    // every workgroup has a histogram row: at most kCalMaxWgs per launch
-    if (target > kCalMaxWgs - kMaxBatch) target = kCalMaxWgs - kMaxBatch;
-    uint32_t wg = 0, grp = 0;
+    const uint64_t target = (uint64_t)((total >> 3) >= long_enough ? 1 : kCalTarget) * cus;
+    uint32_t wg = 0;
     for (uint32_t k = 0; k < count; ++k) {
         a.it[k] = items[k];
         uint64_t g = total ? ceil_div(target * items[k].n, total) : 1;
@@ -1632,13 +1646,9 @@ int launch_calibrate(const CalItem *items, uint32_t count, uint8_t *ws, hipStrea
         if (g > kCalMaxGrid) g = kCalMaxGrid;
         if (g == 0) g = 1;
         a.wg_start[k] = wg;
-        a.grp_start[k] = grp;
         wg += (uint32_t)g;
-        if (g > (uint64_t)kCalSingle) grp += (uint32_t)ceil_div(g, kCalGroup);
     }
     a.wg_start[count] = wg;
-    a.grp_start[count] = grp;
-    if (wg > (uint32_t)kCalMaxWgs || grp > kCalGroupRows) return SPLITZIP_ERR_INTERNAL;
     a.ticket = g_ticket.fetch_add(count, std::memory_order_relaxed);
     k_calibrate<<<wg, kCalThreads, 0, s>>>(a);
     return launched();
