@@ -235,54 +235,71 @@ def slot_decode_phase(S, batch, metas_h, x_all, stream, passes):
     """In-place decode of every tensor: each payload is first copied into the
     head of the tensor's output buffer (untimed, all 64 before the timed
     region, so the payloads are not cache-resident), then the 64 slot decodes
-    are timed with HIP events on the stream they run on."""
+    are timed with HIP events on the stream they run on (the GPU kept busy
+    while the host enqueues them, so the host's marshalling is not timed):
+    one call per tensor, then all 64 as one group (32 per launch).  With the
+    library's default forms (single calls: two launches; groups: one
+    cooperative launch) and with the two-launch form forced for groups.
+    Copies and sleep on the same stream; `torch.cuda._sleep` spins 10M cycles."""
+    import os
     import torch
 
     T = len(batch.xs)
     comp = [m.comp_bytes for m in metas_h]
     stash = torch.empty(max(comp), dtype=torch.uint8, device=x_all.device)
-    slots = [o.view(torch.uint8) for o in batch.outs]
-    ms = 0.0
-    for _ in range(passes):
-        for i in range(T):
-            slots[i][: comp[i]].copy_(batch.payloads[i][: comp[i]])
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(T):
-            S.decode_slot(slots[i], batch.metas[i], batch.cbs[i], batch.ns[i], stash, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms += e0.elapsed_time(e1)
-    ms /= passes
-    assert torch.equal(torch.stack(batch.outs).view(torch.int16), x_all.view(torch.int16)), \
-        "in-place round trip failed"
-    # the same 64 slots as one group (32 per pair of launches), own stash each
     stashes = [torch.empty(c, dtype=torch.uint8, device=x_all.device) for c in comp]
-    ms_b = 0.0
-    for _ in range(passes):
-        for i in range(T):
-            slots[i][: comp[i]].copy_(batch.payloads[i][: comp[i]])
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        S.decode_slots(slots, batch.metas, batch.cbs, batch.ns, stashes, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_b += e0.elapsed_time(e1)
-    ms_b /= passes
-    assert torch.equal(torch.stack(batch.outs).view(torch.int16), x_all.view(torch.int16)), \
-        "batched in-place round trip failed"
-    del stashes
+    slots = [o.view(torch.uint8) for o in batch.outs]
+
+    def timed(grouped):
+        ms = 0.0
+        for k in range(passes + 1):   # the first pass untimed (first use of a launch form)
+            for i in range(T):
+                slots[i][: comp[i]].copy_(batch.payloads[i][: comp[i]])
+            # keep the GPU busy while the host marshals and enqueues the calls
+            torch.cuda._sleep(10_000_000)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if grouped:
+                S.decode_slots(slots, batch.metas, batch.cbs, batch.ns, stashes, stream=stream)
+            else:
+                for i in range(T):
+                    S.decode_slot(slots[i], batch.metas[i], batch.cbs[i], batch.ns[i], stash,
+                                  stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if k:
+                ms += e0.elapsed_time(e1)
+        assert torch.equal(torch.stack(batch.outs).view(torch.int16), x_all.view(torch.int16)), \
+            "in-place round trip failed"
+        return ms / passes
+
     raw = 2 * sum(batch.ns)
     alg = raw + sum(comp)
-    return {"ms": round(ms, 4), "calls": T, "raw_GBps": round(raw / ms / 1e6, 1),
-            "alg_GBps": round(alg / ms / 1e6, 1), "hbm_frac": round(alg / ms / 1e6 / 8000.0, 4),
-            "batched": {"ms": round(ms_b, 4), "launch_pairs": (T + 31) // 32,
-                        "raw_GBps": round(raw / ms_b / 1e6, 1),
-                        "alg_GBps": round(alg / ms_b / 1e6, 1),
-                        "hbm_frac": round(alg / ms_b / 1e6 / 8000.0, 4)},
-            "note": "payload at the head of the output buffer; the inputs of the tiles whose "
-                    "output overlaps it (about 0.75 of the payload) are stashed first, i.e. "
-                    "written and read once more"}
+
+    def rec(ms):
+        return {"ms": round(ms, 4), "raw_GBps": round(raw / ms / 1e6, 1),
+                "alg_GBps": round(alg / ms / 1e6, 1), "hbm_frac": round(alg / ms / 1e6 / 8000.0, 4)}
+
+    ms, ms_b = timed(False), timed(True)
+    old = os.environ.get("SPLITZIP_SLOT_LAUNCH")
+    try:
+        os.environ["SPLITZIP_SLOT_LAUNCH"] = "two"
+        ms2_b = timed(True)
+        os.environ["SPLITZIP_SLOT_LAUNCH"] = "coop"
+        msc = timed(False)
+    finally:
+        if old is None:
+            del os.environ["SPLITZIP_SLOT_LAUNCH"]
+        else:
+            os.environ["SPLITZIP_SLOT_LAUNCH"] = old
+    del stashes
+    return dict(rec(ms), calls=T, form="two launches per call",
+                batched=dict(rec(ms_b), launches=(T + 31) // 32, form="one cooperative launch per 32"),
+                batched_two_launch=rec(ms2_b), single_coop=rec(msc),
+                note="payload at the head of the output buffer; cooperative form: the inputs of "
+                     "the tiles whose output overlaps it wait in registers across a grid "
+                     "barrier (a cooperative launch costs ~14 us more than an ordinary one); "
+                     "two-launch form: they are stashed first, i.e. written and read once more")
 
 
 def h2d_pipeline(S, batch, metas_h, x_all, dev, count):

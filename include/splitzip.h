@@ -265,15 +265,19 @@ int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const spli
  *   d_dec_lut   the codebook's 16-entry dec_lut (device)
  *   d_stash     caller-owned device scratch of stash_bytes >= comp_bytes
  *               (splitzip_payload_size(n, n_esc)) bytes, 16-byte aligned, not
- *               overlapping the slot; the inputs of the tiles whose output
- *               overlaps the payload, and the escape sections, are copied
- *               there first (about three quarters of the payload)
+ *               overlapping the slot; it receives what a later step reads
+ *               after the slot head has been overwritten (see below)
  *   d_status    optional, as for splitzip_decode (escapes are re-applied from
- *               the decoded sign and mantissa)
- * Three kernels on `stream` (stash and direct decode, stashed tiles, then the
- * order-independent escape pass, which does nothing for a stream marked
- * SPLITZIP_META_ASCENDING without d_status); calls that share a stash must be
- * ordered on one stream.
+ *               the decoded sign and mantissa); bit 16 reports a grid
+ *               barrier of the cooperative form that gave up waiting (about
+ *               a second; the output is then not trustworthy)
+ * Two kernels on `stream`: the first stashes the inputs of every tile whose
+ * output overlaps the payload, and the escape sections, and decodes the
+ * other tiles; the second decodes the stashed tiles.  With d_status, a
+ * validation kernel follows.  Calls that share a stash must be ordered on
+ * one stream.  (splitzip_decode_slot_batch takes one cooperative kernel per
+ * group instead, see there; the environment variable SPLITZIP_SLOT_LAUNCH =
+ * "coop" or "two" selects either form for every call.)
  * Synchronous errors: INVALID (also for overlapping slot and stash), HIP. */
 int splitzip_decode_slot(uint8_t *d_slot, uint64_t slot_bytes, const splitzip_meta *d_meta,
                          const uint8_t *d_dec_lut, uint64_t n, uint8_t *d_stash,
@@ -282,8 +286,16 @@ int splitzip_decode_slot(uint8_t *d_slot, uint64_t slot_bytes, const splitzip_me
 /* In-place decode of a group of slots (page "SplitZip in DDO -- VMM routes",
  * "Route B (fallback)": the staging route expands the slots of an execution
  * group after their upload, on the upload stream): the
- * same result as splitzip_decode_slot on every item in order, with up to 32
- * items sharing each pair of launches.  Each item needs its own stash; no
+ * same result as splitzip_decode_slot on every item in order.  Where the
+ * device supports cooperative launches, up to 32 items share one cooperative
+ * kernel: for each item, every workgroup holds the inputs of up to three whole
+ * tiles whose output overlaps the payload in registers, decodes the tiles
+ * past the payload, and writes the held tiles after a grid barrier (one
+ * item's stores overlap the next one's loads); overlapping tiles beyond that
+ * reach, and a partial last one, go through the stash, and so do the escape
+ * sections when a later step needs them (validation, an unmarked stream,
+ * stashed tiles).  A group of one item, or a device without cooperative
+ * launches, takes the two-kernel form.  Each item needs its own stash; no
  * slot or stash may overlap another item's buffers.  d_status (optional)
  * collects the status bits of all items.
  * Synchronous errors: INVALID (any item; nothing is enqueued), HIP. */

@@ -32,6 +32,7 @@ DEC_BAD_META = 1
 DEC_ESC_OUT_OF_RANGE = 2
 DEC_POS_GE_CHUNK = 4
 DEC_NOT_INCREASING = 8
+DEC_BARRIER_TIMEOUT = 16       # cooperative in-place decode only
 
 
 class Codebook(ctypes.Structure):

@@ -203,7 +203,7 @@ def decode_slot(slot: torch.Tensor, meta: torch.Tensor, cb_or_dec_lut: torch.Ten
 def decode_slots(slots, metas, cbs_or_luts, ns, stashes, status: torch.Tensor | None = None,
                  stream=None):
     """In-place decode of a group of slots (see ``decode_slot``), up to 32
-    per pair of launches.  Returns the flat bfloat16 views of the slots."""
+    per launch.  Returns the flat bfloat16 views of the slots."""
     count = len(slots)
     if not (len(metas) == len(cbs_or_luts) == len(ns) == len(stashes) == count):
         raise ValueError("one meta, codebook, size and stash per slot")

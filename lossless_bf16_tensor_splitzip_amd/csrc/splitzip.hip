@@ -58,6 +58,8 @@
 #include <atomic>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "splitzip.h"
 
@@ -1464,6 +1466,529 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_slot_finish(DecArgs a) {
     decode_tile<kDecThreads, kDecUnits, kSlotFinish>(a);
 }
 
+// ---------------------------------------------------------------------------
+// In-place decode in one cooperative launch (page 1, decode_slot_into; page
+// "SplitZip in DDO -- VMM routes", the CUDA route's expansion in place)
+// ---------------------------------------------------------------------------
+//
+// Tile t writes slot bytes [2tT, 2(t+1)T) (T = 8192 elements); the tiles from
+// t_split = ceil(comp / 2T) on write only past the payload.  In a grid that
+// is resident as a whole (cooperative launch), every workgroup first decodes
+// its tiles from t_split on, then loads the pk/sm inputs of its tiles wg +
+// jG below t_split (j < kHold) into registers, their escape entries having
+// gone to LDS; after a grid barrier it writes the held tiles straight from
+// the registers, then their escapes.  After the barrier a workgroup reads no
+// slot byte and only the stash bytes it wrote itself, so the barrier needs
+// no cache flush: it only has to order the held tiles' stores after every
+// load of the first phase.  Overlapping tiles beyond the registers' reach
+// (more than kHold * G of them), and a partial last one, go through the
+// stash as in the two-launch form.  A group of slots takes one barrier per
+// slot, the stores of one slot overlapping the loads of the next.  A stream
+// not marked ascending takes a second barrier (with device-scope fences) and
+// an order-independent pass over all its escapes, read back from the stash.
+// Compared with the two-launch form, the held tiles' inputs never go through
+// memory a second time; a cooperative launch costs about 14 us more than an
+// ordinary one, so only groups of slots take this form.
+constexpr int kHold = 3;                   // held tiles per workgroup and tensor
+constexpr uint32_t kHoldEsc = 512;         // escape entries per held tile in LDS
+constexpr uint32_t kCoopSpin = 1u << 20;   // barrier: polls before giving up (about a second)
+constexpr int kCoopTile = kDecThreads * kUnit * kDecUnits;   // 8192 elements
+constexpr int kCoopUnits = kCoopTile / kUnit;                // 8-element units per tile
+static_assert(kHold <= kDecThreads / 64, "one wave finds each held tile's escapes");
+
+struct CoopLds {
+    uint32_t pair_lut[256];
+    uint32_t tile[kCoopTile / 2];          // one decoded tile
+    uint32_t esc[kHold][kHoldEsc];         // (position << 16) | (sign, mantissa << 8) | exponent, or ~0
+    uint64_t hr0[kHold], hr1[kHold];       // escape ranks of the held tiles
+    uint64_t dr0, dr1;                     // escape ranks of a direct tile
+};
+
+// Grid barrier of the cooperative decode.  Same-address atomics serialise
+// at the memory side, so the grid arrives in two levels: workgroups on the
+// counter of their group of kCoopGroup, the last of each group on the top
+// counter; the last arrival of a round writes the round's release word to
+// every group's flag, and each group polls only its own flag.  Counters and
+// flags are tagged ((tag << 32) | count, see tagged_claim): a call takes a
+// block of them by its ticket and claims what it increments, so nothing is
+// cleared between calls; after its last barrier every workgroup arrives once
+// more, and the last of those arrivals puts the block back to (tag << 32)
+// so that a replay of the same arguments starts from zero.
+constexpr uint32_t kCoopGroup = 16;                        // workgroups per group counter
+constexpr uint32_t kCoopMaxGrid = 4096;
+constexpr uint32_t kCoopGroups = kCoopMaxGrid / kCoopGroup;
+constexpr uint32_t kCoopLine = 16;                         // words per counter (128 bytes)
+constexpr uint32_t kCoopWords = (2 * kCoopGroups + 1) * kCoopLine;
+constexpr uint32_t kCoopBlocks = 16;                       // calls in flight with distinct blocks
+__device__ __align__(256) uint64_t g_coop_sync[kCoopBlocks * kCoopWords];
+
+struct CoopBar {
+    uint64_t *blk;        // the call's block: group counters, group flags, top counter
+    uint32_t tag, passed;
+};
+
+__device__ inline uint32_t coop_ngroups() { return (gridDim.x + kCoopGroup - 1) / kCoopGroup; }
+
+__device__ inline uint64_t *coop_grp(const CoopBar &b, uint32_t g) { return b.blk + g * kCoopLine; }
+__device__ inline uint64_t *coop_flag(const CoopBar &b, uint32_t g) {
+    return b.blk + (kCoopGroups + g) * kCoopLine;
+}
+__device__ inline uint64_t *coop_top(const CoopBar &b) { return b.blk + 2 * kCoopGroups * kCoopLine; }
+
+// Claims this workgroup's group counter (and, for the first workgroup of a
+// group, the top counter: every arrival on it follows the arrival of some
+// group's first workgroup, which claimed it before arriving).
+__device__ inline void coop_bar_init(CoopBar &b, uint64_t *blk, uint32_t tag) {
+    b.blk = blk;
+    b.tag = tag;
+    b.passed = 0;
+    if (threadIdx.x == 0) {
+        uint64_t *c = coop_grp(b, blockIdx.x / kCoopGroup);
+        counter_claim(c, ld_agent(c), tag);
+        if (blockIdx.x % kCoopGroup == 0) counter_claim(coop_top(b), ld_agent(coop_top(b)), tag);
+    }
+}
+
+// Arrival of this workgroup for round `round` (thread 0); true for the last
+// arrival of the round over the whole grid.
+__device__ inline bool coop_arrive(const CoopBar &b, uint32_t round) {
+    const uint32_t group = blockIdx.x / kCoopGroup;
+    const uint32_t gsize = min(kCoopGroup, gridDim.x - group * kCoopGroup);
+    const uint64_t p = __hip_atomic_fetch_add(coop_grp(b, group), 1ull, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)p + 1u != gsize * round) return false;
+    const uint64_t q = __hip_atomic_fetch_add(coop_top(b), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (uint32_t)q + 1u == coop_ngroups() * round;
+}
+
+// Every workgroup is resident (cooperative launch), so the wait ends; it is
+// bounded anyway and sets status bit 16 when the bound trips.
+__device__ inline void coop_barrier(CoopBar &b, int32_t *status, bool fence) {
+    if (fence) __threadfence();
+    wait_vector_memory();
+    __syncthreads();
+    ++b.passed;
+    const uint64_t want = ((uint64_t)b.tag << 32) | b.passed;
+    if (threadIdx.x < 64) {
+        const int last = threadIdx.x == 0 ? (int)coop_arrive(b, b.passed) : 0;
+        if (__shfl(last, 0, 64))
+            for (uint32_t g = threadIdx.x; g < coop_ngroups(); g += 64)
+                __hip_atomic_store(coop_flag(b, g), want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) {
+            const uint64_t *f = coop_flag(b, blockIdx.x / kCoopGroup);
+            uint32_t k = 0;
+            for (;;) {
+                const uint64_t v = ld_agent(f);
+                if ((v >> 32) == b.tag && (uint32_t)v >= b.passed) break;
+                if (++k > kCoopSpin) {
+                    if (status) atomicOr(status, 16);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+    }
+    __syncthreads();
+    if (fence) __threadfence();
+}
+
+// The final arrival; the last one puts the block back for a replay.
+__device__ inline void coop_leave(CoopBar &b) {
+    wait_vector_memory();
+    __syncthreads();
+    if (threadIdx.x == 0 && coop_arrive(b, b.passed + 1)) {
+        const uint64_t z = (uint64_t)b.tag << 32;
+        for (uint32_t g = 0; g < coop_ngroups(); ++g) {
+            __hip_atomic_store(coop_grp(b, g), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(coop_flag(b, g), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __hip_atomic_store(coop_top(b), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Dense values of the first cnt < T elements of a tile into the LDS tile,
+// element by element (pk bytes from pkb, sm bytes from smb).
+__device__ inline void decode_partial_lds(const uint8_t *pkb, const uint8_t *smb, uint32_t cnt,
+                                          const uint32_t *pair_lut, uint32_t *tile, uint32_t tid) {
+    uint16_t *t16 = reinterpret_cast<uint16_t *>(tile);
+    for (uint32_t i = tid; i < cnt; i += kDecThreads) {
+        const uint32_t ee = pair_lut[pkb[i / 2]];
+        t16[i] = (uint16_t)join16(smb[i], (i & 1) ? ee >> 16 : ee & 0xFFu);
+    }
+}
+
+// Dense values of one unit (pair table in LDS): its 8 BF16 bit patterns.
+__device__ __forceinline__ u32x4 decode_unit(const uint32_t *pair_lut, uint32_t p, u32x2 m) {
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t ee = pair_lut[(p >> (8 * k)) & 0xFFu];
+        const uint32_t s = m[k >> 1] >> (16 * (k & 1));
+        o[k] = join16(s & 0xFFu, ee & 0xFFu) | (join16((s >> 8) & 0xFFu, ee >> 16) << 16);
+    }
+    return o;
+}
+
+// ... into the LDS tile at element l0.
+__device__ __forceinline__ void decode_unit_lds(const uint32_t *pair_lut, uint32_t p, u32x2 m,
+                                                uint32_t *tile, uint32_t l0) {
+    *reinterpret_cast<u32x4 *>(tile + l0 / 2) = decode_unit(pair_lut, p, m);
+}
+
+// The dense values of a whole tile, from registers straight to out[0, T).
+__device__ __forceinline__ void store_units(const uint32_t *pair_lut, const uint32_t (&p)[kDecUnits],
+                                            const u32x2 (&m)[kDecUnits], uint16_t *out, uint32_t tid) {
+#pragma unroll
+    for (int u = 0; u < kDecUnits; ++u)
+        __builtin_nontemporal_store(decode_unit(pair_lut, p[u], m[u]),
+                                    reinterpret_cast<u32x4 *>(out + (u * kDecThreads + tid) * kUnit));
+}
+
+// The LDS tile to out[0, cnt).
+__device__ __forceinline__ void store_tile(const uint32_t *tile, uint16_t *out, uint32_t cnt,
+                                           uint32_t tid) {
+    if (cnt == kCoopTile) {
+#pragma unroll
+        for (int u = 0; u < kDecUnits; ++u) {
+            const uint32_t l0 = (u * kDecThreads + tid) * kUnit;
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(tile + l0 / 2),
+                                        reinterpret_cast<u32x4 *>(out + l0));
+        }
+    } else {
+        const uint16_t *t16 = reinterpret_cast<const uint16_t *>(tile);
+        for (uint32_t i = tid; i < cnt; i += kDecThreads) out[i] = t16[i];
+    }
+}
+
+// Escape ranks [r0, r1) of the chunks that hold the tile at element base
+// (one wave; the stream ascending).
+__device__ inline void tile_escape_range(const int32_t *cid, uint64_t e, uint64_t n, uint32_t chunk,
+                                         uint64_t base, uint64_t &r0, uint64_t &r1) {
+    const int lane = threadIdx.x & 63;
+    uint64_t c0, c1, nchunks;
+    uint32_t p0, p1, pn;
+    chunk_split(base, chunk, c0, p0);
+    chunk_split(base + kCoopTile - 1, chunk, c1, p1);
+    chunk_split(n - 1, chunk, nchunks, pn);
+    ++c1;
+    ++nchunks;
+    if (c1 > nchunks) c1 = nchunks;
+    const double per_chunk = (double)e / (double)nchunks;
+    r0 = lower_bound_wave(cid, 0, e, (int64_t)c0, (uint64_t)(per_chunk * (double)c0), lane);
+    r1 = lower_bound_wave(cid, r0, e, (int64_t)c1, r0 + (uint64_t)(per_chunk * (double)(c1 - c0)), lane);
+}
+
+// Applies the escapes of ranks [r0, r1) that fall in the LDS tile at element base.
+__device__ inline void patch_tile_lds(uint32_t *tile, const int32_t *cid, const uint16_t *lpos,
+                                      const uint8_t *ev, uint64_t r0, uint64_t r1, uint32_t chunk,
+                                      uint64_t base, uint32_t tid) {
+    uint16_t *t16 = reinterpret_cast<uint16_t *>(tile);
+    for (uint64_t r = r0 + tid; r < r1; r += kDecThreads) {
+        const int64_t v = (int64_t)cid[r] * chunk + lpos[r] - (int64_t)base;
+        if (v >= 0 && v < kCoopTile) t16[v] = (uint16_t)((t16[v] & 0x807Fu) | ((uint32_t)ev[r] << 7));
+    }
+}
+
+// Escapes of the LDS tile at element base (ranks found by wave 0 in the
+// ascending stream cid/lpos/ev), then the tile to out[base, base + cnt).
+__device__ inline void finish_tile(CoopLds &sh, bool patch, const int32_t *cid, const uint16_t *lpos,
+                                   const uint8_t *ev, uint64_t e, uint64_t n, uint32_t chunk,
+                                   uint64_t base, uint32_t cnt, uint16_t *out, uint32_t tid) {
+    if (patch && tid < 64) {
+        uint64_t r0, r1;
+        tile_escape_range(cid, e, n, chunk, base, r0, r1);
+        if (tid == 0) {
+            sh.dr0 = r0;
+            sh.dr1 = r1;
+        }
+    }
+    __syncthreads();
+    if (patch) {
+        patch_tile_lds(sh.tile, cid, lpos, ev, sh.dr0, sh.dr1, chunk, base, tid);
+        __syncthreads();
+    }
+    store_tile(sh.tile, out + base, cnt, tid);
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kDecThreads) void k_decode_slot_coop(DecArgs a) {
+    __shared__ CoopLds sh;
+    // the call's barrier block (order_sync) and tag (order_ticket + 1)
+    CoopBar bar;
+    coop_bar_init(bar, a.order_sync, (uint32_t)a.order_ticket + 1u);
+
+#pragma unroll 1
+    for (uint32_t item = 0; item < a.count; ++item) {
+        // Fresh copies of the ids for every tensor keep the compiler from
+        // hoisting the addresses of every held unit out of the loop (they
+        // would take the registers the held tiles need).
+        uint32_t tid = threadIdx.x, wg = blockIdx.x, G = gridDim.x;
+        asm volatile("" : "+v"(tid), "+s"(wg), "+s"(G));
+        const DecItem I = a.it[item];
+        if (I.n == 0) continue;
+        Layout L;
+        if (!meta_ok(I, L) || L.total > I.other_bytes) {   // payload fits slot and stash
+            if (wg == 0 && tid == 0 && a.status) atomicOr(a.status, 1);
+            continue;
+        }
+        const uint64_t e = I.meta->n_esc;
+        const uint32_t chunk = (uint32_t)I.meta->chunk_size;
+        const bool ascending = (I.meta->flags & SPLITZIP_META_ASCENDING) != 0;
+        const bool patch = e && ascending;   // escapes applied tile by tile
+        // A tensor whose escapes average more than 512 per tile is patched
+        // tile by tile in LDS; a sparser one has its dense values stored
+        // straight from registers and its escapes stored after them.
+        const bool in_lds = patch && e * (uint64_t)kCoopTile > (uint64_t)kHoldEsc * I.n;
+        const Layout L0 = layout_of(I.n, 0);
+        const uint32_t *pk = reinterpret_cast<const uint32_t *>(I.payload);
+        const u32x2 *sm = reinterpret_cast<const u32x2 *>(I.payload + L0.off_sm);
+        const uint8_t *sm8 = I.payload + L0.off_sm;
+        const int32_t *cid = reinterpret_cast<const int32_t *>(I.payload + L.off_cid);
+        const uint16_t *lpos = reinterpret_cast<const uint16_t *>(I.payload + L.off_lpos);
+        const uint8_t *ev = I.payload + L.off_ev;
+        const int32_t *scid = reinterpret_cast<const int32_t *>(I.stash + L.off_cid);
+        const uint16_t *slpos = reinterpret_cast<const uint16_t *>(I.stash + L.off_lpos);
+        const uint8_t *sev = I.stash + L.off_ev;
+        const uint64_t tiles = (I.n + kCoopTile - 1) / kCoopTile;
+        const uint64_t t_split = slot_split(L.total, tiles, kCoopTile);
+        // Tiles below t_split: tile wg + jG is held in registers for j <
+        // kHold when it is whole; the others (beyond the registers' reach,
+        // or the partial last tile) go through the stash, copied and read
+        // back by the same workgroup.
+        const uint32_t last_cnt = (uint32_t)(I.n - (tiles - 1) * kCoopTile);
+        const bool part_held = last_cnt < kCoopTile && tiles - 1 < t_split;
+        const uint64_t t_whole = part_held ? tiles - 1 : t_split;   // whole tiles below t_split
+        const uint64_t reach = (uint64_t)kHold * G;
+        const bool mine_part = part_held && (tiles - 1) % G == wg;
+        // Stashed tiles search and patch their escapes after the barrier,
+        // from the stash: then the escape sections go there first, and the
+        // barrier makes every workgroup's copy visible.
+        const bool stashed = part_held || t_whole > reach;
+        const bool esc_to_stash = a.status || (e && (!ascending || stashed));
+
+        // ---- phase 1: the stashed tiles' inputs, the held tiles' escape
+        // entries, the escape sections when a later pass reads them, the
+        // direct tiles, then the held tiles' inputs
+        for (uint64_t t = wg + reach; t < t_whole; t += G) {
+            const uint64_t k0 = t * kCoopUnits;
+            uint32_t *spk = reinterpret_cast<uint32_t *>(I.stash);
+            u32x2 *ssm = reinterpret_cast<u32x2 *>(I.stash + L0.off_sm);
+#pragma unroll
+            for (int u = 0; u < kDecUnits; ++u) {
+                const uint64_t k = k0 + u * kDecThreads + tid;
+                spk[k] = __builtin_nontemporal_load(pk + k);
+                ssm[k] = __builtin_nontemporal_load(sm + k);
+            }
+        }
+        if (mine_part) {   // the partial tile's inputs, at their payload offsets
+            const uint64_t base = (tiles - 1) * kCoopTile;
+            for (uint32_t i = tid; i < last_cnt; i += kDecThreads) {
+                I.stash[L0.off_sm + base + i] = I.payload[L0.off_sm + base + i];
+                if (!(i & 1)) I.stash[(base + i) / 2] = I.payload[(base + i) / 2];
+            }
+        }
+        __syncthreads();   // the previous tensor's last reads of LDS
+        if (tid < 256)
+            sh.pair_lut[tid] = (uint32_t)I.dec_lut[(tid >> 4) & 15] | ((uint32_t)I.dec_lut[tid & 15] << 16);
+        if (patch && (tid >> 6) < kHold) {   // wave j: the escapes of held tile j
+            const uint32_t wave = tid >> 6, lane = tid & 63;
+            const uint64_t t = wg + (uint64_t)wave * G;
+            const uint64_t base = t * kCoopTile;
+            uint64_t r0 = 0, r1 = 0;
+            if (t < t_whole) tile_escape_range(cid, e, I.n, chunk, base, r0, r1);
+            if (lane == 0) {
+                sh.hr0[wave] = r0;
+                sh.hr1[wave] = r1;
+            }
+            // (position << 16) | (sign and mantissa << 8) | exponent
+            if (r1 - r0 <= kHoldEsc)
+                for (uint64_t r = r0 + lane; r < r1; r += 64) {
+                    const int64_t v = (int64_t)cid[r] * chunk + lpos[r] - (int64_t)base;
+                    sh.esc[wave][r - r0] = (v >= 0 && v < kCoopTile)
+                                               ? ((uint32_t)v << 16) | ((uint32_t)sm8[base + v] << 8) | ev[r]
+                                               : ~0u;
+                }
+        }
+        __syncthreads();
+        if (esc_to_stash) {
+            // the escape sections, for the stashed tiles, the validation
+            // pass or the order-independent pass
+            const uint64_t bytes = L.total - L.off_cid;
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(I.payload + L.off_cid);
+            uint32_t *dst = reinterpret_cast<uint32_t *>(I.stash + L.off_cid);
+            for (uint64_t w = (uint64_t)wg * kDecThreads + tid; w < bytes / 4; w += (uint64_t)G * kDecThreads)
+                dst[w] = src[w];
+            if (wg == 0 && tid < (uint32_t)(bytes & 3)) {
+                const uint64_t b = L.off_cid + (bytes & ~uint64_t(3)) + tid;
+                I.stash[b] = I.payload[b];
+            }
+        }
+        if (patch) {
+            // held tiles with many escapes: their entries to the stash, read
+            // back after the barrier by this workgroup
+            for (int j = 0; j < kHold; ++j) {
+                const uint64_t r0 = sh.hr0[j], r1 = sh.hr1[j];
+                if (r1 - r0 <= kHoldEsc) continue;
+                for (uint64_t r = r0 + tid; r < r1; r += kDecThreads) {
+                    reinterpret_cast<int32_t *>(I.stash + L.off_cid)[r] = cid[r];
+                    reinterpret_cast<uint16_t *>(I.stash + L.off_lpos)[r] = lpos[r];
+                    I.stash[L.off_ev + r] = ev[r];
+                }
+            }
+        }
+        // direct tiles: their output lies past the payload.  Whole tiles of
+        // a sparse tensor: dense values straight to memory, then the escapes.
+        const uint64_t t_dl = in_lds ? t_split : (last_cnt < kCoopTile ? tiles - 1 : tiles);
+        for (uint64_t t = t_split + wg; t < t_dl; t += G) {
+            const uint64_t base = t * kCoopTile;
+            const uint32_t *pkt = pk + t * kCoopUnits;
+            const u32x2 *smt = sm + t * kCoopUnits;
+            uint32_t p[kDecUnits];
+            u32x2 m[kDecUnits];
+#pragma unroll
+            for (int u = 0; u < kDecUnits; ++u) {
+                p[u] = __builtin_nontemporal_load(pkt + u * kDecThreads + tid);
+                m[u] = __builtin_nontemporal_load(smt + u * kDecThreads + tid);
+            }
+            store_units(sh.pair_lut, p, m, I.out + base, tid);
+            if (patch) {
+                if (tid < 64) {
+                    uint64_t r0, r1;
+                    tile_escape_range(cid, e, I.n, chunk, base, r0, r1);
+                    if (tid == 0) {
+                        sh.dr0 = r0;
+                        sh.dr1 = r1;
+                    }
+                }
+                __syncthreads();   // (also orders the dense stores before the patches)
+                for (uint64_t r = sh.dr0 + tid; r < sh.dr1; r += kDecThreads) {
+                    const int64_t v = (int64_t)cid[r] * chunk + lpos[r] - (int64_t)base;
+                    if (v >= 0 && v < kCoopTile) I.out[base + v] = (uint16_t)join16(sm8[base + v], ev[r]);
+                }
+                __syncthreads();
+            }
+        }
+        // the rest (a dense tensor's tiles, the partial last tile) through LDS
+        for (uint64_t t = t_split + wg; t < tiles; t += G) {
+            if (t < t_dl) continue;
+            const uint64_t base = t * kCoopTile;
+            const uint32_t cnt = t == tiles - 1 ? last_cnt : kCoopTile;
+            if (cnt == kCoopTile) {
+                const uint32_t *pkt = pk + t * kCoopUnits;
+                const u32x2 *smt = sm + t * kCoopUnits;
+#pragma unroll
+                for (int u = 0; u < kDecUnits; ++u)
+                    decode_unit_lds(sh.pair_lut, __builtin_nontemporal_load(pkt + u * kDecThreads + tid),
+                                    __builtin_nontemporal_load(smt + u * kDecThreads + tid), sh.tile,
+                                    (u * kDecThreads + tid) * kUnit);
+            } else {
+                decode_partial_lds(I.payload + base / 2, sm8 + base, cnt, sh.pair_lut, sh.tile, tid);
+            }
+            finish_tile(sh, patch, cid, lpos, ev, e, I.n, chunk, base, cnt, I.out, tid);
+        }
+        // the held tiles' inputs last: their registers are live only across
+        // the barrier
+        uint32_t hpk[kHold][kDecUnits];
+        u32x2 hsm[kHold][kDecUnits];
+#pragma unroll
+        for (int j = 0; j < kHold; ++j) {
+            const uint64_t t = wg + (uint64_t)j * G;
+            // (defined on both paths, so that no register stays live
+            // across the loop over tensors)
+#pragma unroll
+            for (int u = 0; u < kDecUnits; ++u) {
+                hpk[j][u] = 0;
+                hsm[j][u] = u32x2{0u, 0u};
+            }
+            if (t < t_whole) {
+                const uint32_t *pkt = pk + t * kCoopUnits;
+                const u32x2 *smt = sm + t * kCoopUnits;
+#pragma unroll
+                for (int u = 0; u < kDecUnits; ++u) {
+                    hpk[j][u] = __builtin_nontemporal_load(pkt + u * kDecThreads + tid);
+                    hsm[j][u] = __builtin_nontemporal_load(smt + u * kDecThreads + tid);
+                }
+            }
+        }
+        coop_barrier(bar, a.status, esc_to_stash && patch && stashed);
+
+        // ---- phase 2: the held tiles (dense values straight from the
+        // registers, or through LDS for a tile with many escapes), their
+        // escapes, then the stashed tiles
+#pragma unroll
+        for (int j = 0; j < kHold; ++j) {
+            const uint64_t t = wg + (uint64_t)j * G;
+            if (t >= t_whole) break;
+            const uint64_t base = t * kCoopTile;
+            if (!patch || sh.hr1[j] - sh.hr0[j] <= kHoldEsc) {
+                store_units(sh.pair_lut, hpk[j], hsm[j], I.out + base, tid);
+                continue;
+            }
+#pragma unroll
+            for (int u = 0; u < kDecUnits; ++u)
+                decode_unit_lds(sh.pair_lut, hpk[j][u], hsm[j][u], sh.tile, (u * kDecThreads + tid) * kUnit);
+            __syncthreads();
+            // entries this workgroup copied to the stash
+            patch_tile_lds(sh.tile, scid, slpos, sev, sh.hr0[j], sh.hr1[j], chunk, base, tid);
+            __syncthreads();
+            store_tile(sh.tile, I.out + base, kCoopTile, tid);
+            __syncthreads();
+        }
+        if (patch) {
+            __syncthreads();   // the dense stores before the escapes' stores
+            for (int j = 0; j < kHold; ++j) {
+                const uint64_t t = wg + (uint64_t)j * G;
+                const uint64_t c = sh.hr1[j] - sh.hr0[j];
+                if (t >= t_whole || c > kHoldEsc) continue;
+                uint16_t *o = I.out + t * kCoopTile;
+                for (uint32_t k = tid; k < (uint32_t)c; k += kDecThreads) {
+                    const uint32_t w = sh.esc[j][k];
+                    if (w != ~0u) o[w >> 16] = (uint16_t)join16((w >> 8) & 0xFFu, w & 0xFFu);
+                }
+            }
+        }
+        if (stashed) {
+            for (uint64_t t = wg + reach; t < t_whole; t += G) {
+                const uint32_t *spk = reinterpret_cast<const uint32_t *>(I.stash) + t * kCoopUnits;
+                const u32x2 *ssm = reinterpret_cast<const u32x2 *>(I.stash + L0.off_sm) + t * kCoopUnits;
+                uint32_t p[kDecUnits];
+                u32x2 m[kDecUnits];
+#pragma unroll
+                for (int u = 0; u < kDecUnits; ++u) {
+                    p[u] = __builtin_nontemporal_load(spk + u * kDecThreads + tid);
+                    m[u] = __builtin_nontemporal_load(ssm + u * kDecThreads + tid);
+                }
+                __syncthreads();   // LDS tile free
+#pragma unroll
+                for (int u = 0; u < kDecUnits; ++u)
+                    decode_unit_lds(sh.pair_lut, p[u], m[u], sh.tile, (u * kDecThreads + tid) * kUnit);
+                finish_tile(sh, patch, scid, slpos, sev, e, I.n, chunk, t * kCoopTile, kCoopTile, I.out,
+                            tid);
+            }
+            if (mine_part) {
+                const uint64_t base = (tiles - 1) * kCoopTile;
+                __syncthreads();
+                decode_partial_lds(I.stash + base / 2, I.stash + L0.off_sm + base, last_cnt, sh.pair_lut,
+                                   sh.tile, tid);
+                finish_tile(sh, patch, scid, slpos, sev, e, I.n, chunk, base, last_cnt, I.out, tid);
+            }
+        }
+        if (e && !ascending) {
+            coop_barrier(bar, a.status, true);
+            // every escape, in any order, from the stash; the sign and
+            // mantissa from the decoded value
+            for (uint64_t r = (uint64_t)wg * kDecThreads + tid; r < e; r += (uint64_t)G * kDecThreads) {
+                const int32_t c = scid[r];
+                if (c < 0) continue;
+                const uint64_t idx = (uint64_t)c * chunk + slpos[r];
+                if (idx >= I.n) continue;
+                I.out[idx] = (uint16_t)join16(sm_of16(I.out[idx]), sev[r]);
+            }
+        }
+    }
+    coop_leave(bar);
+}
+
 // Validation (and order-independent re-application) of every escape, only
 // when a status word is requested.  The sign and mantissa come from the
 // payload, or, after a slot decode (whose stash holds only part of the sm
@@ -1532,6 +2057,29 @@ bool cu_count(int &cus) {
     return true;
 }
 
+// Workgroups of the cooperative slot decode that the current device keeps
+// resident at once, cached per device (-1: no cooperative launch).
+std::atomic<int> g_coop_grid[kMaxDevices];
+
+bool coop_grid(uint32_t &grid) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+    int g = dev < kMaxDevices ? g_coop_grid[dev].load(std::memory_order_relaxed) : 0;
+    if (g == 0) {
+        int coop = 0, per_cu = 0, cus = 0;
+        if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
+            !cu_count(cus) ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_slot_coop, kDecThreads, 0) !=
+                hipSuccess)
+            return false;
+        g = coop && per_cu > 0 ? per_cu * cus : -1;
+        if (g > (int)kCoopMaxGrid) g = (int)kCoopMaxGrid;
+        if (dev < kMaxDevices) g_coop_grid[dev].store(g, std::memory_order_relaxed);
+    }
+    grid = g > 0 ? (uint32_t)g : 0u;
+    return true;
+}
+
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // The current device's address of g_order_sync (each device holds its own
@@ -1578,6 +2126,24 @@ bool order_counters(DecArgs &a, uint32_t count) {
     }
     a.order_sync = p;
     a.order_ticket = g_ticket.fetch_add(count, std::memory_order_relaxed);
+    return true;
+}
+
+// The barrier block of a cooperative slot decode: blocks go round by ticket.
+std::atomic<uint64_t *> g_coop_pool[kMaxDevices];
+
+bool coop_block(DecArgs &a) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+    uint64_t *p = dev < kMaxDevices ? g_coop_pool[dev].load(std::memory_order_relaxed) : nullptr;
+    if (!p) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(g_coop_sync)) != hipSuccess || !q) return false;
+        p = static_cast<uint64_t *>(q);
+        if (dev < kMaxDevices) g_coop_pool[dev].store(p, std::memory_order_relaxed);
+    }
+    a.order_ticket = g_ticket.fetch_add(1, std::memory_order_relaxed);
+    a.order_sync = p + (a.order_ticket % kCoopBlocks) * kCoopWords;
     return true;
 }
 
@@ -1746,7 +2312,6 @@ int launch_decode_slot(const splitzip_slot_item *items, uint32_t count, int32_t 
     DecArgs a{};
     a.count = count;
     a.status = status;
-    if (!order_counters(a, count)) return SPLITZIP_ERR_HIP;
     uint64_t tiles = 0, n_all = 0;
     for (uint32_t k = 0; k < count; ++k) {
         const splitzip_slot_item &I = items[k];
@@ -1758,16 +2323,37 @@ int launch_decode_slot(const splitzip_slot_item *items, uint32_t count, int32_t 
     }
     a.tile_start[count] = tiles;
     if (tiles == 0) return SPLITZIP_OK;
-    k_decode_slot_stage<<<(unsigned)tiles, kDecThreads, 0, s>>>(a);
-    if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
+    // A group of two or more slots takes one cooperative launch where the
+    // device has them: a cooperative launch costs about 17 us more than an
+    // ordinary one, more than a single slot gains from it.  The environment
+    // variable SPLITZIP_SLOT_LAUNCH = "two" or "coop" selects either form for
+    // every call.
+    uint32_t grid = 0;
+    const char *form = getenv("SPLITZIP_SLOT_LAUNCH");
+    const bool two = form && strcmp(form, "two") == 0;
+    const bool coop = form && strcmp(form, "coop") == 0;
+    if (!two && (coop || count >= 2) && !coop_grid(grid)) return SPLITZIP_ERR_HIP;
+    if (grid) {
+        if (!coop_block(a)) return SPLITZIP_ERR_HIP;
+        void *args[] = {&a};
+        if (hipLaunchCooperativeKernel(reinterpret_cast<const void *>(k_decode_slot_coop), dim3(grid),
+                                       dim3(kDecThreads), args, 0, s) != hipSuccess)
+            return SPLITZIP_ERR_HIP;
+    } else {
+        if (!order_counters(a, count)) return SPLITZIP_ERR_HIP;
+        k_decode_slot_stage<<<(unsigned)tiles, kDecThreads, 0, s>>>(a);
+        if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
+    }
     for (uint32_t k = 0; k < count; ++k) {
         a.it[k].payload = items[k].stash;
         a.it[k].payload_bytes = items[k].stash_bytes;
         a.it[k].stash = nullptr;
         a.it[k].other_bytes = items[k].slot_bytes;
     }
-    k_decode_slot_finish<<<(unsigned)tiles, kDecThreads, 0, s>>>(a);
-    if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
+    if (!grid) {
+        k_decode_slot_finish<<<(unsigned)tiles, kDecThreads, 0, s>>>(a);
+        if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
+    }
     if (status) {
         uint64_t cgrid = ceil_div(n_all, 16 * kThreads);
         if (cgrid > 1024) cgrid = 1024;

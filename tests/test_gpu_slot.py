@@ -26,6 +26,15 @@ def setup_module(module):
     S.lib()
 
 
+@pytest.fixture(params=["coop", "two"])
+def form(request, monkeypatch):
+    """Launch form of the in-place decode, forced for every call: one
+    cooperative launch (by default only groups of slots take it) or the
+    two-launch form (by default single slots)."""
+    monkeypatch.setenv("SPLITZIP_SLOT_LAUNCH", request.param)
+    return request.param
+
+
 def slot_for(payload: bytes, n: int, extra: int = 0) -> torch.Tensor:
     size = max(2 * n, S.payload_size(n, 0), len(payload)) + extra
     slot = torch.full((size,), FILL, dtype=torch.uint8)
@@ -78,18 +87,18 @@ SIZES = [1, 2, 3, 7, 8, 9, 1023, 1025, 4095, 8191, 8192, 8193, 2 * TILE, 2 * TIL
 
 
 @pytest.mark.parametrize("n", SIZES)
-def test_slot_gaussian(n):
+def test_slot_gaussian(n, form):
     check_slot(W.gaussian_weight(n, seed=100 + n % 97), "gaussian")
 
 
 @pytest.mark.parametrize("n", [1, 9, 8193, 3 * TILE + 77, 65_537])
-def test_slot_escape_heavy(n):
+def test_slot_escape_heavy(n, form):
     # most exponents escape: the payload is longer than the tensor's 2n bytes
     check_slot(W.log_uniform_stress(n, seed=200 + n % 89), "escape heavy")
 
 
 @pytest.mark.parametrize("n,esc_every", [(16 * TILE, 40), (16 * TILE + 3, 7), (40 * TILE, 3)])
-def test_slot_split_positions(n, esc_every):
+def test_slot_split_positions(n, esc_every, form):
     """Escape densities that move the first directly decoded tile."""
     b = host_bits(W.gaussian_weight(n, seed=300 + esc_every)).copy()
     k = np.arange(0, n, esc_every)
@@ -99,7 +108,7 @@ def test_slot_split_positions(n, esc_every):
     check_slot(x, "esc every %d" % esc_every, extra=12345)
 
 
-def test_slot_matches_gpu_encode_and_plain_decode():
+def test_slot_matches_gpu_encode_and_plain_decode(form):
     """GPU encode -> payload copied to the slot head -> in-place decode, equal
     to the out-of-place decode, on one 33,554,432-element KV-cache tensor."""
     x = W.kv_cache_tensor(3, 1, device=DEV).reshape(-1)
@@ -125,7 +134,36 @@ def test_slot_matches_gpu_encode_and_plain_decode():
     assert torch.equal(out.view(torch.int16), x.view(torch.int16))
 
 
-def test_slot_rejects_bad_metadata_and_leaves_slot():
+@pytest.mark.parametrize("make,n,seed", [(W.gaussian_weight, 40 * 2**20 + 5, 1),
+                                         (W.log_uniform_stress, 40 * 2**20 + 3, 2)])
+def test_slot_beyond_register_reach(make, n, seed, form):
+    """More tiles overlap the payload than the cooperative grid holds in
+    registers (3 per workgroup): the rest, and the partial last tile, go
+    through the stash; stress data also gives held tiles with more escapes
+    than their LDS list takes.  GPU encode, then the in-place decode with the
+    stream marked ascending or not, with and without validation."""
+    x = make(n, seed=2000 + seed).reshape(-1).to(DEV)
+    ws = workspace(n)
+    cb = S.calibrate(x, ws)
+    payload, meta = S.encode(x, cb, ws)
+    m = S.read_meta(meta)
+    _say("slot beyond reach n=%d e=%d comp=%d form=%s" % (n, m.n_esc, m.comp_bytes, form))
+    unmarked = meta.clone()
+    unmarked[_abi.Meta.flags.offset: _abi.Meta.flags.offset + 4] = 0
+    slot = torch.empty(max(2 * n, m.comp_bytes), dtype=torch.uint8, device=DEV)
+    stash = torch.empty(m.comp_bytes, dtype=torch.uint8, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for md, status in ((meta, None), (meta, st), (unmarked, None), (unmarked, st)):
+        slot.fill_(FILL)
+        slot[: m.comp_bytes].copy_(payload[: m.comp_bytes])
+        out = S.decode_slot(slot, md, cb, n, stash, status=status)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        assert torch.equal(out.view(torch.int16), x.view(torch.int16))
+    del slot, stash, payload
+
+
+def test_slot_rejects_bad_metadata_and_leaves_slot(form):
     x = W.gaussian_weight(5 * TILE + 11, seed=400)
     xs, ocb, opay, om = oracle_case(x)
     n = om.n
@@ -154,7 +192,7 @@ def test_slot_rejects_bad_metadata_and_leaves_slot():
         S.decode_slot(slot, meta_to_device(om), lut, n, slot[-om.comp_bytes:])
 
 
-def test_slot_unsorted_escape_stream_with_validation():
+def test_slot_unsorted_escape_stream_with_validation(form):
     n = 6 * TILE + 77
     x = torch.full((n,), 1.0, dtype=torch.bfloat16)
     pos = [3, 900, 5000, 8191, 8192, 9000, 17000, 24000, 40000, n - 1]
@@ -175,7 +213,7 @@ def test_slot_unsorted_escape_stream_with_validation():
     assert np.array_equal(out, xs)
 
 
-def test_h2d_pipeline_into_slots():
+def test_h2d_pipeline_into_slots(form):
     """Payloads in pinned host memory are copied into the heads of their
     slots on a copy stream; a second stream waits on each copy's event and
     expands the slot in place, while the next copies proceed."""
@@ -214,7 +252,7 @@ def test_h2d_pipeline_into_slots():
         assert np.array_equal(host_bits(out.cpu()), host_bits(x))
 
 
-def test_slot_batch_matches_inputs_across_launches():
+def test_slot_batch_matches_inputs_across_launches(form):
     """40 payloads of mixed sizes and escape densities (two launch pairs),
     each at the head of its own slot, decoded in place as one group."""
     g = torch.Generator().manual_seed(11)
