@@ -46,6 +46,12 @@ def parse():
     ap.add_argument("--no-small", action="store_true", help="skip the small single-tensor configs")
     ap.add_argument("--h2d-tensors", type=int, default=8,
                     help="KV tensors in the host-to-device pipeline sample")
+    ap.add_argument("--small-only", metavar="WORKLOAD", nargs="?", const="all",
+                    help="instead of the benchmark, run the smaller single-tensor workloads only "
+                         "(or the one named) and print them as one JSON line")
+    ap.add_argument("--probes", action="store_true",
+                    help="instead of the benchmark, run the probes of the part's costs that the "
+                         "design rests on (reference-stream library) and print them as one JSON line")
     return ap.parse_args()
 
 
@@ -123,13 +129,133 @@ def pattern_ceilings(S, x_all, phases, stream, reps):
     return res
 
 
-def small_configs(S, W, dev, stream, host_inputs=None):
+def design_probes(S, dev):
+    """Costs of the part that the codec's design rests on, measured with the
+    reference-stream library (HIP events on the launch stream, mean over the
+    timed launches after two untimed ones):
+
+    * access shapes: the encode / decode patterns with 8-element units per
+      thread (the codec's) against thread-contiguous 32-element units, over
+      2^30 elements per launch, and over one 2^25-element tensor per launch
+      (64 launches back to back over 32 tensors' worth of memory: the
+      single-call ceiling);
+    * the encode pattern with a fused arrival (count store, s_waitcnt,
+      two-level arrival counter), and with an agent-scope fence per
+      workgroup;
+    * device-scope atomics: dependent adds by one thread (latency), one add
+      by each of 8,192 workgroups on one address against 64 spread ones;
+    * 64 launches of an almost empty kernel, ordinary and cooperative."""
+    import torch
+
+    lib = S._abi.ceiling_lib()
+    stream = torch.cuda.current_stream(dev)
+    sh = int(stream.cuda_stream)
+
+    def ok(rc):
+        if rc:
+            raise S._abi.SplitZipError("probe", rc)
+
+    def timed(fn, reps):
+        fn()
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps   # ms
+
+    res = {}
+    big = 1 << 30
+    x = torch.empty(big, dtype=torch.int16, device=dev)
+    x.random_(-32768, 32767)
+    pk = torch.empty(big // 2, dtype=torch.uint8, device=dev)
+    sm = torch.empty(big, dtype=torch.uint8, device=dev)
+    out = torch.empty(big, dtype=torch.int16, device=dev)
+    tiles = big // 8192
+    counts = torch.zeros(tiles, dtype=torch.int32, device=dev)
+    ctrs = torch.zeros(8 * (1 + (tiles + 15) // 16), dtype=torch.int64, device=dev)
+    ready = torch.zeros(4, dtype=torch.int32, device=dev)
+    epoch = [0]
+
+    def ptrs(n, k):
+        """Element offset k * n of every buffer (the per-call runs cycle through
+        32 different tensors' worth of memory, so that nothing is cache-resident)."""
+        o = k * n
+        return (x.data_ptr() + 2 * o, pk.data_ptr() + o // 2, sm.data_ptr() + o, out.data_ptr() + 2 * o)
+
+    def arrive(n, k):
+        epoch[0] += 1
+        xp, pp, sp, _ = ptrs(n, k)
+        ok(lib.splitzip_ceiling_encode_arrive(xp, n, pp, sp, counts.data_ptr(), ctrs.data_ptr(),
+                                              ready.data_ptr(), epoch[0], sh))
+
+    def call(fn, enc_side):
+        def run(n, k):
+            xp, pp, sp, op = ptrs(n, k)
+            ok(fn(xp, n, pp, sp, sh) if enc_side else fn(pp, sp, op, n, sh))
+        return run
+
+    enc = {
+        "shape_8": call(lib.splitzip_ceiling_encode_shape, True),
+        "wide_32": call(lib.splitzip_ceiling_encode_wide, True),
+        "fused_arrival": arrive,
+        "fence_per_workgroup": call(lib.splitzip_ceiling_encode_fenced, True),
+    }
+    dec = {
+        "shape_8": call(lib.splitzip_ceiling_decode_shape, False),
+        "wide_32": call(lib.splitzip_ceiling_decode_wide, False),
+    }
+    one = 1 << 25   # one KV tensor
+    slices = big // one
+    for name, table in (("encode", enc), ("decode", dec)):
+        res[name] = {}
+        for k, fn in table.items():
+            ms_big = timed(lambda: fn(big, 0), 5)
+            turn = [0]
+
+            def next_call():
+                fn(one, turn[0] % slices)
+                turn[0] += 1
+            ms_one = timed(next_call, 64)
+            moved = 3.5   # bytes per element, both patterns
+            res[name][k] = {
+                "per_2^30_launch": {"ms": round(ms_big, 4),
+                                    "TBps": round(moved * big / ms_big / 1e9, 3)},
+                "per_2^25_call": {"us": round(ms_one * 1e3, 2),
+                                  "TBps": round(moved * one / ms_one / 1e9, 3)}}
+    torch.cuda.synchronize()
+    assert int(ready[0].item()) == epoch[0], "fused arrival: the last arrival was not seen"
+    del x, pk, sm, out, counts
+
+    ac = torch.zeros(8 * 64, dtype=torch.int64, device=dev)
+    lat_ms = timed(lambda: ok(lib.splitzip_ceiling_atomics(ac.data_ptr(), 1, 1, 4096, sh)), 3)
+    one_ms = timed(lambda: ok(lib.splitzip_ceiling_atomics(ac.data_ptr(), 8192, 1, 1, sh)), 5)
+    spread_ms = timed(lambda: ok(lib.splitzip_ceiling_atomics(ac.data_ptr(), 8192, 64, 1, sh)), 5)
+    res["atomics"] = {
+        "dependent_add_latency_us": round(lat_ms * 1e3 / 4096, 3),
+        "8192_workgroups_one_address_us": round(one_ms * 1e3, 2),
+        "8192_workgroups_64_addresses_us": round(spread_ms * 1e3, 2),
+        "one_address_ns_per_add": round(one_ms * 1e6 / 8192, 2)}
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    res["launch"] = {}
+    for coop in (0, 1):
+        ms = timed(lambda: ok(lib.splitzip_ceiling_launch(coop, 64, sink.data_ptr(), sh)), 64)
+        res["launch"]["cooperative" if coop else "ordinary"] = {"us_per_launch": round(ms * 1e3, 2)}
+    return res
+
+def small_configs(S, W, dev, stream, host_inputs=None, only=None):
     """The smaller single-tensor workloads: one call per phase, median GPU
     time of 20 calls (100 decodes into one output buffer for the linear
     weight), warm (after 3 warm-up calls; they fit the 256 MB last-level
-    cache) and cold (a 512 MiB buffer is written before each call).  No
-    roofline claim is made for these.  With ``host_inputs`` (a dict), each
-    workload's bits are also copied to it for the oracle."""
+    cache), cold (a 512 MiB buffer is read before each call, so the caches
+    hold other, clean data) and cold_dirty (it is written instead: the call
+    also pays for writing that buffer's dirty lines back); rates on
+    raw and on algorithmic bytes (calibrate 2n, encode and decode 2n plus the
+    payload).  With ``host_inputs`` (a dict), each workload's bits are also
+    copied to it for the oracle; ``only`` names the one workload to run."""
     import statistics
 
     import torch
@@ -144,12 +270,14 @@ def small_configs(S, W, dev, stream, host_inputs=None):
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     ws = S.Workspace(1 << 26, device=dev)
 
-    def gpu_time(fn, reps, cold):
+    def gpu_time(fn, reps, mode):
         for _ in range(3):
             fn()
         ts = []
         for _ in range(reps):
-            if cold:
+            if mode == "cold":
+                scrub.view(torch.int64).sum()
+            elif mode == "cold_dirty":
                 scrub.fill_(1)
             torch.cuda._sleep(100_000)      # keep the GPU busy while the call is enqueued
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -162,20 +290,22 @@ def small_configs(S, W, dev, stream, host_inputs=None):
 
     out = {}
     for name, xs in cfgs.items():
+        if only and name != only:
+            continue
         rec = {"tensors": len(xs), "elements": sum(x.numel() for x in xs)}
         comp = esc = 0
-        for mode in ("warm", "cold"):
+        for mode in ("warm", "cold", "cold_dirty"):
             us = {"calibrate": 0.0, "encode": 0.0, "decode": 0.0}
             for x in xs:
                 cb = S.calibrate(x, ws)
                 payload, meta = S.encode(x, cb, ws)
                 dst = torch.empty(x.numel(), dtype=torch.bfloat16, device=dev)
                 reps = 100 if name.startswith("linear") else 20
-                us["calibrate"] += gpu_time(lambda: S.calibrate(x, ws, cb=cb), 20, mode == "cold")
+                us["calibrate"] += gpu_time(lambda: S.calibrate(x, ws, cb=cb), 20, mode)
                 us["encode"] += gpu_time(lambda: S.encode(x, cb, ws, payload=payload, meta=meta),
-                                         20, mode == "cold")
+                                         20, mode)
                 us["decode"] += gpu_time(lambda: S.decode(payload, meta, cb, x.numel(), out=dst),
-                                         reps, mode == "cold")
+                                         reps, mode)
                 if not torch.equal(dst.view(torch.int16), x.reshape(-1).view(torch.int16)):
                     raise AssertionError("round trip failed on " + name)
                 if mode == "warm":
@@ -183,7 +313,10 @@ def small_configs(S, W, dev, stream, host_inputs=None):
                     comp += m.comp_bytes
                     esc += m.n_esc
             raw = 2 * rec["elements"]
-            rec[mode] = {k: {"us": round(v, 2), "raw_GBps": round(raw / v / 1e3, 1)}
+            alg = {"calibrate": raw, "encode": raw + comp, "decode": comp + raw}
+            rec[mode] = {k: {"us": round(v, 2), "raw_GBps": round(raw / v / 1e3, 1),
+                             "alg_GBps": round(alg[k] / v / 1e3, 1),
+                             "hbm_frac": round(alg[k] / v / 1e3 / HBM_PEAK_GBPS, 4)}
                          for k, v in us.items()}
         rec["payload_over_raw"] = round(comp / (2 * rec["elements"]), 6)
         rec["escape_fraction"] = round(esc / rec["elements"], 6)
@@ -437,6 +570,13 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     sh = int(stream.cuda_stream)
+    if args.probes:
+        print(json.dumps({"probes": design_probes(S, dev), "device": torch.cuda.get_device_name(dev)}))
+        return
+    if args.small_only:
+        only = None if args.small_only == "all" else args.small_only
+        print(json.dumps({"small_configs": small_configs(S, W, dev, stream, only=only)}))
+        return
     T = 2 * LAYERS
 
     # inputs, generated on the GPU, resident in HBM
@@ -564,6 +704,22 @@ def main():
                 "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                 "alg_bytes_per_launch": alg[dom] // launches,
                 "ms_per_launch": round(phase_ms[dom] / launches, 4)}
+    # The main encode kernel is as long as the decode kernel (the longer of
+    # the two in the kernel trace).  Its phase also holds the placement
+    # launches, so the event-timed figure below is a lower bound for the
+    # kernel itself; the kernel trace's duration of the same source, when
+    # the committed summary matches it, gives the kernel's own rate.
+    enc_trace = traced_duration_us("k_encode", 131072)
+    roofline_encode = {
+        "bound": "hbm", "kernel": "k_encode", "phase": "encode", "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s", "alg_bytes_per_launch": alg["encode"] // launches,
+        "phase_achieved": round(gbps(alg["encode"], phase_ms["encode"]), 1),
+        "phase_frac": round(gbps(alg["encode"], phase_ms["encode"]) / HBM_PEAK_GBPS, 4),
+        "phase_ms_per_launch": round(phase_ms["encode"] / launches, 4),
+        "kernel_trace_us": enc_trace,
+        "kernel_trace_frac": (round(alg["encode"] / launches / (enc_trace * 1e-6) / 1e9
+                                    / HBM_PEAK_GBPS, 4) if enc_trace else None),
+        "traffic": counted_traffic("k_encode")}
 
     slot = slot_decode_phase(S, batch, metas_h, x_all, stream, max(2, args.steps // 2))
     copy = d2d_copy(x_all, stream)
@@ -615,6 +771,7 @@ def main():
         "small_configs": small,
         "h2d_pipeline": h2d,
         "roofline": roofline,
+        "roofline_encode": roofline_encode,
         "cpu_baseline": cpu,
         "context_h200": {"encode_GBps": 613, "decode_GBps": 2182,
                          "note": "pages' figures on LLM KV activations, other hardware"},
@@ -647,6 +804,30 @@ def counted_traffic(kernel):
         parts = ln.split()
         if len(parts) == 3 and parts[0] == "traffic_bytes_per_launch" and parts[1] == kernel:
             return int(parts[2])
+    return None
+
+
+def traced_duration_us(kernel, workgroups):
+    """Mean duration of `kernel` at that launch shape from the committed
+    kernel-trace summary, or None when the kernel source has changed since
+    it was taken."""
+    import hashlib
+
+    src = os.path.join(ROOT, "lossless_bf16_tensor_splitzip_amd", "csrc", "splitzip.hip")
+    summary = os.path.join(ROOT, "profiles", "kv_stream_4gib_kernel_trace.md")
+    try:
+        lines = open(summary).read().splitlines()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    recorded = [ln.split()[1] for ln in lines if ln.startswith("source_sha256 ")]
+    if not recorded or recorded[0] != sha:
+        return None
+    for ln in lines:
+        parts = ln.split()
+        if (len(parts) == 4 and parts[0] == "duration_us" and parts[1] == kernel
+                and parts[2] == str(workgroups)):
+            return float(parts[3])
     return None
 
 

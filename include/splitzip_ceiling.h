@@ -14,6 +14,17 @@
  *   splitzip_ceiling_decode_shape   the dense decode (reads n/2 + n B,
  *                                   writes 2n B)
  *
+ * and probes of the part's costs that the codec's design rests on:
+ *
+ *   splitzip_ceiling_encode_wide / _decode_wide   the same patterns with
+ *                                   thread-contiguous 32-element units
+ *   splitzip_ceiling_encode_arrive  the encode pattern with a fused arrival
+ *   splitzip_ceiling_encode_fenced  the encode pattern with a fence per
+ *                                   workgroup
+ *   splitzip_ceiling_atomics        device-scope atomics: latency, and cost
+ *                                   on one address against spread ones
+ *   splitzip_ceiling_launch         ordinary against cooperative launches
+ *
  * Conventions: every pointer is a device (or pinned host) address the
  * caller owns and keeps alive until the stream has run the call; calls are
  * asynchronous on `stream` (0 = the null stream); the output bytes are
@@ -55,6 +66,46 @@ int splitzip_ceiling_encode_shape(const uint16_t *d_x, uint64_t n, uint8_t *d_pk
  * holds n/2 bytes, d_sm n bytes, d_out 2n bytes.  INVALID otherwise. */
 int splitzip_ceiling_decode_shape(const uint8_t *d_pk, const uint8_t *d_sm, uint16_t *d_out,
                                   uint64_t n, hipStream_t stream);
+
+/* The encode / decode patterns with thread-contiguous 32-element units: per
+ * 32 elements four 16-byte loads of d_x, one 16-byte store to d_pk + i/2 and
+ * two to d_sm + i (encode); one 16-byte load of d_pk + i/2, two of d_sm + i
+ * and four 16-byte stores to d_out + i (decode).  Sizes, alignment and
+ * errors as for the shapes above. */
+int splitzip_ceiling_encode_wide(const uint16_t *d_x, uint64_t n, uint8_t *d_pk, uint8_t *d_sm,
+                                 hipStream_t stream);
+int splitzip_ceiling_decode_wide(const uint8_t *d_pk, const uint8_t *d_sm, uint16_t *d_out,
+                                 uint64_t n, hipStream_t stream);
+
+/* The encode pattern, then what a placement fused into the encode kernel
+ * would add: each workgroup stores a 4-byte count to d_counts[tile] (n/8192
+ * of them), waits for its stores to complete and arrives on a two-level
+ * counter (groups of 16 workgroups) in d_ctrs (8 * (1 + ceil(tiles / 16))
+ * uint64 words, counters 64 bytes apart, tagged with `epoch` in their high
+ * half: a counter with another tag is claimed for it, so d_ctrs needs no
+ * clearing as long as every call passes a new nonzero epoch); the last
+ * arrival writes `epoch` to *d_ready.  All pointers 16-byte aligned. */
+int splitzip_ceiling_encode_arrive(const uint16_t *d_x, uint64_t n, uint8_t *d_pk, uint8_t *d_sm,
+                                   uint32_t *d_counts, uint64_t *d_ctrs, uint32_t *d_ready,
+                                   uint32_t epoch, hipStream_t stream);
+
+/* The encode pattern with an agent-scope fence (__threadfence) at the end of
+ * every workgroup.  As splitzip_ceiling_encode_shape otherwise. */
+int splitzip_ceiling_encode_fenced(const uint16_t *d_x, uint64_t n, uint8_t *d_pk, uint8_t *d_sm,
+                                   hipStream_t stream);
+
+/* `grid` workgroups of 64 threads; lane 0 of workgroup b adds 1 to
+ * d_ctrs[(b % spread) * 8] (device scope) `rounds` times, each add waiting
+ * for the previous one's result.  d_ctrs: 8 * spread uint64 words, 16-byte
+ * aligned; spread in [1, 4096], rounds in [1, 2^20]. */
+int splitzip_ceiling_atomics(uint64_t *d_ctrs, uint32_t grid, uint32_t spread, uint32_t rounds,
+                             hipStream_t stream);
+
+/* An almost empty kernel (`grid` <= 1024 workgroups of 64 threads; one
+ * thread adds 1 to *d_sink), launched ordinarily or, with cooperative != 0,
+ * with hipLaunchCooperativeKernel. */
+int splitzip_ceiling_launch(uint32_t cooperative, uint32_t grid, uint32_t *d_sink,
+                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -84,6 +84,137 @@ __global__ __launch_bounds__(kThreads) void k_decode_shape(const uint8_t *pk, co
     }
 }
 
+// ---- probes behind the design's choices (see include/splitzip_ceiling.h) ----
+
+// The encode pattern with thread-contiguous 32-element units.
+__global__ __launch_bounds__(kThreads) void k_encode_wide(const uint16_t *x, uint8_t *pk, uint8_t *sm) {
+    const uint64_t i0 = (uint64_t)blockIdx.x * kTile + (uint64_t)threadIdx.x * 32;
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x + i0);
+    u32x4 q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = __builtin_nontemporal_load(xv + k);
+    const u32x4 p = {q[0].x ^ q[0].y, q[1].x ^ q[1].y, q[2].x ^ q[2].y, q[3].x ^ q[3].y};
+    const u32x4 s0 = {q[0].x ^ q[0].z, q[0].y ^ q[0].w, q[1].x ^ q[1].z, q[1].y ^ q[1].w};
+    const u32x4 s1 = {q[2].x ^ q[2].z, q[2].y ^ q[2].w, q[3].x ^ q[3].z, q[3].y ^ q[3].w};
+    __builtin_nontemporal_store(p, reinterpret_cast<u32x4 *>(pk + i0 / 2));
+    __builtin_nontemporal_store(s0, reinterpret_cast<u32x4 *>(sm + i0));
+    __builtin_nontemporal_store(s1, reinterpret_cast<u32x4 *>(sm + i0 + 16));
+}
+
+// The decode pattern with thread-contiguous 32-element units.
+__global__ __launch_bounds__(kThreads) void k_decode_wide(const uint8_t *pk, const uint8_t *sm,
+                                                          uint16_t *out) {
+    const uint64_t i0 = (uint64_t)blockIdx.x * kTile + (uint64_t)threadIdx.x * 32;
+    const u32x4 p = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(pk + i0 / 2));
+    const u32x4 s0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(sm + i0));
+    const u32x4 s1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(sm + i0 + 16));
+    u32x4 *o = reinterpret_cast<u32x4 *>(out + i0);
+    __builtin_nontemporal_store(u32x4{p.x ^ s0.x, p.y ^ s0.y, p.z ^ s0.z, p.w ^ s0.w}, o);
+    __builtin_nontemporal_store(u32x4{p.x ^ s1.x, p.y ^ s1.y, p.z ^ s1.z, p.w ^ s1.w}, o + 1);
+    __builtin_nontemporal_store(u32x4{s0.x, s0.y ^ p.x, s1.z, s1.w ^ p.y}, o + 2);
+    __builtin_nontemporal_store(u32x4{s1.x ^ p.z, s0.z, s0.w ^ p.w, s1.y}, o + 3);
+}
+
+__device__ inline uint64_t ld_agent(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Replaces a counter whose high half is not `epoch` by (epoch << 32).
+__device__ inline void claim(uint64_t *c, uint32_t epoch) {
+    uint64_t cur = ld_agent(c);
+    for (int k = 0; k < 64 && (uint32_t)(cur >> 32) != epoch; ++k)
+        if (__hip_atomic_compare_exchange_strong(c, &cur, (uint64_t)epoch << 32, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            break;
+}
+
+// The encode pattern, then a fused arrival as a placement in the same kernel
+// would need it: the tile's count is stored, the workgroup waits for its
+// stores to complete (s_waitcnt) and arrives on a two-level counter (groups
+// of 16 workgroups, each counter on its own 64-byte line, tagged with the
+// call's epoch); the last arrival writes the epoch to *ready.
+__global__ __launch_bounds__(kThreads) void k_encode_arrive(const uint16_t *x, uint8_t *pk, uint8_t *sm,
+                                                            uint32_t *counts, uint64_t *ctrs,
+                                                            uint32_t *ready, uint32_t epoch) {
+    constexpr uint32_t kGroup = 16;
+    const uint32_t t = blockIdx.x, tiles = gridDim.x;
+    const uint32_t ngroups = (tiles + kGroup - 1) / kGroup, g = t / kGroup;
+    uint64_t *top = ctrs, *grp = ctrs + 8 * (1 + g);
+    const uint64_t base = (uint64_t)t * kTile;
+    const int tid = threadIdx.x;
+    u32x4 q[kUnits];
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+        const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+        q[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + i0));
+    }
+    if (tid == 0) {
+        claim(grp, epoch);
+        if (t % kGroup == 0) claim(top, epoch);
+    }
+    uint32_t acc = 0;
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+        const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+        const uint32_t p = q[u].x ^ q[u].y ^ q[u].z ^ q[u].w;
+        const u32x2 s = {q[u].x ^ q[u].z, q[u].y ^ q[u].w};
+        acc ^= p;
+        __builtin_nontemporal_store(p, reinterpret_cast<uint32_t *>(pk + i0 / 2));
+        __builtin_nontemporal_store(s, reinterpret_cast<u32x2_a4 *>(sm + i0));
+    }
+    if (tid == 0) __hip_atomic_store(counts + t, acc & 0xFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t gsize = g * kGroup + kGroup <= tiles ? kGroup : tiles - g * kGroup;
+        const uint64_t prev = __hip_atomic_fetch_add(grp, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)prev + 1u == gsize) {
+            const uint64_t p2 = __hip_atomic_fetch_add(top, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((uint32_t)p2 + 1u == ngroups)
+                __hip_atomic_store(ready, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// The encode pattern with an agent-scope fence (__threadfence: write-back of
+// the L2 and invalidation) at the end of every workgroup.
+__global__ __launch_bounds__(kThreads) void k_encode_fenced(const uint16_t *x, uint8_t *pk, uint8_t *sm) {
+    const uint64_t base = (uint64_t)blockIdx.x * kTile;
+    const int tid = threadIdx.x;
+    u32x4 q[kUnits];
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+        const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+        q[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + i0));
+    }
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+        const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+        const uint32_t p = q[u].x ^ q[u].y ^ q[u].z ^ q[u].w;
+        const u32x2 s = {q[u].x ^ q[u].z, q[u].y ^ q[u].w};
+        __builtin_nontemporal_store(p, reinterpret_cast<uint32_t *>(pk + i0 / 2));
+        __builtin_nontemporal_store(s, reinterpret_cast<u32x2_a4 *>(sm + i0));
+    }
+    __threadfence();
+}
+
+// Device-scope atomic adds: lane 0 of every 64-thread workgroup adds 1 to
+// ctrs[(blockIdx % spread) * 8] `rounds` times, each add waiting for the
+// previous one's result.
+__global__ __launch_bounds__(64) void k_atomics(uint64_t *ctrs, uint32_t spread, uint32_t rounds) {
+    if (threadIdx.x) return;
+    uint64_t *c = ctrs + (uint64_t)(blockIdx.x % spread) * 8;
+    uint64_t v = 0;
+    for (uint32_t r = 0; r < rounds; ++r)   // (v >> 63 is 0, but makes each add wait for the last)
+        v += __hip_atomic_fetch_add(c, 1ull + (v >> 63), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v == 0x9E3779B97F4A7C15ull) ctrs[1] = v;
+}
+
+// An almost empty kernel, for launch costs.
+__global__ __launch_bounds__(64) void k_touch(uint32_t *sink) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) sink[0] += 1u;
+}
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 int launched() { return hipGetLastError() == hipSuccess ? SPLITZIP_OK : SPLITZIP_ERR_HIP; }
@@ -125,5 +256,67 @@ extern "C" int splitzip_ceiling_decode_shape(const uint8_t *d_pk, const uint8_t 
         !aligned16(d_out))
         return SPLITZIP_ERR_INVALID;
     k_decode_shape<<<(uint32_t)(n / kTile), kThreads, 0, stream>>>(d_pk, d_sm, d_out);
+    return launched();
+}
+
+extern "C" int splitzip_ceiling_encode_wide(const uint16_t *d_x, uint64_t n, uint8_t *d_pk,
+                                            uint8_t *d_sm, hipStream_t stream) {
+    if (!tiles_ok(n) || !d_x || !d_pk || !d_sm || !aligned16(d_x) || !aligned16(d_pk) ||
+        !aligned16(d_sm))
+        return SPLITZIP_ERR_INVALID;
+    k_encode_wide<<<(uint32_t)(n / kTile), kThreads, 0, stream>>>(d_x, d_pk, d_sm);
+    return launched();
+}
+
+extern "C" int splitzip_ceiling_decode_wide(const uint8_t *d_pk, const uint8_t *d_sm,
+                                            uint16_t *d_out, uint64_t n, hipStream_t stream) {
+    if (!tiles_ok(n) || !d_pk || !d_sm || !d_out || !aligned16(d_pk) || !aligned16(d_sm) ||
+        !aligned16(d_out))
+        return SPLITZIP_ERR_INVALID;
+    k_decode_wide<<<(uint32_t)(n / kTile), kThreads, 0, stream>>>(d_pk, d_sm, d_out);
+    return launched();
+}
+
+extern "C" int splitzip_ceiling_encode_arrive(const uint16_t *d_x, uint64_t n, uint8_t *d_pk,
+                                              uint8_t *d_sm, uint32_t *d_counts, uint64_t *d_ctrs,
+                                              uint32_t *d_ready, uint32_t epoch, hipStream_t stream) {
+    if (!tiles_ok(n) || !d_x || !d_pk || !d_sm || !d_counts || !d_ctrs || !d_ready ||
+        !aligned16(d_x) || !aligned16(d_pk) || !aligned16(d_sm) || !aligned16(d_counts) ||
+        !aligned16(d_ctrs) || !aligned16(d_ready) || epoch == 0)
+        return SPLITZIP_ERR_INVALID;
+    k_encode_arrive<<<(uint32_t)(n / kTile), kThreads, 0, stream>>>(d_x, d_pk, d_sm, d_counts, d_ctrs,
+                                                                  d_ready, epoch);
+    return launched();
+}
+
+extern "C" int splitzip_ceiling_encode_fenced(const uint16_t *d_x, uint64_t n, uint8_t *d_pk,
+                                              uint8_t *d_sm, hipStream_t stream) {
+    if (!tiles_ok(n) || !d_x || !d_pk || !d_sm || !aligned16(d_x) || !aligned16(d_pk) ||
+        !aligned16(d_sm))
+        return SPLITZIP_ERR_INVALID;
+    k_encode_fenced<<<(uint32_t)(n / kTile), kThreads, 0, stream>>>(d_x, d_pk, d_sm);
+    return launched();
+}
+
+extern "C" int splitzip_ceiling_atomics(uint64_t *d_ctrs, uint32_t grid, uint32_t spread,
+                                        uint32_t rounds, hipStream_t stream) {
+    if (!d_ctrs || !aligned16(d_ctrs) || grid == 0 || spread == 0 || spread > 4096 || rounds == 0 ||
+        rounds > (1u << 20))
+        return SPLITZIP_ERR_INVALID;
+    k_atomics<<<grid, 64, 0, stream>>>(d_ctrs, spread, rounds);
+    return launched();
+}
+
+extern "C" int splitzip_ceiling_launch(uint32_t cooperative, uint32_t grid, uint32_t *d_sink,
+                                       hipStream_t stream) {
+    if (!d_sink || ((uintptr_t)d_sink & 3u) || grid == 0 || grid > 1024) return SPLITZIP_ERR_INVALID;
+    if (cooperative) {
+        void *args[] = {&d_sink};
+        if (hipLaunchCooperativeKernel(reinterpret_cast<const void *>(k_touch), dim3(grid), dim3(64),
+                                       args, 0, stream) != hipSuccess)
+            return SPLITZIP_ERR_HIP;
+        return SPLITZIP_OK;
+    }
+    k_touch<<<grid, 64, 0, stream>>>(d_sink);
     return launched();
 }

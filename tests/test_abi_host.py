@@ -46,6 +46,18 @@ def test_reference_stream_symbols_and_argument_errors():
     assert lib.splitzip_ceiling_encode_shape(0x1008, 8192, 0x2000, 0x3000, 0) == _abi.ERR_INVALID
     assert lib.splitzip_ceiling_decode_shape(0x1000, 0x2000, 0x3000, 0, 0) == _abi.ERR_INVALID
     assert lib.splitzip_ceiling_decode_shape(0x1000, 0, 0x3000, 8192, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_encode_wide(0x1000, 100, 0x2000, 0x3000, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_decode_wide(0x1000, 0x2008, 0x3000, 8192, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_encode_fenced(0x1000, 8192, 0, 0x3000, 0) == _abi.ERR_INVALID
+    # epoch 0 is not a tag; a misaligned counter array
+    assert lib.splitzip_ceiling_encode_arrive(0x1000, 8192, 0x2000, 0x3000, 0x4000, 0x5000,
+                                              0x6000, 0, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_encode_arrive(0x1000, 8192, 0x2000, 0x3000, 0x4000, 0x5008,
+                                              0x6000, 1, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_atomics(0x1000, 1, 4097, 1, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_atomics(0x1000, 1, 1, (1 << 20) + 1, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_launch(1, 0, 0x1000, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_launch(0, 1, 0x1002, 0) == _abi.ERR_INVALID
 
 
 def test_struct_layout_matches_header():

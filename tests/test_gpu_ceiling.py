@@ -63,3 +63,89 @@ def test_read_stream(nbytes, grid):
                                      int(torch.cuda.current_stream().cuda_stream)) == 0
     torch.cuda.synchronize()
     assert int(sink.item()) == 7
+
+
+@pytest.mark.parametrize("tiles", [1, 5])
+def test_wide_shapes_touch_their_bytes(tiles):
+    """Thread-contiguous 32-element units: the stated XORs over the stated
+    ranges, nothing past them."""
+    lib = _abi.ceiling_lib()
+    n = 8192 * tiles
+    _say("wide reference streams n=%d" % n)
+    g = torch.Generator().manual_seed(50 + tiles)
+    x = torch.randint(-(1 << 15), 1 << 15, (n,), generator=g, dtype=torch.int32)
+    x = x.to(torch.int16).to(DEV)
+    guard = 64
+    pk = torch.full((n // 2 + guard,), 0x33, dtype=torch.uint8, device=DEV)
+    sm = torch.full((n + guard,), 0x44, dtype=torch.uint8, device=DEV)
+    out = torch.full((n + guard,), 0x55, dtype=torch.int16, device=DEV)
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    assert lib.splitzip_ceiling_encode_wide(x.data_ptr(), n, pk.data_ptr(), sm.data_ptr(), sh) == 0
+    assert lib.splitzip_ceiling_decode_wide(pk.data_ptr(), sm.data_ptr(), out.data_ptr(), n, sh) == 0
+    torch.cuda.synchronize()
+    q = _u32(x.view(torch.int32)).reshape(-1, 4, 4).cpu()     # per thread: 4 loads of 4 words
+    want_pk = q[:, :, 0] ^ q[:, :, 1]                           # one 16-byte store per thread
+    want_s0 = torch.stack([q[:, 0, 0] ^ q[:, 0, 2], q[:, 0, 1] ^ q[:, 0, 3],
+                           q[:, 1, 0] ^ q[:, 1, 2], q[:, 1, 1] ^ q[:, 1, 3]], 1)
+    want_s1 = torch.stack([q[:, 2, 0] ^ q[:, 2, 2], q[:, 2, 1] ^ q[:, 2, 3],
+                           q[:, 3, 0] ^ q[:, 3, 2], q[:, 3, 1] ^ q[:, 3, 3]], 1)
+    assert torch.equal(_u32(pk[: n // 2]).cpu().reshape(-1, 4), want_pk)
+    s = _u32(sm[:n]).cpu().reshape(-1, 8)
+    assert torch.equal(s[:, :4], want_s0) and torch.equal(s[:, 4:], want_s1)
+    assert bool((pk[n // 2:] == 0x33).all()) and bool((sm[n:] == 0x44).all())
+    p, s0, s1 = want_pk, want_s0, want_s1
+    o = _u32(out[:n]).cpu().reshape(-1, 16)
+    assert torch.equal(o[:, 0:4], p ^ s0) and torch.equal(o[:, 4:8], p ^ s1)
+    assert torch.equal(o[:, 8:12], torch.stack([s0[:, 0], s0[:, 1] ^ p[:, 0], s1[:, 2],
+                                                s1[:, 3] ^ p[:, 1]], 1))
+    assert torch.equal(o[:, 12:16], torch.stack([s1[:, 0] ^ p[:, 2], s0[:, 2], s0[:, 3] ^ p[:, 3],
+                                                 s1[:, 1]], 1))
+    assert bool((out[n:] == 0x55).all())
+
+
+def test_fused_arrival_fence_atomics_and_launch_probes():
+    """The probes run and do what their header states: the encode pattern's
+    bytes with the arrival or the fence, tile counts and the ready word from
+    the last arrival (two calls, counters not cleared between them), every
+    atomic add counted, and both launch forms."""
+    lib = _abi.ceiling_lib()
+    tiles = 37
+    n = 8192 * tiles
+    _say("probes n=%d" % n)
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    g = torch.Generator().manual_seed(77)
+    x = torch.randint(-(1 << 15), 1 << 15, (n,), generator=g, dtype=torch.int32).to(torch.int16).to(DEV)
+    pk0 = torch.zeros(n // 2, dtype=torch.uint8, device=DEV)
+    sm0 = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    assert lib.splitzip_ceiling_encode_shape(x.data_ptr(), n, pk0.data_ptr(), sm0.data_ptr(), sh) == 0
+    pk, sm = torch.zeros_like(pk0), torch.zeros_like(sm0)
+    counts = torch.full((tiles + 3,), -1, dtype=torch.int32, device=DEV)
+    ctrs = torch.full((8 * (1 + (tiles + 15) // 16),), 12345, dtype=torch.int64, device=DEV)
+    ready = torch.zeros(4, dtype=torch.int32, device=DEV)
+    for epoch in (1, 2):
+        assert lib.splitzip_ceiling_encode_arrive(x.data_ptr(), n, pk.data_ptr(), sm.data_ptr(),
+                                                  counts.data_ptr(), ctrs.data_ptr(),
+                                                  ready.data_ptr(), epoch, sh) == 0
+        torch.cuda.synchronize()
+        assert int(ready[0].item()) == epoch
+    assert torch.equal(pk, pk0) and torch.equal(sm, sm0)
+    assert bool(((counts[:tiles] >= 0) & (counts[:tiles] < 256)).all())
+    assert bool((counts[tiles:] == -1).all())
+    pk.zero_()
+    sm.zero_()
+    assert lib.splitzip_ceiling_encode_fenced(x.data_ptr(), n, pk.data_ptr(), sm.data_ptr(), sh) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(pk, pk0) and torch.equal(sm, sm0)
+    ac = torch.zeros(8 * 64, dtype=torch.int64, device=DEV)
+    assert lib.splitzip_ceiling_atomics(ac.data_ptr(), 100, 7, 3, sh) == 0
+    torch.cuda.synchronize()
+    a = ac.cpu().reshape(64, 8)
+    want = [3 * len(range(k, 100, 7)) for k in range(7)]
+    assert a[:7, 0].tolist() == want and int(a[7:].sum()) == 0 and int(a[:, 1:].sum()) == 0
+    sink = torch.zeros(4, dtype=torch.int32, device=DEV)
+    for coop in (0, 1):
+        assert lib.splitzip_ceiling_launch(coop, 64, sink.data_ptr(), sh) == 0
+    torch.cuda.synchronize()
+    assert int(sink[0].item()) == 2
+    assert lib.splitzip_ceiling_launch(0, 2000, sink.data_ptr(), sh) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_atomics(ac.data_ptr(), 1, 0, 1, sh) == _abi.ERR_INVALID
