@@ -143,6 +143,7 @@ static_assert(kSuperTiles == kThreads && kTailMaxTiles <= 64 && kTailMaxTiles <=
               "count sums: one tile per thread, whole tail blocks per superblock");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef u32x2 u32x2_a4 __attribute__((aligned(4)));
 
@@ -310,8 +311,9 @@ struct CalArgs {
 __global__ __launch_bounds__(kCalThreads, 8) void k_calibrate(CalArgs a) {
     __shared__ uint32_t hist[256 * 64];   // [exponent][lane]
     __shared__ uint32_t part[4 * 256];
-    __shared__ uint64_t key[256];
-    __shared__ uint64_t covered;
+    __shared__ __attribute__((aligned(16))) uint64_t key[256];
+    __shared__ uint64_t wcov[4];
+    __shared__ uint32_t wdist[4];
     __shared__ uint32_t proceed;
 
     const uint32_t item = find_item(a.wg_start, a.count, blockIdx.x);
@@ -341,24 +343,27 @@ __global__ __launch_bounds__(kCalThreads, 8) void k_calibrate(CalArgs a) {
         seen_top = ld_agent(ctrs);
         if (!single) seen_grp = ld_agent(ctrs + 8 * (1 + wg / kCalGroup));
     }
-    for (int i = tid; i < 256 * 64; i += kCalThreads) hist[i] = 0;
-    __syncthreads();
-
     uint32_t *hl = hist + lane;
     const uint64_t nvec = I.n >> 3;
     const u32x4 *xv = reinterpret_cast<const u32x4 *>(I.x);
     // One contiguous range of 16-byte loads per workgroup, 4 loads in flight
     // per thread (measured 6.4-6.7 TB/s against 5.8-6.0 for loads interleaved
-    // over the whole grid).
+    // over the whole grid).  The first round goes out before the LDS
+    // histogram is cleared.
     const uint64_t per = (nvec + nwg - 1) / nwg;
     const uint64_t vlo = (uint64_t)wg * per;
     const uint64_t nv = vlo + per < nvec ? vlo + per : nvec;
     constexpr uint64_t stride = kCalThreads;
     uint64_t v = vlo + tid;
-    for (; v + 3 * stride < nv; v += 4 * stride) {
-        u32x4 q[4];
+    u32x4 q[4];
+    if (v + 3 * stride < nv) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) q[k] = __builtin_nontemporal_load(xv + v + k * stride);
+    }
+    for (int i = tid; i < 256 * 64; i += kCalThreads) hist[i] = 0;
+    __syncthreads();
+
+    while (v + 3 * stride < nv) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
 #pragma unroll
@@ -366,6 +371,11 @@ __global__ __launch_bounds__(kCalThreads, 8) void k_calibrate(CalArgs a) {
                 atomicAdd(hl + exp_lo(q[k][w]) * 64, 1u);
                 atomicAdd(hl + exp_hi(q[k][w]) * 64, 1u);
             }
+        }
+        v += 4 * stride;
+        if (v + 3 * stride < nv) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) q[k] = __builtin_nontemporal_load(xv + v + k * stride);
         }
     }
     for (; v < nv; v += stride) {
@@ -445,42 +455,60 @@ __global__ __launch_bounds__(kCalThreads, 8) void k_calibrate(CalArgs a) {
     if (tid == 0)
         __hip_atomic_store(genp, ((uint64_t)next << 32) | (uint64_t)~next, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-    if (tid == 0) covered = 0;
     if (tid < 256) {
         // unique sort key: count first, then the smaller exponent value
         key[tid] = c ? ((c << 8) | (uint64_t)(255 - tid)) : 0;
     }
     __syncthreads();
-    {   // rank = number of larger keys; 4 threads per exponent, 64 keys each
+    {   // rank = number of larger keys; 4 threads per exponent, 64 keys
+        // each, 16 keys loaded at a time
         const int bin = tid & 255, quarter = tid >> 8;
         const uint64_t own = key[bin];
+        const u64x2 *kv = reinterpret_cast<const u64x2 *>(key + quarter * 64);
         uint32_t r = 0;
-        for (int u = quarter * 64; u < quarter * 64 + 64; ++u) r += key[u] > own ? 1u : 0u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            u64x2 kk[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kk[j] = kv[b * 8 + j];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) r += (kk[j].x > own ? 1u : 0u) + (kk[j].y > own ? 1u : 0u);
+        }
         part[tid] = r;
     }
     __syncthreads();
-    splitzip_codebook *cb = I.cb;
+    // codes; per wave the covered count and the distinct exponents, so that
+    // one barrier gives the totals before the codebook is written
     uint32_t code = 16;
     if (tid < 256) {
         const uint32_t rank = part[tid] + part[256 + tid] + part[512 + tid] + part[768 + tid];
         code = (c > 0 && rank < 16) ? rank : 16u;
+        uint64_t cov = code < 16 ? c : 0;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) cov += __shfl_xor(cov, off, 64);
+        const uint32_t dist = (uint32_t)__popcll(__ballot(c > 0));
+        if (lane == 0) {
+            wcov[tid >> 6] = cov;
+            wdist[tid >> 6] = dist;
+        }
+    }
+    __syncthreads();
+    if (tid < 256) {
+        const uint32_t distinct = wdist[0] + wdist[1] + wdist[2] + wdist[3];
+        const uint32_t n_codes = distinct < 16 ? distinct : 16u;
+        splitzip_codebook *cb = I.cb;
         cb->enc_lut[tid] = (uint8_t)(code < 16 ? code : 0);
         cb->enc_lut_marked[tid] = (uint8_t)code;
         cb->common_lut[tid] = (uint8_t)(code < 16 ? 1 : 0);
         cb->counts[tid] = c;
-        if (code < 16) {
-            cb->dec_lut[code] = (uint8_t)tid;
-            atomicAdd(reinterpret_cast<unsigned long long *>(&covered), (unsigned long long)c);
+        if (code < 16) cb->dec_lut[code] = (uint8_t)tid;
+        if (tid < 16 && (uint32_t)tid >= n_codes) cb->dec_lut[tid] = 0;   // (other slots)
+        if (tid == 0) {
+            cb->n_codes = n_codes;
+            cb->reserved = 0;
+            cb->covered = wcov[0] + wcov[1] + wcov[2] + wcov[3];
+            cb->total = I.n;
         }
-    }
-    const int distinct = __syncthreads_count(tid < 256 && c > 0);
-    const uint32_t n_codes = distinct < 16 ? (uint32_t)distinct : 16u;
-    if (tid < 16 && (uint32_t)tid >= n_codes) cb->dec_lut[tid] = 0;
-    if (tid == 0) {
-        cb->n_codes = n_codes;
-        cb->reserved = 0;
-        cb->covered = covered;
-        cb->total = I.n;
     }
 }
 
