@@ -314,3 +314,50 @@ def test_encode_straight_into_pinned_host_memory(make, n):
     assert host[: m.comp_bytes].numpy().tobytes() == opay
     with pytest.raises(ValueError):
         S.encode(xd, cb, ws, payload=torch.empty(16, dtype=torch.uint8))
+
+
+def test_slot_groups_on_concurrent_streams():
+    """Two groups of slots decoded at the same time on two streams (each a
+    cooperative launch), with plain decodes on a third stream: every output
+    exact and no barrier timeout (status bit 16)."""
+    g = torch.Generator().manual_seed(13)
+    sizes = [int(v) for v in torch.randint(50_000, 3_000_000, (12,), generator=g)]
+    cases = []
+    for k, n in enumerate(sizes):
+        x = W.gaussian_weight(n, seed=900 + k) if k % 4 else W.log_uniform_stress(n, seed=900 + k)
+        xs_h, ocb, opay, om = oracle_case(x)
+        cases.append((xs_h, ocb, opay, om))
+    groups = [cases[0:5], cases[5:10]]
+    plain = cases[10:]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    st = [torch.zeros(1, dtype=torch.int32, device=DEV) for _ in range(3)]
+    results = []
+    for rnd in range(3):
+        outs = []
+        bufs = []
+        for gi, grp in enumerate(groups):
+            slots = [slot_for(c[2], c[3].n) for c in grp]
+            metas = [meta_to_device(c[3], True) for c in grp]
+            luts = [torch.tensor(np.asarray(c[1].dec_lut, np.uint8)).to(DEV) for c in grp]
+            stashes = [stash_for(c[3].comp_bytes) for c in grp]
+            bufs.append((slots, metas, luts, stashes))
+        pl = []
+        for c in plain:
+            pay = torch.frombuffer(bytearray(c[2] + b"\0" * 16), dtype=torch.uint8).to(DEV)
+            pl.append((pay, meta_to_device(c[3], True),
+                       torch.tensor(np.asarray(c[1].dec_lut, np.uint8)).to(DEV), c[3].n))
+        torch.cuda.synchronize()
+        _say("concurrent slot groups, round %d" % rnd)
+        for gi, (slots, metas, luts, stashes) in enumerate(bufs):
+            with torch.cuda.stream(streams[gi]):
+                outs.append(S.decode_slots(slots, metas, luts, [c[3].n for c in groups[gi]], stashes,
+                                           status=st[gi], stream=streams[gi]))
+        with torch.cuda.stream(streams[2]):
+            pouts = [S.decode(p, m, l, n, status=st[2], stream=streams[2]) for p, m, l, n in pl]
+        torch.cuda.synchronize()
+        assert [int(s.item()) for s in st] == [0, 0, 0]
+        for gi, grp in enumerate(groups):
+            for out, c in zip(outs[gi], grp):
+                assert np.array_equal(host_bits(out.cpu()), c[0])
+        for out, c in zip(pouts, plain):
+            assert np.array_equal(host_bits(out.cpu()), c[0])
