@@ -370,10 +370,11 @@ def slot_decode_phase(S, batch, metas_h, x_all, stream, passes):
     region, so the payloads are not cache-resident), then the 64 slot decodes
     are timed with HIP events on the stream they run on (the GPU kept busy
     while the host enqueues them, so the host's marshalling is not timed):
-    one call per tensor, then all 64 as one group (32 per launch).  With the
-    library's default forms (single calls: two launches; groups: one
-    cooperative launch) and with the two-launch form forced for groups.
-    Copies and sleep on the same stream; `torch.cuda._sleep` spins 10M cycles."""
+    one call per tensor, then all 64 as one group (32 per launch), in the
+    library's default two-launch form; the same in the resident form (the
+    GPU has nothing else to run here); and groups in the resident form with
+    its first kernel launched cooperatively.  Copies and sleep on the same
+    stream; `torch.cuda._sleep` spins 10M cycles."""
     import os
     import torch
 
@@ -383,7 +384,7 @@ def slot_decode_phase(S, batch, metas_h, x_all, stream, passes):
     stashes = [torch.empty(c, dtype=torch.uint8, device=x_all.device) for c in comp]
     slots = [o.view(torch.uint8) for o in batch.outs]
 
-    def timed(grouped):
+    def timed(grouped, resident):
         ms = 0.0
         for k in range(passes + 1):   # the first pass untimed (first use of a launch form)
             for i in range(T):
@@ -393,11 +394,12 @@ def slot_decode_phase(S, batch, metas_h, x_all, stream, passes):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             if grouped:
-                S.decode_slots(slots, batch.metas, batch.cbs, batch.ns, stashes, stream=stream)
+                S.decode_slots(slots, batch.metas, batch.cbs, batch.ns, stashes, stream=stream,
+                               resident=resident)
             else:
                 for i in range(T):
                     S.decode_slot(slots[i], batch.metas[i], batch.cbs[i], batch.ns[i], stash,
-                                  stream=stream)
+                                  stream=stream, resident=resident)
             e1.record(stream)
             torch.cuda.synchronize()
             if k:
@@ -413,26 +415,30 @@ def slot_decode_phase(S, batch, metas_h, x_all, stream, passes):
         return {"ms": round(ms, 4), "raw_GBps": round(raw / ms / 1e6, 1),
                 "alg_GBps": round(alg / ms / 1e6, 1), "hbm_frac": round(alg / ms / 1e6 / 8000.0, 4)}
 
-    ms, ms_b = timed(False), timed(True)
-    old = os.environ.get("SPLITZIP_SLOT_LAUNCH")
+    old = os.environ.pop("SPLITZIP_SLOT_LAUNCH", None)
     try:
-        os.environ["SPLITZIP_SLOT_LAUNCH"] = "two"
-        ms2_b = timed(True)
+        ms, ms_b = timed(False, False), timed(True, False)
+        msr, msr_b = timed(False, True), timed(True, True)
         os.environ["SPLITZIP_SLOT_LAUNCH"] = "coop"
-        msc = timed(False)
+        msc_b = timed(True, True)
     finally:
         if old is None:
-            del os.environ["SPLITZIP_SLOT_LAUNCH"]
+            os.environ.pop("SPLITZIP_SLOT_LAUNCH", None)
         else:
             os.environ["SPLITZIP_SLOT_LAUNCH"] = old
     del stashes
-    return dict(rec(ms), calls=T, form="two launches per call",
-                batched=dict(rec(ms_b), launches=(T + 31) // 32, form="one cooperative launch per 32"),
-                batched_two_launch=rec(ms2_b), single_coop=rec(msc),
-                note="payload at the head of the output buffer; cooperative form: the inputs of "
+    return dict(rec(ms), calls=T, form="two-launch form (two kernels per call)",
+                batched=dict(rec(ms_b), launches=(T + 31) // 32,
+                             form="two-launch form, two kernels per 32 slots"),
+                resident=dict(rec(msr), form="resident form, ordinary launch (+ a finishing "
+                                             "kernel) per call"),
+                batched_resident=dict(rec(msr_b), form="resident form, one ordinary launch per "
+                                                       "32 slots (+ a finishing kernel)"),
+                batched_cooperative=rec(msc_b),
+                note="payload at the head of the output buffer; resident form: the inputs of "
                      "the tiles whose output overlaps it wait in registers across a grid "
-                     "barrier (a cooperative launch costs ~14 us more than an ordinary one); "
-                     "two-launch form: they are stashed first, i.e. written and read once more")
+                     "barrier; two-launch form: they are stashed first, i.e. written and read "
+                     "once more")
 
 
 def h2d_pipeline(S, batch, metas_h, x_all, dev, count):
@@ -575,7 +581,11 @@ def main():
         return
     if args.small_only:
         only = None if args.small_only == "all" else args.small_only
-        print(json.dumps({"small_configs": small_configs(S, W, dev, stream, only=only)}))
+        line = {"small_configs": small_configs(S, W, dev, stream, only=only)}
+        if args.copy_calibration:
+            copy_calibration(torch, dev)
+            line["copy_calibration_bytes"] = 512 << 20
+        print(json.dumps(line))
         return
     T = 2 * LAYERS
 
@@ -777,12 +787,18 @@ def main():
                          "note": "pages' figures on LLM KV activations, other hardware"},
     }
     if args.copy_calibration:
-        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
+        copy_calibration(torch, dev)
         line["copy_calibration_bytes"] = 512 << 20
     print(json.dumps(line))
+
+
+def copy_calibration(torch, dev):
+    """One 512 MiB device-to-device copy, the last dispatch of the run: the
+    reference for scaling hardware byte counters."""
+    src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def counted_traffic(kernel):

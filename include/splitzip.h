@@ -268,16 +268,19 @@ int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const spli
  *               overlapping the slot; it receives what a later step reads
  *               after the slot head has been overwritten (see below)
  *   d_status    optional, as for splitzip_decode (escapes are re-applied from
- *               the decoded sign and mantissa); bit 16 reports a grid
- *               barrier of the cooperative form that gave up waiting (about
- *               a second; the output is then not trustworthy)
- * Two kernels on `stream`: the first stashes the inputs of every tile whose
- * output overlaps the payload, and the escape sections, and decodes the
- * other tiles; the second decodes the stashed tiles.  With d_status, a
- * validation kernel follows.  Calls that share a stash must be ordered on
- * one stream.  (splitzip_decode_slot_batch takes one cooperative kernel per
- * group instead, see there; the environment variable SPLITZIP_SLOT_LAUNCH =
- * "coop" or "two" selects either form for every call.)
+ *               the decoded sign and mantissa)
+ * Two kernels on `stream` (and, with d_status, a validation kernel): the
+ * first stashes the inputs of every tile whose output overlaps the payload,
+ * and the escape sections, and decodes the other tiles; the second decodes
+ * the stashed tiles.  Calls that share a stash must be ordered on one
+ * stream.  The kernels' workgroups depend on no other workgroup, so the
+ * decode shares the GPU with concurrent work as any kernel does;
+ * splitzip_decode_slot_batch_resident is faster on a GPU the decode has to
+ * itself.  The environment variable SPLITZIP_SLOT_LAUNCH selects a form for
+ * every slot decode of the process: "two" (this one), "one" (the resident
+ * form) or "coop" (the resident form, its first kernel launched
+ * cooperatively); SPLITZIP_SLOT_WAIT_US sets the resident form's bounded
+ * wait in microseconds (0: nearly every barrier gives up).
  * Synchronous errors: INVALID (also for overlapping slot and stash), HIP. */
 int splitzip_decode_slot(uint8_t *d_slot, uint64_t slot_bytes, const splitzip_meta *d_meta,
                          const uint8_t *d_dec_lut, uint64_t n, uint8_t *d_stash,
@@ -286,21 +289,39 @@ int splitzip_decode_slot(uint8_t *d_slot, uint64_t slot_bytes, const splitzip_me
 /* In-place decode of a group of slots (page "SplitZip in DDO -- VMM routes",
  * "Route B (fallback)": the staging route expands the slots of an execution
  * group after their upload, on the upload stream): the
- * same result as splitzip_decode_slot on every item in order.  Where the
- * device supports cooperative launches, up to 32 items share one cooperative
- * kernel: for each item, every workgroup holds the inputs of up to three whole
- * tiles whose output overlaps the payload in registers, decodes the tiles
- * past the payload, and writes the held tiles after a grid barrier (one
- * item's stores overlap the next one's loads); overlapping tiles beyond that
- * reach, and a partial last one, go through the stash, and so do the escape
- * sections when a later step needs them (validation, an unmarked stream,
- * stashed tiles).  A group of one item, or a device without cooperative
- * launches, takes the two-kernel form.  Each item needs its own stash; no
- * slot or stash may overlap another item's buffers.  d_status (optional)
- * collects the status bits of all items.
+ * same result as splitzip_decode_slot on every item in order, up to 32
+ * items sharing each launch of its two kernels.  Each item needs its own
+ * stash; no slot or stash may overlap another item's buffers.  d_status
+ * (optional) collects the status bits of all items.
  * Synchronous errors: INVALID (any item; nothing is enqueued), HIP. */
 int splitzip_decode_slot_batch(const splitzip_slot_item *items, uint32_t count, int32_t *d_status,
                                void *stream);
+
+/* In-place decode of a group of slots (page "SplitZip in DDO -- VMM routes",
+ * as splitzip_decode_slot_batch): the same result, in a form that needs the
+ * whole grid resident at once and pays off on a GPU that the decode has to
+ * itself (e.g. a bulk restore between compute phases).  Two kernels per 32
+ * items on `stream`.  The first is an ordinary launch of as many workgroups
+ * as the GPU keeps resident at once: each decodes its tiles whose output
+ * lies past the payload, loads the inputs of up to three whole tiles whose
+ * output overlaps the payload into registers, waits on a grid barrier (every
+ * load of the payload done) and then writes them, one barrier per item (one
+ * item's stores overlap the next one's loads); overlapping tiles beyond that
+ * reach, a partial last one, and the escape sections when a later step needs
+ * them go through the stash.  The barrier's wait is bounded: when concurrent
+ * work keeps part of the grid from being placed (checked after about 20 us)
+ * or the wait passes 200 us, the launch gives up, stashes its held tiles
+ * instead and leaves them, and every later item of the launch, to the
+ * second kernel -- the same result, later (then slower than
+ * splitzip_decode_slot_batch, which shares the GPU without waiting).  The
+ * second kernel also decodes an item whose escape stream is not marked
+ * ascending (its escapes applied by index); otherwise it reads one word and
+ * ends.  The barrier's counters live in the library, 64 blocks per device,
+ * one per stream that used one last: calls may run at the same time on at
+ * most 64 streams of a device.  Arguments, stash rules and errors as for
+ * splitzip_decode_slot_batch. */
+int splitzip_decode_slot_batch_resident(const splitzip_slot_item *items, uint32_t count,
+                                        int32_t *d_status, void *stream);
 
 /* Batched forms of calibrate / encode / decode for many tensors with one
  * codebook each (the per-tensor granularity of page 1, SplitZipCodebook):

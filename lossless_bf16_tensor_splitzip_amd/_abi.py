@@ -32,7 +32,6 @@ DEC_BAD_META = 1
 DEC_ESC_OUT_OF_RANGE = 2
 DEC_POS_GE_CHUNK = 4
 DEC_NOT_INCREASING = 8
-DEC_BARRIER_TIMEOUT = 16       # cooperative in-place decode only
 
 
 class Codebook(ctypes.Structure):
@@ -113,6 +112,7 @@ SIGNATURES = {
     "splitzip_decode": (ctypes.c_int, [_P, _U64, _P, _P, _P, _U64, _P, _P]),
     "splitzip_decode_slot": (ctypes.c_int, [_P, _U64, _P, _P, _U64, _P, _U64, _P, _P]),
     "splitzip_decode_slot_batch": (ctypes.c_int, [_P, ctypes.c_uint32, _P, _P]),
+    "splitzip_decode_slot_batch_resident": (ctypes.c_int, [_P, ctypes.c_uint32, _P, _P]),
     "splitzip_workspace_size_batch": (_SZ, [ctypes.POINTER(ctypes.c_uint64), ctypes.c_uint32]),
     "splitzip_calibrate_batch": (ctypes.c_int, [_P, ctypes.c_uint32, _P, _SZ, _P]),
     "splitzip_encode_batch": (ctypes.c_int, [_P, ctypes.c_uint32, _P, _SZ, _P]),
@@ -247,6 +247,10 @@ def splitzip_decode_slot(d_slot: int, slot_bytes: int, d_meta: int, d_dec_lut: i
 
 def splitzip_decode_slot_batch(items, count: int, d_status: int, stream: int) -> int:
     return lib().splitzip_decode_slot_batch(_items_ptr(items), count, d_status, stream)
+
+
+def splitzip_decode_slot_batch_resident(items, count: int, d_status: int, stream: int) -> int:
+    return lib().splitzip_decode_slot_batch_resident(_items_ptr(items), count, d_status, stream)
 
 
 def splitzip_workspace_size_batch(ns) -> int:

@@ -178,12 +178,17 @@ def _lut_ptr(cb_or_dec_lut: torch.Tensor) -> int:
 
 def decode_slot(slot: torch.Tensor, meta: torch.Tensor, cb_or_dec_lut: torch.Tensor, n: int,
                 stash: torch.Tensor, status: torch.Tensor | None = None,
-                stream=None) -> torch.Tensor:
+                stream=None, resident: bool = False) -> torch.Tensor:
     """Decode in place: ``slot`` (contiguous device tensor of any dtype, at
     least max(2n, payload_size(n, 0)) bytes) holds the payload at its head;
     afterwards its first 2n bytes hold the n bfloat16 values, returned as a
     flat bfloat16 view.  ``stash`` is device scratch of at least comp_bytes
-    bytes that does not overlap the slot."""
+    bytes that does not overlap the slot.  ``resident`` takes the form that
+    needs the whole grid resident at once (faster on a GPU the decode has to
+    itself, see ``decode_slots``)."""
+    if resident:
+        return decode_slots([slot], [meta], [cb_or_dec_lut], [n], [stash], status=status,
+                            stream=stream, resident=True)[0]
     if not slot.is_contiguous():
         # page 1, decode_slot_into: the slot must be contiguous
         raise ValueError("the slot tensor must be contiguous")
@@ -201,9 +206,13 @@ def decode_slot(slot: torch.Tensor, meta: torch.Tensor, cb_or_dec_lut: torch.Ten
 
 
 def decode_slots(slots, metas, cbs_or_luts, ns, stashes, status: torch.Tensor | None = None,
-                 stream=None):
+                 stream=None, resident: bool = False):
     """In-place decode of a group of slots (see ``decode_slot``), up to 32
-    per launch.  Returns the flat bfloat16 views of the slots."""
+    per launch.  Returns the flat bfloat16 views of the slots.  With
+    ``resident`` the library's resident form runs (one grid barrier per
+    slot, overlapping tiles held in registers; it gives up and finishes the
+    slots later when concurrent work keeps its grid from being placed), else
+    the two-launch form, which shares the GPU with concurrent work."""
     count = len(slots)
     if not (len(metas) == len(cbs_or_luts) == len(ns) == len(stashes) == count):
         raise ValueError("one meta, codebook, size and stash per slot")
@@ -224,8 +233,8 @@ def decode_slots(slots, metas, cbs_or_luts, ns, stashes, status: torch.Tensor | 
     st_ptr = _status_ptr(status)
     dev = _gpu_of(*slots, *metas) if count else torch.device("cuda")
     _same_gpu(dev, *slots, *stashes, *metas, *cbs_or_luts, status)
-    _abi._check("splitzip_decode_slot_batch",
-                _abi.splitzip_decode_slot_batch(items, count, st_ptr, _stream(stream, dev)))
+    fn = "splitzip_decode_slot_batch_resident" if resident else "splitzip_decode_slot_batch"
+    _abi._check(fn, getattr(_abi, fn)(items, count, st_ptr, _stream(stream, dev)))
     return [raw[: 2 * n].view(torch.bfloat16) for raw, n in zip(raws, ns)]
 
 

@@ -56,6 +56,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -1121,6 +1122,9 @@ struct DecArgs {
     int32_t *status;
     uint64_t *order_sync;                 // this device's arrival counters (below)
     uint64_t order_ticket;                // this call's first counter, and its tag
+    uint64_t *hold_block;                 // one-kernel in-place decode: the call's barrier block,
+    uint32_t hold_tag;                    // its tag,
+    uint32_t wait_ticks;                  // and the barrier's bounded wait (10 ns ticks)
 };
 
 // Arrival counters of the order-independent escape pass (streams not marked
@@ -1500,26 +1504,34 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_slot_finish(DecArgs a) {
 // ---------------------------------------------------------------------------
 //
 // Tile t writes slot bytes [2tT, 2(t+1)T) (T = 8192 elements); the tiles from
-// t_split = ceil(comp / 2T) on write only past the payload.  In a grid that
-// is resident as a whole (cooperative launch), every workgroup first decodes
-// its tiles from t_split on, then loads the pk/sm inputs of its tiles wg +
-// jG below t_split (j < kHold) into registers, their escape entries having
-// gone to LDS; after a grid barrier it writes the held tiles straight from
-// the registers, then their escapes.  After the barrier a workgroup reads no
-// slot byte and only the stash bytes it wrote itself, so the barrier needs
-// no cache flush: it only has to order the held tiles' stores after every
-// load of the first phase.  Overlapping tiles beyond the registers' reach
-// (more than kHold * G of them), and a partial last one, go through the
-// stash as in the two-launch form.  A group of slots takes one barrier per
-// slot, the stores of one slot overlapping the loads of the next.  A stream
-// not marked ascending takes a second barrier (with device-scope fences) and
-// an order-independent pass over all its escapes, read back from the stash.
-// Compared with the two-launch form, the held tiles' inputs never go through
-// memory a second time; a cooperative launch costs about 14 us more than an
-// ordinary one, so only groups of slots take this form.
+// t_split = ceil(comp / 2T) on write only past the payload.  One ordinary
+// launch with as many workgroups as the GPU keeps resident at once: every
+// workgroup first decodes its tiles from t_split on, then loads the pk/sm
+// inputs of its tiles wg + jG below t_split (j < kHold) into registers,
+// their escape entries having gone to LDS; after a grid barrier it writes
+// the held tiles straight from the registers, then their escapes.  After the
+// barrier a workgroup reads no slot byte and only the stash bytes it wrote
+// itself, so the barrier needs no cache flush: it only has to order the held
+// tiles' stores after every load of the first phase.  Overlapping tiles
+// beyond the registers' reach (more than kHold * G of them), and a partial
+// last one, go through the stash as in the two-launch form.  A group of
+// slots takes one barrier per slot, the stores of one slot overlapping the
+// loads of the next.
+//
+// An ordinary launch does not promise that the whole grid is resident (other
+// work may hold part of the GPU), so the barrier's wait is bounded: a
+// workgroup that has waited wait_ticks (10 ns each) marks the round aborted
+// unless its last arrival has already come, and that arrival's atomic on the
+// top counter decides: go unless a mark came first.  An abort is sticky for
+// the rest of the launch (the grid stayed partly absent).  On an abort every
+// workgroup stashes its held tiles' inputs (and its share of the escape
+// sections) and leaves the slot to k_decode_slot_defer, launched after this
+// kernel, which decodes the stashed tiles as the two-launch form's second
+// kernel does.  A stream not marked ascending is always left to it (its
+// escapes are applied by index once every tile is decoded).  Neither outcome
+// depends on which workgroups were resident.
 constexpr int kHold = 3;                   // held tiles per workgroup and tensor
 constexpr uint32_t kHoldEsc = 512;         // escape entries per held tile in LDS
-constexpr uint32_t kCoopSpin = 1u << 20;   // barrier: polls before giving up (about a second)
 constexpr int kCoopTile = kDecThreads * kUnit * kDecUnits;   // 8192 elements
 constexpr int kCoopUnits = kCoopTile / kUnit;                // 8-element units per tile
 static_assert(kHold <= kDecThreads / 64, "one wave finds each held tile's escapes");
@@ -1532,106 +1544,256 @@ struct CoopLds {
     uint64_t dr0, dr1;                     // escape ranks of a direct tile
 };
 
-// Grid barrier of the cooperative decode.  Same-address atomics serialise
-// at the memory side, so the grid arrives in two levels: workgroups on the
-// counter of their group of kCoopGroup, the last of each group on the top
-// counter; the last arrival of a round writes the round's release word to
-// every group's flag, and each group polls only its own flag.  Counters and
-// flags are tagged ((tag << 32) | count, see tagged_claim): a call takes a
-// block of them by its ticket and claims what it increments, so nothing is
-// cleared between calls; after its last barrier every workgroup arrives once
-// more, and the last of those arrivals puts the block back to (tag << 32)
-// so that a replay of the same arguments starts from zero.
+// Grid barrier of the one-kernel in-place decode.  Same-address atomics
+// serialise at the memory side, so the grid arrives in two levels:
+// workgroups on the counter of their group of kCoopGroup, the last of each
+// group on the top counter, whose arrival tells it whether the round is
+// complete.  Whoever knows a round's outcome writes it to every group's
+// flag, and each group polls only its own flag.  The group and top counters
+// are tagged ((tag << 32) | value, see tagged_claim) and claimed by the
+// launch that increments them.  Besides them each group has a start word
+// and a leave word, and the launch a leave word and a pending word; the last
+// workgroup to leave puts all of them back to (tag << 32), so that the next
+// launch on the block, or a replay of the same arguments, starts from zero.
 constexpr uint32_t kCoopGroup = 16;                        // workgroups per group counter
-constexpr uint32_t kCoopMaxGrid = 4096;
+constexpr uint32_t kCoopMaxGrid = 2048;
 constexpr uint32_t kCoopGroups = kCoopMaxGrid / kCoopGroup;
 constexpr uint32_t kCoopLine = 16;                         // words per counter (128 bytes)
-constexpr uint32_t kCoopWords = (2 * kCoopGroups + 1) * kCoopLine;
-constexpr uint32_t kCoopBlocks = 16;                       // calls in flight with distinct blocks
+constexpr uint32_t kCoopWords = (2 * kCoopGroups + 2) * kCoopLine;
+constexpr uint32_t kCoopBlocks = 64;                       // streams with blocks of their own
+constexpr uint64_t kGo = 1, kAbort = 2;
+constexpr uint64_t kHoldWaitUs = 200;   // barrier wait before a workgroup gives up
+constexpr uint32_t kStartWaitTicks = 2000;   // 20 us: the wait while part of the grid has not started
 __device__ __align__(256) uint64_t g_coop_sync[kCoopBlocks * kCoopWords];
 
 struct CoopBar {
-    uint64_t *blk;        // the call's block: group counters, group flags, top counter
+    uint64_t *blk;        // the launch's block of counters and flags
     uint32_t tag, passed;
 };
 
 __device__ inline uint32_t coop_ngroups() { return (gridDim.x + kCoopGroup - 1) / kCoopGroup; }
+__device__ inline uint32_t coop_gsize(uint32_t g) { return min(kCoopGroup, gridDim.x - g * kCoopGroup); }
 
 __device__ inline uint64_t *coop_grp(const CoopBar &b, uint32_t g) { return b.blk + g * kCoopLine; }
 __device__ inline uint64_t *coop_flag(const CoopBar &b, uint32_t g) {
     return b.blk + (kCoopGroups + g) * kCoopLine;
 }
+// the number of the group's workgroups that have started, and that have left
+__device__ inline uint64_t *coop_started(const CoopBar &b, uint32_t g) { return coop_flag(b, g) + 1; }
+__device__ inline uint64_t *coop_left(const CoopBar &b, uint32_t g) { return coop_flag(b, g) + 2; }
 __device__ inline uint64_t *coop_top(const CoopBar &b) { return b.blk + 2 * kCoopGroups * kCoopLine; }
+__device__ inline uint64_t *coop_top_left(const CoopBar &b) { return coop_top(b) + 1; }
+// (tag << 32) | (first aborted round << 8) | 1 when some slot of the launch
+// was left to the second kernel
+__device__ inline uint64_t *coop_pending(const CoopBar &b) {
+    return b.blk + (2 * kCoopGroups + 1) * kCoopLine;
+}
+__device__ inline void coop_set_pending(const CoopBar &b) {
+    __hip_atomic_store(coop_pending(b), ((uint64_t)b.tag << 32) | 1u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Claims this workgroup's group counter (and, for the first workgroup of a
 // group, the top counter: every arrival on it follows the arrival of some
-// group's first workgroup, which claimed it before arriving).
+// group's first workgroup, which claimed it before arriving), and counts
+// the workgroup on its group's start word (an atomic whose result it does
+// not wait for; start and leave words are not tagged, see coop_leave).
 __device__ inline void coop_bar_init(CoopBar &b, uint64_t *blk, uint32_t tag) {
     b.blk = blk;
     b.tag = tag;
     b.passed = 0;
     if (threadIdx.x == 0) {
-        uint64_t *c = coop_grp(b, blockIdx.x / kCoopGroup);
+        const uint32_t g = blockIdx.x / kCoopGroup;
+        __hip_atomic_fetch_add(coop_started(b, g), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint64_t *c = coop_grp(b, g);
         counter_claim(c, ld_agent(c), tag);
-        if (blockIdx.x % kCoopGroup == 0) counter_claim(coop_top(b), ld_agent(coop_top(b)), tag);
+        if (g * kCoopGroup == blockIdx.x) counter_claim(coop_top(b), ld_agent(coop_top(b)), tag);
     }
 }
 
+// The top counter's low word: the arrivals of the launch's groups in its
+// low 24 bits, and in the high 8 bits the first round that a workgroup gave
+// up waiting on (0: none).  An abort is sticky: that round and every later
+// one of the launch abort, so the first aborted round decides every verdict.
+constexpr uint32_t kCountMask = (1u << 24) - 1;
+__device__ inline uint32_t top_count(uint64_t v) { return (uint32_t)v & kCountMask; }
+__device__ inline uint32_t top_abort_round(uint64_t v) { return (uint32_t)v >> 24 & 0xFFu; }
+__device__ inline uint64_t round_verdict(uint32_t abort_round, uint32_t round) {
+    return abort_round != 0 && abort_round <= round ? kAbort : kGo;
+}
+static_assert(kMaxBatch < 0xFF, "rounds fit the top counter's abort field");
+static_assert(kMaxBatch * kCoopGroups <= kCountMask, "arrivals fit the top counter");
+
 // Arrival of this workgroup for round `round` (thread 0); true for the last
-// arrival of the round over the whole grid.
-__device__ inline bool coop_arrive(const CoopBar &b, uint32_t round) {
+// arrival of the round over the whole grid, which also learns the first
+// aborted round so far.  Until a round aborts, no workgroup arrives for a
+// round before every one has arrived for the previous one, so the counts
+// identify each round's last arrival.  After an abort, workgroups that gave
+// up go on while others have yet to arrive, the counters mix rounds, and a
+// "last arrival" may be misplaced or missing -- but it then sees the abort
+// (set before any workgroup went on), so every verdict stays an abort, and
+// a workgroup that finds no flag gives up by itself.
+__device__ inline bool coop_arrive(const CoopBar &b, uint32_t round, uint32_t &abort_round) {
     const uint32_t group = blockIdx.x / kCoopGroup;
-    const uint32_t gsize = min(kCoopGroup, gridDim.x - group * kCoopGroup);
+    abort_round = 0;
     const uint64_t p = __hip_atomic_fetch_add(coop_grp(b, group), 1ull, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
-    if ((uint32_t)p + 1u != gsize * round) return false;
+    if ((uint32_t)p + 1u != coop_gsize(group) * round) return false;
     const uint64_t q = __hip_atomic_fetch_add(coop_top(b), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return (uint32_t)q + 1u == coop_ngroups() * round;
+    abort_round = top_abort_round(q);
+    return top_count(q) + 1u == coop_ngroups() * round;
 }
 
-// Every workgroup is resident (cooperative launch), so the wait ends; it is
-// bounded anyway and sets status bit 16 when the bound trips.
-__device__ inline void coop_barrier(CoopBar &b, int32_t *status, bool fence) {
-    if (fence) __threadfence();
+// Whether every workgroup of the grid has started (thread 0; read only by a
+// workgroup that has waited a while).  A workgroup that has started runs to
+// its end on its compute unit, so once every one has started every barrier
+// of the launch completes; while some have not, other work holds the
+// compute units they need.
+__device__ inline bool coop_all_started(const CoopBar &b) {
+    const uint32_t ng = coop_ngroups();
+    bool ok = true;
+    for (uint32_t g0 = 0; g0 < ng && ok; g0 += 8) {
+        uint64_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = g0 + j < ng ? ld_agent(coop_started(b, g0 + j)) : 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (g0 + j < ng) ok = ok && (uint32_t)v[j] >= coop_gsize(g0 + j);
+    }
+    return ok;
+}
+
+// A workgroup that has waited too long on round `round` marks it aborted
+// unless the round is already complete (its count reached) or an earlier
+// round aborted.  0: the round completed first (its last arrival then
+// decides it from the abort field it saw); 1: the round aborts, marked by
+// another workgroup (which publishes it); 2: marked by this one.
+__device__ inline int coop_poison(const CoopBar &b, uint32_t round) {
+    uint64_t *top = coop_top(b);
+    uint64_t cur = ld_agent(top);
+    counter_claim(top, cur, b.tag);   // (its group's first workgroup may not have run)
+    if ((uint32_t)(cur >> 32) != b.tag) cur = ld_agent(top);
+    for (int k = 0; k < 4096; ++k) {
+        if ((uint32_t)(cur >> 32) != b.tag) return 2;   // (not a state this launch produces)
+        const uint32_t ar = top_abort_round(cur);
+        if (ar != 0) return ar <= round ? 1 : 0;
+        if (top_count(cur) >= coop_ngroups() * round) return 0;
+        if (__hip_atomic_compare_exchange_strong(top, &cur, cur | (uint64_t)round << 24, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            return 2;
+    }
+    return 2;
+}
+
+// One round; true when the grid goes on (every workgroup arrived before any
+// gave up, in this round or an earlier one).  A waiting workgroup gives up
+// after kStartWaitTicks (staggered by 1 us over the workgroups of a group,
+// so that one of them usually decides for all) if the grid has not all
+// started by then, else after wait_ticks.  Whoever decides the verdict
+// publishes (round << 2) | verdict to every group's flag: the round's last
+// arrival, or the workgroup that marked the launch aborted.  A flag may be overwritten by an older round's late
+// publication; a waiter reads its round's verdict from any flag of this
+// round or later, or of an earlier aborted round (aborts are sticky), and
+// otherwise keeps waiting.  `st` is a word of LDS.
+__device__ inline bool coop_barrier(CoopBar &b, uint32_t wait_ticks, bool fence, uint32_t *st) {
+    if (fence) __threadfence();   // (stash bytes other workgroups read after a go)
     wait_vector_memory();
     __syncthreads();
     ++b.passed;
-    const uint64_t want = ((uint64_t)b.tag << 32) | b.passed;
+    const uint32_t r = b.passed;
     if (threadIdx.x < 64) {
-        const int last = threadIdx.x == 0 ? (int)coop_arrive(b, b.passed) : 0;
-        if (__shfl(last, 0, 64))
-            for (uint32_t g = threadIdx.x; g < coop_ngroups(); g += 64)
-                __hip_atomic_store(coop_flag(b, g), want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint64_t verdict = 0;
+        int publish = 0;
         if (threadIdx.x == 0) {
-            const uint64_t *f = coop_flag(b, blockIdx.x / kCoopGroup);
-            uint32_t k = 0;
-            for (;;) {
-                const uint64_t v = ld_agent(f);
-                if ((v >> 32) == b.tag && (uint32_t)v >= b.passed) break;
-                if (++k > kCoopSpin) {
-                    if (status) atomicOr(status, 16);
-                    break;
+            uint32_t ar;
+            if (coop_arrive(b, r, ar)) {
+                verdict = round_verdict(ar, r);
+                publish = 1;
+            } else {
+                const uint64_t *f = coop_flag(b, blockIdx.x / kCoopGroup);
+                const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                const uint32_t start_ticks =
+                    min(wait_ticks, kStartWaitTicks + blockIdx.x % kCoopGroup * 100u);
+                bool waited = false, started = false;
+                for (uint32_t k = 1;; ++k) {
+                    const uint64_t v = ld_agent(f);
+                    if ((uint32_t)(v >> 32) == b.tag) {
+                        const uint32_t fr = (uint32_t)v >> 2;
+                        if ((v & 3u) == kAbort && fr <= r) {   // this round or an earlier one aborted
+                            verdict = kAbort;
+                            break;
+                        }
+                        if ((v & 3u) == kAbort && fr > r) {    // a later round aborted: the first decides
+                            verdict = round_verdict(top_abort_round(ld_agent(coop_top(b))), r);
+                            break;
+                        }
+                        if ((v & 3u) == kGo && fr >= r) {
+                            verdict = kGo;
+                            break;
+                        }
+                    }
+                    if (!waited && (k & 7) == 0) {
+                        const uint64_t dt = __builtin_amdgcn_s_memrealtime() - t0;
+                        bool give_up = dt > wait_ticks;
+                        if (!give_up && !started && dt > start_ticks) {
+                            started = coop_all_started(b);
+                            give_up = !started;
+                        }
+                        if (give_up) {
+                            waited = true;   // once: afterwards the round is decided either way
+                            const int pz = coop_poison(b, r);
+                            if (pz) {
+                                verdict = kAbort;
+                                publish = pz == 2;
+                                break;
+                            }
+                        }
+                    }
+                    __builtin_amdgcn_s_sleep(1);
                 }
-                __builtin_amdgcn_s_sleep(1);
             }
+            if (verdict != kGo) coop_set_pending(b);
+            *st = (uint32_t)verdict;
+        }
+        if (__shfl(publish, 0, 64)) {
+            const uint64_t w = ((uint64_t)b.tag << 32) | ((uint64_t)r << 2) | __shfl(verdict, 0, 64);
+            for (uint32_t g = threadIdx.x; g < coop_ngroups(); g += 64)
+                __hip_atomic_store(coop_flag(b, g), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     __syncthreads();
     if (fence) __threadfence();
+    return *st == kGo;
 }
 
-// The final arrival; the last one puts the block back for a replay.
-__device__ inline void coop_leave(CoopBar &b) {
+// Every workgroup leaves once, on leave words of its own (two levels, as the
+// rounds), so the last to leave is known even when aborted rounds mixed the
+// round counters.  It puts the block back to (tag << 32); with `record` (the
+// first kernel) it records the first aborted round in the pending word for
+// the second kernel and keeps a pending mark, else it clears the word.  Its
+// reads follow every workgroup's stores, which precede their leaving.
+__device__ inline void coop_leave(CoopBar &b, bool record) {
     wait_vector_memory();
     __syncthreads();
-    if (threadIdx.x == 0 && coop_arrive(b, b.passed + 1)) {
-        const uint64_t z = (uint64_t)b.tag << 32;
-        for (uint32_t g = 0; g < coop_ngroups(); ++g) {
-            __hip_atomic_store(coop_grp(b, g), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(coop_flag(b, g), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __hip_atomic_store(coop_top(b), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x != 0) return;
+    const uint32_t g = blockIdx.x / kCoopGroup;
+    const uint64_t p = __hip_atomic_fetch_add(coop_left(b, g), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)p + 1u != coop_gsize(g)) return;
+    const uint64_t q = __hip_atomic_fetch_add(coop_top_left(b), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)q + 1u != coop_ngroups()) return;
+    const uint64_t z = (uint64_t)b.tag << 32;
+    const uint32_t ar = top_abort_round(ld_agent(coop_top(b)));
+    for (uint32_t k = 0; k < coop_ngroups(); ++k) {
+        __hip_atomic_store(coop_grp(b, k), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(coop_flag(b, k), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(coop_started(b, k), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(coop_left(b, k), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    __hip_atomic_store(coop_top(b), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(coop_top_left(b), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t pend = z;
+    if (record && (ar != 0 || ld_agent(coop_pending(b)) == (z | 1u))) pend = z | (uint64_t)ar << 8 | 1u;
+    __hip_atomic_store(coop_pending(b), pend, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Dense values of the first cnt < T elements of a tile into the LDS tile,
@@ -1739,11 +1901,12 @@ __device__ inline void finish_tile(CoopLds &sh, bool patch, const int32_t *cid, 
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kDecThreads) void k_decode_slot_coop(DecArgs a) {
+// (5 workgroups per compute unit: at most 96 VGPRs, 1,280 resident workgroups)
+__global__ __launch_bounds__(kDecThreads, 5) void k_decode_slot_hold(DecArgs a) {
     __shared__ CoopLds sh;
-    // the call's barrier block (order_sync) and tag (order_ticket + 1)
+    __shared__ uint32_t verdict;
     CoopBar bar;
-    coop_bar_init(bar, a.order_sync, (uint32_t)a.order_ticket + 1u);
+    coop_bar_init(bar, a.hold_block, a.hold_tag);
 
 #pragma unroll 1
     for (uint32_t item = 0; item < a.count; ++item) {
@@ -1763,6 +1926,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_slot_coop(DecArgs a) {
         const uint32_t chunk = (uint32_t)I.meta->chunk_size;
         const bool ascending = (I.meta->flags & SPLITZIP_META_ASCENDING) != 0;
         const bool patch = e && ascending;   // escapes applied tile by tile
+        // an unmarked stream with escapes is left to k_decode_slot_defer whole
+        const bool deferred = e && !ascending;
         // A tensor whose escapes average more than 512 per tile is patched
         // tile by tile in LDS; a sparser one has its dense values stored
         // straight from registers and its escapes stored after them.
@@ -1786,7 +1951,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_slot_coop(DecArgs a) {
         const uint32_t last_cnt = (uint32_t)(I.n - (tiles - 1) * kCoopTile);
         const bool part_held = last_cnt < kCoopTile && tiles - 1 < t_split;
         const uint64_t t_whole = part_held ? tiles - 1 : t_split;   // whole tiles below t_split
-        const uint64_t reach = (uint64_t)kHold * G;
+        const uint64_t reach = deferred ? 0 : (uint64_t)kHold * G;
         const bool mine_part = part_held && (tiles - 1) % G == wg;
         // Stashed tiles search and patch their escapes after the barrier,
         // from the stash: then the escape sections go there first, and the
@@ -1928,7 +2093,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_slot_coop(DecArgs a) {
                 hpk[j][u] = 0;
                 hsm[j][u] = u32x2{0u, 0u};
             }
-            if (t < t_whole) {
+            if (t < t_whole && !deferred) {
                 const uint32_t *pkt = pk + t * kCoopUnits;
                 const u32x2 *smt = sm + t * kCoopUnits;
 #pragma unroll
@@ -1938,7 +2103,39 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_slot_coop(DecArgs a) {
                 }
             }
         }
-        coop_barrier(bar, a.status, esc_to_stash && patch && stashed);
+        if (deferred) {
+            if (wg == 0 && tid == 0) coop_set_pending(bar);
+            continue;
+        }
+        if (!coop_barrier(bar, a.wait_ticks, patch && stashed, &verdict)) {
+            // aborted: the held tiles' inputs and this workgroup's share of
+            // the escape sections to the stash, for k_decode_slot_defer
+#pragma unroll
+            for (int j = 0; j < kHold; ++j) {
+                const uint64_t t = wg + (uint64_t)j * G;
+                if (t >= t_whole) break;
+                uint32_t *spk = reinterpret_cast<uint32_t *>(I.stash) + t * kCoopUnits;
+                u32x2 *ssm = reinterpret_cast<u32x2 *>(I.stash + L0.off_sm) + t * kCoopUnits;
+#pragma unroll
+                for (int u = 0; u < kDecUnits; ++u) {
+                    spk[u * kDecThreads + tid] = hpk[j][u];
+                    ssm[u * kDecThreads + tid] = hsm[j][u];
+                }
+            }
+            if (e && !esc_to_stash) {
+                const uint64_t bytes = L.total - L.off_cid;
+                const uint32_t *src = reinterpret_cast<const uint32_t *>(I.payload + L.off_cid);
+                uint32_t *dst = reinterpret_cast<uint32_t *>(I.stash + L.off_cid);
+                for (uint64_t w = (uint64_t)wg * kDecThreads + tid; w < bytes / 4;
+                     w += (uint64_t)G * kDecThreads)
+                    dst[w] = src[w];
+                if (wg == 0 && tid < (uint32_t)(bytes & 3)) {
+                    const uint64_t b = L.off_cid + (bytes & ~uint64_t(3)) + tid;
+                    I.stash[b] = I.payload[b];
+                }
+            }
+            continue;
+        }
 
         // ---- phase 2: the held tiles (dense values straight from the
         // registers, or through LDS for a tile with many escapes), their
@@ -2001,20 +2198,104 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_slot_coop(DecArgs a) {
                 finish_tile(sh, patch, scid, slpos, sev, e, I.n, chunk, base, last_cnt, I.out, tid);
             }
         }
-        if (e && !ascending) {
-            coop_barrier(bar, a.status, true);
-            // every escape, in any order, from the stash; the sign and
-            // mantissa from the decoded value
-            for (uint64_t r = (uint64_t)wg * kDecThreads + tid; r < e; r += (uint64_t)G * kDecThreads) {
-                const int32_t c = scid[r];
-                if (c < 0) continue;
-                const uint64_t idx = (uint64_t)c * chunk + slpos[r];
-                if (idx >= I.n) continue;
-                I.out[idx] = (uint16_t)join16(sm_of16(I.out[idx]), sev[r]);
+    }
+    coop_leave(bar, true);
+}
+
+// The slots k_decode_slot_hold left: those whose barrier aborted and those
+// with an unmarked escape stream.  Their tiles below t_split are decoded
+// from the stash (the inputs and escape sections the first kernel put
+// there) as the two-launch form's second kernel does; an unmarked stream's
+// escapes are then applied at their indices by the last workgroup to finish
+// the tensor.  The last workgroup of the grid puts the barrier block back.
+__global__ __launch_bounds__(kDecThreads) void k_decode_slot_defer(DecArgs a) {
+    __shared__ CoopLds sh;
+    __shared__ uint32_t last;
+    // the first kernel's last workgroup put the counters back to (tag << 32)
+    CoopBar bar;
+    bar.blk = a.hold_block;
+    bar.tag = a.hold_tag;
+    bar.passed = 0;
+    if (threadIdx.x == 0) {
+        const uint64_t pend = ld_agent(coop_pending(bar));
+        last = (uint32_t)(pend >> 32) == bar.tag && (pend & 1u) ? 1u | ((uint32_t)pend & 0xFF00u) : 0u;
+    }
+    __syncthreads();
+    if (!last) return;   // nothing was left (the common case)
+    const uint32_t abort_round = last >> 8;
+    uint32_t round = 0;
+
+#pragma unroll 1
+    for (uint32_t item = 0; item < a.count; ++item) {
+        const uint32_t tid = threadIdx.x, wg = blockIdx.x, G = gridDim.x;
+        const DecItem I = a.it[item];
+        if (I.n == 0) continue;
+        Layout L;
+        if (!meta_ok(I, L) || L.total > I.other_bytes) continue;   // reported by the first kernel
+        const uint64_t e = I.meta->n_esc;
+        const uint32_t chunk = (uint32_t)I.meta->chunk_size;
+        const bool ascending = (I.meta->flags & SPLITZIP_META_ASCENDING) != 0;
+        const bool deferred = e && !ascending;
+        if (!deferred) {
+            ++round;
+            if (round_verdict(abort_round, round) == kGo) continue;
+        }
+        const bool patch = e && ascending;
+        const Layout L0 = layout_of(I.n, 0);
+        const int32_t *scid = reinterpret_cast<const int32_t *>(I.stash + L.off_cid);
+        const uint16_t *slpos = reinterpret_cast<const uint16_t *>(I.stash + L.off_lpos);
+        const uint8_t *sev = I.stash + L.off_ev;
+        const uint64_t tiles = (I.n + kCoopTile - 1) / kCoopTile;
+        const uint64_t t_split = slot_split(L.total, tiles, kCoopTile);
+        const uint32_t last_cnt = (uint32_t)(I.n - (tiles - 1) * kCoopTile);
+        __syncthreads();   // the previous tensor's last reads of LDS
+        if (tid < 256)
+            sh.pair_lut[tid] = (uint32_t)I.dec_lut[(tid >> 4) & 15] | ((uint32_t)I.dec_lut[tid & 15] << 16);
+        __syncthreads();
+        for (uint64_t t = wg; t < t_split; t += G) {
+            const uint64_t base = t * kCoopTile;
+            const uint32_t cnt = t == tiles - 1 ? last_cnt : kCoopTile;
+            if (cnt == kCoopTile) {
+                const uint32_t *spk = reinterpret_cast<const uint32_t *>(I.stash) + t * kCoopUnits;
+                const u32x2 *ssm = reinterpret_cast<const u32x2 *>(I.stash + L0.off_sm) + t * kCoopUnits;
+#pragma unroll
+                for (int u = 0; u < kDecUnits; ++u)
+                    decode_unit_lds(sh.pair_lut, __builtin_nontemporal_load(spk + u * kDecThreads + tid),
+                                    __builtin_nontemporal_load(ssm + u * kDecThreads + tid), sh.tile,
+                                    (u * kDecThreads + tid) * kUnit);
+            } else {
+                decode_partial_lds(I.stash + base / 2, I.stash + L0.off_sm + base, cnt, sh.pair_lut,
+                                   sh.tile, tid);
+            }
+            finish_tile(sh, patch, scid, slpos, sev, e, I.n, chunk, base, cnt, I.out, tid);
+        }
+        if (deferred) {
+            // every workgroup releases its stores and arrives; the last one
+            // applies every escape at its index (sign and mantissa from the
+            // decoded value)
+            __threadfence();
+            wait_vector_memory();
+            __syncthreads();
+            if (tid == 0) {
+                const uint64_t t = a.order_ticket + item;
+                uint64_t *c = a.order_sync + (t & (kOrderSlots - 1));
+                counter_claim(c, ld_agent(c), (uint32_t)t + 1u);
+                last = tagged_arrive(c, G, (uint32_t)t + 1u);
+            }
+            __syncthreads();
+            if (last) {
+                __threadfence();
+                for (uint64_t r = tid; r < e; r += kDecThreads) {
+                    const int32_t c = scid[r];
+                    if (c < 0) continue;
+                    const uint64_t idx = (uint64_t)c * chunk + slpos[r];
+                    if (idx >= I.n) continue;
+                    I.out[idx] = (uint16_t)join16(sm_of16(I.out[idx]), sev[r]);
+                }
             }
         }
     }
-    coop_leave(bar);
+    coop_leave(bar, false);
 }
 
 // Validation (and order-independent re-application) of every escape, only
@@ -2085,26 +2366,34 @@ bool cu_count(int &cus) {
     return true;
 }
 
-// Workgroups of the cooperative slot decode that the current device keeps
-// resident at once, cached per device (-1: no cooperative launch).
+// Workgroups of the one-kernel slot decode that the current device keeps
+// resident at once (0: none), and whether it has cooperative launches,
+// cached per device (-1: not known yet).
 std::atomic<int> g_coop_grid[kMaxDevices];
+std::atomic<int> g_coop_ok[kMaxDevices];
 
-bool coop_grid(uint32_t &grid) {
+bool coop_grid(uint32_t &grid, bool &coop) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
     int g = dev < kMaxDevices ? g_coop_grid[dev].load(std::memory_order_relaxed) : 0;
-    if (g == 0) {
-        int coop = 0, per_cu = 0, cus = 0;
-        if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
-            !cu_count(cus) ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_slot_coop, kDecThreads, 0) !=
+    int c = dev < kMaxDevices ? g_coop_ok[dev].load(std::memory_order_relaxed) : -1;
+    if (g == 0 || c < 0) {
+        int per_cu = 0, cus = 0;
+        if (!cu_count(cus) ||
+            hipDeviceGetAttribute(&c, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_slot_hold, kDecThreads, 0) !=
                 hipSuccess)
             return false;
-        g = coop && per_cu > 0 ? per_cu * cus : -1;
+        g = per_cu > 0 ? per_cu * cus : -1;
         if (g > (int)kCoopMaxGrid) g = (int)kCoopMaxGrid;
-        if (dev < kMaxDevices) g_coop_grid[dev].store(g, std::memory_order_relaxed);
+        c = c ? 1 : 0;
+        if (dev < kMaxDevices) {
+            g_coop_grid[dev].store(g, std::memory_order_relaxed);
+            g_coop_ok[dev].store(c, std::memory_order_relaxed);
+        }
     }
     grid = g > 0 ? (uint32_t)g : 0u;
+    coop = c == 1;
     return true;
 }
 
@@ -2157,10 +2446,21 @@ bool order_counters(DecArgs &a, uint32_t count) {
     return true;
 }
 
-// The barrier block of a cooperative slot decode: blocks go round by ticket.
+// The barrier block of a one-kernel slot decode.  Calls on one stream run
+// one after another and share a block (each claims it with its own tag);
+// each stream keeps its block while it is among the kCoopBlocks streams of
+// the device that used one last, so two calls that run at the same time
+// share a block only when more than kCoopBlocks streams decode slots at once.
 std::atomic<uint64_t *> g_coop_pool[kMaxDevices];
+struct CoopOwner {
+    hipStream_t stream;
+    uint64_t used;   // 0: never
+};
+CoopOwner g_coop_owner[kMaxDevices][kCoopBlocks];
+uint64_t g_coop_clock = 0;
+std::mutex g_coop_mutex;
 
-bool coop_block(DecArgs &a) {
+bool coop_block(DecArgs &a, hipStream_t s) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
     uint64_t *p = dev < kMaxDevices ? g_coop_pool[dev].load(std::memory_order_relaxed) : nullptr;
@@ -2170,8 +2470,23 @@ bool coop_block(DecArgs &a) {
         p = static_cast<uint64_t *>(q);
         if (dev < kMaxDevices) g_coop_pool[dev].store(p, std::memory_order_relaxed);
     }
-    a.order_ticket = g_ticket.fetch_add(1, std::memory_order_relaxed);
-    a.order_sync = p + (a.order_ticket % kCoopBlocks) * kCoopWords;
+    uint32_t blk = 0;
+    {
+        std::lock_guard<std::mutex> lock(g_coop_mutex);
+        CoopOwner *own = g_coop_owner[dev < kMaxDevices ? dev : 0];
+        for (uint32_t k = 0; k < kCoopBlocks; ++k) {
+            if (own[k].used && own[k].stream == s) {
+                blk = k;
+                break;
+            }
+            if (own[k].used < own[blk].used) blk = k;   // else the least recently used
+        }
+        own[blk].stream = s;
+        own[blk].used = ++g_coop_clock;
+    }
+    const uint64_t ticket = g_ticket.fetch_add(1, std::memory_order_relaxed);
+    a.hold_block = p + (uint64_t)blk * kCoopWords;
+    a.hold_tag = (uint32_t)ticket + 1u;
     return true;
 }
 
@@ -2334,7 +2649,7 @@ int launch_decode(const DecItem *items, uint32_t count, int32_t *status, hipStre
 // output buffer (a slot): pass 1 stashes the inputs of the tiles whose
 // output overlaps the payload and decodes the rest, pass 2 decodes the
 // stashed tiles over the payload.
-int launch_decode_slot(const splitzip_slot_item *items, uint32_t count, int32_t *status,
+int launch_decode_slot(const splitzip_slot_item *items, uint32_t count, int32_t *status, bool resident,
                        hipStream_t s) {
     constexpr uint64_t kTile = (uint64_t)kDecUnits * kDecThreads * kUnit;
     DecArgs a{};
@@ -2351,24 +2666,44 @@ int launch_decode_slot(const splitzip_slot_item *items, uint32_t count, int32_t 
     }
     a.tile_start[count] = tiles;
     if (tiles == 0) return SPLITZIP_OK;
-    // A group of two or more slots takes one cooperative launch where the
-    // device has them: a cooperative launch costs about 17 us more than an
-    // ordinary one, more than a single slot gains from it.  The environment
-    // variable SPLITZIP_SLOT_LAUNCH = "two" or "coop" selects either form for
-    // every call.
-    uint32_t grid = 0;
+    // The resident form (k_decode_slot_hold, then k_decode_slot_defer for
+    // what it left) in an ordinary launch, or the two-launch form
+    // (k_decode_slot_stage, k_decode_slot_finish).  The environment variable
+    // SPLITZIP_SLOT_LAUNCH selects a form for every call: "one" (resident),
+    // "coop" (resident, the first kernel launched cooperatively) or "two";
+    // SPLITZIP_SLOT_WAIT_US sets the resident form's bounded barrier wait
+    // (default kHoldWaitUs; 0 makes nearly every barrier give up, which
+    // exercises the path taken when the grid is not resident).
     const char *form = getenv("SPLITZIP_SLOT_LAUNCH");
-    const bool two = form && strcmp(form, "two") == 0;
-    const bool coop = form && strcmp(form, "coop") == 0;
-    if (!two && (coop || count >= 2) && !coop_grid(grid)) return SPLITZIP_ERR_HIP;
+    const bool want_two = form && strcmp(form, "two") == 0;
+    const bool want_one = form && strcmp(form, "one") == 0;
+    const bool want_coop = form && strcmp(form, "coop") == 0;
+    const bool one_kernel = want_one || want_coop || (resident && !want_two);
+    uint32_t grid = 0;
+    bool coop_ok = false;
+    if (one_kernel && !coop_grid(grid, coop_ok)) return SPLITZIP_ERR_HIP;
+    const bool coop = grid && coop_ok && want_coop;
+    int cus = 0;
+    if (!cu_count(cus)) return SPLITZIP_ERR_HIP;
+    if (!order_counters(a, count)) return SPLITZIP_ERR_HIP;
     if (grid) {
-        if (!coop_block(a)) return SPLITZIP_ERR_HIP;
-        void *args[] = {&a};
-        if (hipLaunchCooperativeKernel(reinterpret_cast<const void *>(k_decode_slot_coop), dim3(grid),
-                                       dim3(kDecThreads), args, 0, s) != hipSuccess)
-            return SPLITZIP_ERR_HIP;
+        if (!coop_block(a, s)) return SPLITZIP_ERR_HIP;
+        const char *w = getenv("SPLITZIP_SLOT_WAIT_US");
+        const uint64_t us = w ? strtoull(w, nullptr, 10) : kHoldWaitUs;
+        a.wait_ticks = (uint32_t)(us < 40000000ull ? us * 100 : 4000000000ull);
+        if (coop) {
+            void *args[] = {&a};
+            if (hipLaunchCooperativeKernel(reinterpret_cast<const void *>(k_decode_slot_hold), dim3(grid),
+                                           dim3(kDecThreads), args, 0, s) != hipSuccess)
+                return SPLITZIP_ERR_HIP;
+        } else {
+            k_decode_slot_hold<<<grid, kDecThreads, 0, s>>>(a);
+        }
+        if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
+        k_decode_slot_defer<<<(unsigned)(cus < (int)kCoopMaxGrid ? cus : (int)kCoopMaxGrid), kDecThreads,
+                              0, s>>>(a);
+        if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     } else {
-        if (!order_counters(a, count)) return SPLITZIP_ERR_HIP;
         k_decode_slot_stage<<<(unsigned)tiles, kDecThreads, 0, s>>>(a);
         if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     }
@@ -2518,18 +2853,28 @@ int splitzip_decode_slot(uint8_t *d_slot, uint64_t slot_bytes, const splitzip_me
     return splitzip_decode_slot_batch(&it, 1, d_status, stream);
 }
 
-int splitzip_decode_slot_batch(const splitzip_slot_item *items, uint32_t count, int32_t *d_status,
-                               void *stream) {
+static int decode_slot_batch(const splitzip_slot_item *items, uint32_t count, int32_t *d_status,
+                             bool resident, void *stream) {
     if ((count && !items) || (d_status && !aligned(d_status, 4))) return SPLITZIP_ERR_INVALID;
     for (uint32_t k = 0; k < count; ++k)
         if (check_slot_item(items[k])) return SPLITZIP_ERR_INVALID;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     for (uint32_t k0 = 0; k0 < count; k0 += kMaxBatch) {
         const uint32_t m = count - k0 < (uint32_t)kMaxBatch ? count - k0 : (uint32_t)kMaxBatch;
-        const int rc = launch_decode_slot(items + k0, m, d_status, s);
+        const int rc = launch_decode_slot(items + k0, m, d_status, resident, s);
         if (rc) return rc;
     }
     return SPLITZIP_OK;
+}
+
+int splitzip_decode_slot_batch(const splitzip_slot_item *items, uint32_t count, int32_t *d_status,
+                               void *stream) {
+    return decode_slot_batch(items, count, d_status, false, stream);
+}
+
+int splitzip_decode_slot_batch_resident(const splitzip_slot_item *items, uint32_t count,
+                                        int32_t *d_status, void *stream) {
+    return decode_slot_batch(items, count, d_status, true, stream);
 }
 
 int splitzip_calibrate_batch(const splitzip_item *items, uint32_t count, void *d_ws,

@@ -26,7 +26,7 @@ def declared_functions(header=HEADER):
 def test_every_declared_symbol_is_exported():
     lib = S.lib()
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for name in names:
         assert hasattr(lib, name), name
         assert name in _abi.SIGNATURES, name
@@ -112,8 +112,9 @@ def test_argument_errors_need_no_device():
     items[0].n, items[0].stash, items[0].stash_bytes = 5, 0x40000, 1 << 10
     items[1] = items[0]
     items[1].stash = 0x10100                      # overlaps its slot
-    assert _abi.splitzip_decode_slot_batch(items, 2, 0, 0) == _abi.ERR_INVALID
-    assert _abi.splitzip_decode_slot_batch(None, 1, 0, 0) == _abi.ERR_INVALID
+    for fn in (_abi.splitzip_decode_slot_batch, _abi.splitzip_decode_slot_batch_resident):
+        assert fn(items, 2, 0, 0) == _abi.ERR_INVALID
+        assert fn(None, 1, 0, 0) == _abi.ERR_INVALID
     # chunk sizes the wire format cannot carry
     for chunk, n in ((0, 5), (65537, 5), (1, (1 << 31) + 1)):
         assert _abi.splitzip_encode_chunked(0x1000, n, 0x2000, chunk, 0x4000, 1 << 40, 0x3000,

@@ -26,13 +26,36 @@ def setup_module(module):
     S.lib()
 
 
-@pytest.fixture(params=["coop", "two"])
+@pytest.fixture(params=["two", "resident", "resident_abort", "coop"])
 def form(request, monkeypatch):
-    """Launch form of the in-place decode, forced for every call: one
-    cooperative launch (by default only groups of slots take it) or the
-    two-launch form (by default single slots)."""
-    monkeypatch.setenv("SPLITZIP_SLOT_LAUNCH", request.param)
-    return request.param
+    """Form of the in-place decode: the library's two-launch form (the
+    default entry points), the resident form (the resident entry point;
+    one grid barrier per slot, in an ordinary launch), the same with a zero
+    barrier wait, so that nearly every barrier gives up and the slot is
+    finished by the deferral kernel (the path taken when concurrent work
+    keeps the grid from being placed), or the resident form launched
+    cooperatively (forced for every call)."""
+    monkeypatch.delenv("SPLITZIP_SLOT_WAIT_US", raising=False)
+    monkeypatch.delenv("SPLITZIP_SLOT_LAUNCH", raising=False)
+    if request.param == "resident_abort":
+        monkeypatch.setenv("SPLITZIP_SLOT_WAIT_US", "0")
+    elif request.param == "coop":
+        monkeypatch.setenv("SPLITZIP_SLOT_LAUNCH", "coop")
+    _RESIDENT[0] = request.param != "two"
+    yield request.param
+    _RESIDENT[0] = False
+
+
+_RESIDENT = [False]
+
+
+def decode_slot(*args, **kw):
+    """S.decode_slot in the form the test's `form` fixture chose."""
+    return S.decode_slot(*args, resident=_RESIDENT[0], **kw)
+
+
+def decode_slots(*args, **kw):
+    return S.decode_slots(*args, resident=_RESIDENT[0], **kw)
 
 
 def slot_for(payload: bytes, n: int, extra: int = 0) -> torch.Tensor:
@@ -60,7 +83,7 @@ def run_slot(opay, om, dec_lut, validate=True, extra=0, stash_extra=0, ascending
     stash = stash_for(om.comp_bytes, stash_extra)
     lut = torch.tensor(np.asarray(dec_lut, np.uint8)).to(DEV)
     st = torch.zeros(1, dtype=torch.int32, device=DEV) if validate else None
-    out = S.decode_slot(slot, meta_to_device(om, ascending), lut, n, stash, status=st)
+    out = decode_slot(slot, meta_to_device(om, ascending), lut, n, stash, status=st)
     torch.cuda.synchronize()
     return slot, host_bits(out), (int(st.item()) if validate else 0)
 
@@ -122,14 +145,14 @@ def test_slot_matches_gpu_encode_and_plain_decode(form):
     slot[: m.comp_bytes].copy_(payload[: m.comp_bytes])
     stash = torch.empty(m.comp_bytes, dtype=torch.uint8, device=DEV)
     st = torch.zeros(1, dtype=torch.int32, device=DEV)
-    out = S.decode_slot(slot, meta, cb, n, stash, status=st)
+    out = decode_slot(slot, meta, cb, n, stash, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     assert torch.equal(out.view(torch.int16), x.view(torch.int16))
     assert torch.equal(plain.view(torch.int16), x.view(torch.int16))
     # and again without validation, into the same slot
     slot[: m.comp_bytes].copy_(payload[: m.comp_bytes])
-    out = S.decode_slot(slot, meta, cb, n, stash)
+    out = decode_slot(slot, meta, cb, n, stash)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), x.view(torch.int16))
 
@@ -137,7 +160,7 @@ def test_slot_matches_gpu_encode_and_plain_decode(form):
 @pytest.mark.parametrize("make,n,seed", [(W.gaussian_weight, 40 * 2**20 + 5, 1),
                                          (W.log_uniform_stress, 40 * 2**20 + 3, 2)])
 def test_slot_beyond_register_reach(make, n, seed, form):
-    """More tiles overlap the payload than the cooperative grid holds in
+    """More tiles overlap the payload than the one-kernel form's grid holds in
     registers (3 per workgroup): the rest, and the partial last tile, go
     through the stash; stress data also gives held tiles with more escapes
     than their LDS list takes.  GPU encode, then the in-place decode with the
@@ -156,7 +179,7 @@ def test_slot_beyond_register_reach(make, n, seed, form):
     for md, status in ((meta, None), (meta, st), (unmarked, None), (unmarked, st)):
         slot.fill_(FILL)
         slot[: m.comp_bytes].copy_(payload[: m.comp_bytes])
-        out = S.decode_slot(slot, md, cb, n, stash, status=status)
+        out = decode_slot(slot, md, cb, n, stash, status=status)
         torch.cuda.synchronize()
         assert int(st.item()) == 0
         assert torch.equal(out.view(torch.int16), x.view(torch.int16))
@@ -172,7 +195,7 @@ def test_slot_rejects_bad_metadata_and_leaves_slot(form):
     slot = slot_for(opay, n)
     before = slot.cpu().clone()
     st = torch.zeros(1, dtype=torch.int32, device=DEV)
-    S.decode_slot(slot, meta_to_device(om), lut, n, stash_for(om.comp_bytes)[: om.comp_bytes - 1],
+    decode_slot(slot, meta_to_device(om), lut, n, stash_for(om.comp_bytes)[: om.comp_bytes - 1],
                   status=st)
     torch.cuda.synchronize()
     assert int(st.item()) & _abi.DEC_BAD_META
@@ -181,15 +204,15 @@ def test_slot_rejects_bad_metadata_and_leaves_slot(form):
     bad = oracle.Meta(om.n, om.n_pairs, om.chunk_size, om.n_esc, om.comp_bytes,
                       (0, om.offsets[1] + 4) + tuple(om.offsets[2:]))
     st.zero_()
-    S.decode_slot(slot, meta_to_device(bad), lut, n, stash_for(om.comp_bytes), status=st)
+    decode_slot(slot, meta_to_device(bad), lut, n, stash_for(om.comp_bytes), status=st)
     torch.cuda.synchronize()
     assert int(st.item()) & _abi.DEC_BAD_META
     assert torch.equal(slot.cpu(), before)
     # non-contiguous slot and overlapping stash are argument errors
     with pytest.raises(ValueError):
-        S.decode_slot(slot.view(-1, 2)[:, 0], meta_to_device(om), lut, n, stash_for(16))
+        decode_slot(slot.view(-1, 2)[:, 0], meta_to_device(om), lut, n, stash_for(16))
     with pytest.raises(S.SplitZipError):
-        S.decode_slot(slot, meta_to_device(om), lut, n, slot[-om.comp_bytes:])
+        decode_slot(slot, meta_to_device(om), lut, n, slot[-om.comp_bytes:])
 
 
 def test_slot_unsorted_escape_stream_with_validation(form):
@@ -245,7 +268,7 @@ def test_h2d_pipeline_into_slots(form):
             ev = torch.cuda.Event()
             ev.record(copy_s)
         dec_s.wait_event(ev)
-        outs.append(S.decode_slot(slots[k], metas[k], cbs[k], n, stash, status=st, stream=dec_s))
+        outs.append(decode_slot(slots[k], metas[k], cbs[k], n, stash, status=st, stream=dec_s))
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     for x, out in zip(xs, outs):
@@ -270,7 +293,7 @@ def test_slot_batch_matches_inputs_across_launches(form):
         want.append(xs_h)
     _say("slot batch of %d" % len(xs))
     st = torch.zeros(1, dtype=torch.int32, device=DEV)
-    outs = S.decode_slots(slots, metas, luts, sizes, stashes, status=st)
+    outs = decode_slots(slots, metas, luts, sizes, stashes, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     for k, (out, w) in enumerate(zip(outs, want)):
@@ -316,10 +339,12 @@ def test_encode_straight_into_pinned_host_memory(make, n):
         S.encode(xd, cb, ws, payload=torch.empty(16, dtype=torch.uint8))
 
 
-def test_slot_groups_on_concurrent_streams():
-    """Two groups of slots decoded at the same time on two streams (each a
-    cooperative launch), with plain decodes on a third stream: every output
-    exact and no barrier timeout (status bit 16)."""
+def test_slot_groups_on_concurrent_streams(form):
+    """Two groups of slots decoded at the same time on two streams, with
+    plain decodes on a third stream: every output exact.  In the resident
+    form each group's grid fills the GPU, so the two contend for it and a
+    barrier may give up (the deferral kernel then finishes the slots); in a
+    cooperative launch the runtime places each grid whole."""
     g = torch.Generator().manual_seed(13)
     sizes = [int(v) for v in torch.randint(50_000, 3_000_000, (12,), generator=g)]
     cases = []
@@ -347,10 +372,10 @@ def test_slot_groups_on_concurrent_streams():
             pl.append((pay, meta_to_device(c[3], True),
                        torch.tensor(np.asarray(c[1].dec_lut, np.uint8)).to(DEV), c[3].n))
         torch.cuda.synchronize()
-        _say("concurrent slot groups, round %d" % rnd)
+        _say("concurrent slot groups (%s), round %d" % (form, rnd))
         for gi, (slots, metas, luts, stashes) in enumerate(bufs):
             with torch.cuda.stream(streams[gi]):
-                outs.append(S.decode_slots(slots, metas, luts, [c[3].n for c in groups[gi]], stashes,
+                outs.append(decode_slots(slots, metas, luts, [c[3].n for c in groups[gi]], stashes,
                                            status=st[gi], stream=streams[gi]))
         with torch.cuda.stream(streams[2]):
             pouts = [S.decode(p, m, l, n, status=st[2], stream=streams[2]) for p, m, l, n in pl]
