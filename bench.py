@@ -142,6 +142,8 @@ def design_probes(S, dev):
     * the encode pattern with a fused arrival (count store, s_waitcnt,
       two-level arrival counter), and with an agent-scope fence per
       workgroup;
+    * both patterns with `run` consecutive tiles per XCD in turn against the
+      plain order of tiles (TB/s);
     * device-scope atomics: dependent adds by one thread (latency), one add
       by each of 8,192 workgroups on one address against 64 spread ones;
     * 64 launches of an almost empty kernel, ordinary and cooperative."""
@@ -228,6 +230,26 @@ def design_probes(S, dev):
                                   "TBps": round(moved * one / ms_one / 1e9, 3)}}
     torch.cuda.synchronize()
     assert int(ready[0].item()) == epoch[0], "fused arrival: the last arrival was not seen"
+
+    # order of tiles over the XCDs: `run` consecutive tiles per XCD in turn
+    # (0: the plain order), both patterns, per 2^30 launch and per 2^25 call
+    res["tile_order"] = {}
+    for name, dec_side in (("encode", 0), ("decode", 1)):
+        res["tile_order"][name] = {}
+        for n, runs in ((big, (0, 8, 64, 512, big // 8192 // 8)), (one, (0, 8, 64, 512))):
+            key = "per_2^30_launch" if n == big else "per_2^25_call"
+            row = {}
+            for run in runs:
+                turn = [0]
+
+                def order_call(run=run, n=n):
+                    k = turn[0] % (big // n)
+                    turn[0] += 1
+                    xp, pp, sp, op = ptrs(n, k)
+                    ok(lib.splitzip_ceiling_order(dec_side, run, xp, pp, sp, op, n, sh))
+                ms = timed(order_call, 5 if n == big else 64)
+                row["plain" if run == 0 else "run_%d" % run] = round(3.5 * n / ms / 1e9, 3)
+            res["tile_order"][name][key] = row
     del x, pk, sm, out, counts
 
     ac = torch.zeros(8 * 64, dtype=torch.int64, device=dev)

@@ -16,6 +16,8 @@
  *
  * and probes of the part's costs that the codec's design rests on:
  *
+ *   splitzip_ceiling_order          the same patterns in another order of
+ *                                   tiles over the XCDs
  *   splitzip_ceiling_encode_wide / _decode_wide   the same patterns with
  *                                   thread-contiguous 32-element units
  *   splitzip_ceiling_encode_arrive  the encode pattern with a fused arrival
@@ -24,6 +26,11 @@
  *   splitzip_ceiling_atomics        device-scope atomics: latency, and cost
  *                                   on one address against spread ones
  *   splitzip_ceiling_launch         ordinary against cooperative launches
+ *
+ * Every tile-per-workgroup stream takes its tiles in the codec's order: in a
+ * launch of at least 32,768 tiles each XCD (workgroup b runs on XCD b % 8)
+ * takes 64 consecutive tiles in turn, and the last (tiles mod 512)
+ * workgroups, like every smaller launch, take tile b.
  *
  * Conventions: every pointer is a device (or pinned host) address the
  * caller owns and keeps alive until the stream has run the call; calls are
@@ -66,6 +73,15 @@ int splitzip_ceiling_encode_shape(const uint16_t *d_x, uint64_t n, uint8_t *d_pk
  * holds n/2 bytes, d_sm n bytes, d_out 2n bytes.  INVALID otherwise. */
 int splitzip_ceiling_decode_shape(const uint8_t *d_pk, const uint8_t *d_sm, uint16_t *d_out,
                                   uint64_t n, hipStream_t stream);
+
+/* The encode (decode = 0: d_x -> d_pk, d_sm) or decode (decode = 1: d_pk,
+ * d_sm -> d_out) pattern of the shapes above with `run` consecutive tiles per
+ * XCD in turn (run a power of two up to 65536; 0: tile b for workgroup b),
+ * at any launch size; the last (tiles mod 8 * run) workgroups take tile b.
+ * The unused pointer may be NULL.  Sizes, alignment and errors as for the
+ * shapes above. */
+int splitzip_ceiling_order(uint32_t decode, uint32_t run, const uint16_t *d_x, uint8_t *d_pk,
+                           uint8_t *d_sm, uint16_t *d_out, uint64_t n, hipStream_t stream);
 
 /* The encode / decode patterns with thread-contiguous 32-element units: per
  * 32 elements four 16-byte loads of d_x, one 16-byte store to d_pk + i/2 and

@@ -126,6 +126,8 @@ CEILING_SIGNATURES = {
     "splitzip_ceiling_read": (ctypes.c_int, [_P, ctypes.c_uint64, ctypes.c_uint32, _P, _P]),
     "splitzip_ceiling_encode_shape": (ctypes.c_int, [_P, ctypes.c_uint64, _P, _P, _P]),
     "splitzip_ceiling_decode_shape": (ctypes.c_int, [_P, _P, _P, ctypes.c_uint64, _P]),
+    "splitzip_ceiling_order": (ctypes.c_int, [ctypes.c_uint32, ctypes.c_uint32, _P, _P, _P, _P,
+                                              ctypes.c_uint64, _P]),
     "splitzip_ceiling_encode_wide": (ctypes.c_int, [_P, ctypes.c_uint64, _P, _P, _P]),
     "splitzip_ceiling_decode_wide": (ctypes.c_int, [_P, _P, _P, ctypes.c_uint64, _P]),
     "splitzip_ceiling_encode_arrive": (ctypes.c_int, [_P, ctypes.c_uint64, _P, _P, _P, _P, _P,

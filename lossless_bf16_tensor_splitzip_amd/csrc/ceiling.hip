@@ -22,6 +22,17 @@ constexpr int kUnits = 4;            // units per thread and tile
 constexpr uint64_t kTile = (uint64_t)kThreads * kUnit * kUnits;
 constexpr uint32_t kSinkMagic = 0x9E3779B9u;
 
+// The codec's map from workgroups to tiles (one tile per workgroup): in a
+// launch of at least 32,768 tiles each XCD (workgroup b runs on XCD b % 8)
+// takes 64 consecutive tiles in turn, the last G mod 512 workgroups keeping
+// the plain order; smaller launches take the plain order.
+__device__ inline uint64_t launch_tile(uint64_t b, uint64_t G) {
+    constexpr uint64_t kRun = 64, B = 8 * kRun;
+    if (G < 32768 || b >= G / B * B) return b;
+    const uint64_t x = b % 8, j = b / 8;
+    return (j / kRun) * B + x * kRun + j % kRun;
+}
+
 __global__ __launch_bounds__(kReadThreads) void k_read_shape(const u32x4 *x, uint64_t nvec,
                                                              uint32_t *sink) {
     const uint64_t per = (nvec + gridDim.x - 1) / gridDim.x;
@@ -46,7 +57,7 @@ __global__ __launch_bounds__(kReadThreads) void k_read_shape(const u32x4 *x, uin
 
 __global__ __launch_bounds__(kThreads) void k_encode_shape(const uint16_t *x, uint8_t *pk,
                                                            uint8_t *sm) {
-    const uint64_t base = (uint64_t)blockIdx.x * kTile;
+    const uint64_t base = launch_tile(blockIdx.x, gridDim.x) * kTile;
     const int tid = threadIdx.x;
     u32x4 q[kUnits];
 #pragma unroll
@@ -66,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_shape(const uint16_t *x, ui
 
 __global__ __launch_bounds__(kThreads) void k_decode_shape(const uint8_t *pk, const uint8_t *sm,
                                                            uint16_t *out) {
-    const uint64_t base = (uint64_t)blockIdx.x * kTile;
+    const uint64_t base = launch_tile(blockIdx.x, gridDim.x) * kTile;
     const int tid = threadIdx.x;
     uint32_t p[kUnits];
     u32x2 s[kUnits];
@@ -88,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_shape(const uint8_t *pk, co
 
 // The encode pattern with thread-contiguous 32-element units.
 __global__ __launch_bounds__(kThreads) void k_encode_wide(const uint16_t *x, uint8_t *pk, uint8_t *sm) {
-    const uint64_t i0 = (uint64_t)blockIdx.x * kTile + (uint64_t)threadIdx.x * 32;
+    const uint64_t i0 = launch_tile(blockIdx.x, gridDim.x) * kTile + (uint64_t)threadIdx.x * 32;
     const u32x4 *xv = reinterpret_cast<const u32x4 *>(x + i0);
     u32x4 q[4];
 #pragma unroll
@@ -104,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_wide(const uint16_t *x, uin
 // The decode pattern with thread-contiguous 32-element units.
 __global__ __launch_bounds__(kThreads) void k_decode_wide(const uint8_t *pk, const uint8_t *sm,
                                                           uint16_t *out) {
-    const uint64_t i0 = (uint64_t)blockIdx.x * kTile + (uint64_t)threadIdx.x * 32;
+    const uint64_t i0 = launch_tile(blockIdx.x, gridDim.x) * kTile + (uint64_t)threadIdx.x * 32;
     const u32x4 p = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(pk + i0 / 2));
     const u32x4 s0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(sm + i0));
     const u32x4 s1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(sm + i0 + 16));
@@ -140,7 +151,8 @@ __global__ __launch_bounds__(kThreads) void k_encode_arrive(const uint16_t *x, u
     const uint32_t t = blockIdx.x, tiles = gridDim.x;
     const uint32_t ngroups = (tiles + kGroup - 1) / kGroup, g = t / kGroup;
     uint64_t *top = ctrs, *grp = ctrs + 8 * (1 + g);
-    const uint64_t base = (uint64_t)t * kTile;
+    const uint64_t dt = launch_tile(t, tiles);   // the tile this workgroup codes
+    const uint64_t base = dt * kTile;
     const int tid = threadIdx.x;
     u32x4 q[kUnits];
 #pragma unroll
@@ -162,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_arrive(const uint16_t *x, u
         __builtin_nontemporal_store(p, reinterpret_cast<uint32_t *>(pk + i0 / 2));
         __builtin_nontemporal_store(s, reinterpret_cast<u32x2_a4 *>(sm + i0));
     }
-    if (tid == 0) __hip_atomic_store(counts + t, acc & 0xFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(counts + dt, acc & 0xFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
@@ -176,10 +188,61 @@ __global__ __launch_bounds__(kThreads) void k_encode_arrive(const uint16_t *x, u
     }
 }
 
+// The encode / decode patterns with `run` consecutive tiles per XCD in turn
+// (0: the plain order, every launch size; the last G mod 8*run workgroups
+// keep it too).
+__device__ inline uint64_t run_tile(uint64_t b, uint64_t G, uint32_t run) {
+    if (run == 0) return b;
+    const uint64_t B = 8ull * run;
+    if (b >= G / B * B) return b;
+    const uint64_t x = b % 8, j = b / 8;
+    return (j / run) * B + x * run + j % run;
+}
+
+__global__ __launch_bounds__(kThreads) void k_encode_order(const uint16_t *x, uint8_t *pk, uint8_t *sm,
+                                                           uint32_t run) {
+    const uint64_t base = run_tile(blockIdx.x, gridDim.x, run) * kTile;
+    const int tid = threadIdx.x;
+    u32x4 q[kUnits];
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+        const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+        q[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + i0));
+    }
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+        const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+        const uint32_t p = q[u].x ^ q[u].y ^ q[u].z ^ q[u].w;
+        const u32x2 s = {q[u].x ^ q[u].z, q[u].y ^ q[u].w};
+        __builtin_nontemporal_store(p, reinterpret_cast<uint32_t *>(pk + i0 / 2));
+        __builtin_nontemporal_store(s, reinterpret_cast<u32x2_a4 *>(sm + i0));
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_decode_order(const uint8_t *pk, const uint8_t *sm,
+                                                           uint16_t *out, uint32_t run) {
+    const uint64_t base = run_tile(blockIdx.x, gridDim.x, run) * kTile;
+    const int tid = threadIdx.x;
+    uint32_t p[kUnits];
+    u32x2 s[kUnits];
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+        const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+        p[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(pk + i0 / 2));
+        s[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4 *>(sm + i0));
+    }
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+        const uint64_t i0 = base + (uint64_t)u * (kThreads * kUnit) + tid * kUnit;
+        const u32x4 o = {p[u] ^ s[u].x, p[u] ^ s[u].y, s[u].x ^ 0x5A5A5A5Au, s[u].y ^ 0xA5A5A5A5u};
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(out + i0));
+    }
+}
+
 // The encode pattern with an agent-scope fence (__threadfence: write-back of
 // the L2 and invalidation) at the end of every workgroup.
 __global__ __launch_bounds__(kThreads) void k_encode_fenced(const uint16_t *x, uint8_t *pk, uint8_t *sm) {
-    const uint64_t base = (uint64_t)blockIdx.x * kTile;
+    const uint64_t base = launch_tile(blockIdx.x, gridDim.x) * kTile;
     const int tid = threadIdx.x;
     u32x4 q[kUnits];
 #pragma unroll
@@ -256,6 +319,20 @@ extern "C" int splitzip_ceiling_decode_shape(const uint8_t *d_pk, const uint8_t 
         !aligned16(d_out))
         return SPLITZIP_ERR_INVALID;
     k_decode_shape<<<(uint32_t)(n / kTile), kThreads, 0, stream>>>(d_pk, d_sm, d_out);
+    return launched();
+}
+
+extern "C" int splitzip_ceiling_order(uint32_t decode, uint32_t run, const uint16_t *d_x,
+                                      uint8_t *d_pk, uint8_t *d_sm, uint16_t *d_out, uint64_t n,
+                                      hipStream_t stream) {
+    if (!tiles_ok(n) || !d_pk || !d_sm || !aligned16(d_pk) || !aligned16(d_sm) ||
+        (run & (run - 1)) || run > 65536 || decode > 1)
+        return SPLITZIP_ERR_INVALID;
+    if (decode ? (!d_out || !aligned16(d_out)) : (!d_x || !aligned16(d_x))) return SPLITZIP_ERR_INVALID;
+    if (decode)
+        k_decode_order<<<(uint32_t)(n / kTile), kThreads, 0, stream>>>(d_pk, d_sm, d_out, run);
+    else
+        k_encode_order<<<(uint32_t)(n / kTile), kThreads, 0, stream>>>(d_x, d_pk, d_sm, run);
     return launched();
 }
 

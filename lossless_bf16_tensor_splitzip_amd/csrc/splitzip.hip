@@ -627,11 +627,27 @@ __device__ inline uint32_t tile_ranks(const uint32_t *flags, uint32_t (*wtot)[4]
 
 // Dense sections of one tile, its escape count, and (up to kStageCap) its
 // escapes staged in element order; no communication between tiles.
+// Tile of workgroup b in a launch of G one-tile workgroups.  Workgroups go
+// to the 8 XCDs in turn (b % 8), so with the plain order the XCDs work on
+// interleaved tiles; a large launch instead gives each XCD 64 consecutive
+// tiles in turn, which streams faster there (the encode's access pattern
+// 6.25 against 5.89 TB/s over 2^30 elements, the decode's 6.11 against 5.96;
+// no gain, or a loss, below 2^28 elements).  The last G mod 512 workgroups
+// keep the plain order.
+constexpr uint64_t kXcdRun = 64;
+constexpr uint64_t kXcdBlockedMin = 32768;   // tiles per launch
+__device__ inline uint64_t launch_tile(uint64_t b, uint64_t G) {
+    constexpr uint64_t B = 8 * kXcdRun;
+    if (G < kXcdBlockedMin || b >= G / B * B) return b;
+    const uint64_t x = b % 8, j = b / 8;   // the j-th workgroup of XCD x
+    return (j / kXcdRun) * B + x * kXcdRun + j % kXcdRun;
+}
+
 __global__ __launch_bounds__(kThreads) void k_encode(EncArgs a) {
     __shared__ uint8_t lut[256];
     __shared__ uint32_t wtot[kEncUnits][4];
 
-    const uint64_t gt = blockIdx.x;
+    const uint64_t gt = launch_tile(blockIdx.x, gridDim.x);
     const uint32_t item = find_item(a.tile_start, a.count, gt);
     const EncItem I = a.it[item];
     const uint64_t t = gt - a.tile_start[item];
@@ -1254,7 +1270,7 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     // Output tile of a tensor with dense escapes, or the sm bytes of a tile
     // with many escapes in an otherwise sparse tensor.
     __shared__ uint32_t tile_buf[kDecTile / 2];
-    const uint64_t gt = blockIdx.x;
+    const uint64_t gt = launch_tile(blockIdx.x, gridDim.x);
     const uint32_t item = find_item(a.tile_start, a.count, gt);
     const DecItem I = a.it[item];
     const int tid = threadIdx.x;

@@ -58,6 +58,11 @@ def test_reference_stream_symbols_and_argument_errors():
     assert lib.splitzip_ceiling_atomics(0x1000, 1, 1, (1 << 20) + 1, 0) == _abi.ERR_INVALID
     assert lib.splitzip_ceiling_launch(1, 0, 0x1000, 0) == _abi.ERR_INVALID
     assert lib.splitzip_ceiling_launch(0, 1, 0x1002, 0) == _abi.ERR_INVALID
+    # order probe: run not a power of two, decode without an output, encode without an input
+    assert lib.splitzip_ceiling_order(0, 3, 0x1000, 0x2000, 0x3000, 0, 8192, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_order(1, 64, 0, 0x2000, 0x3000, 0, 8192, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_order(0, 64, 0, 0x2000, 0x3000, 0x4000, 8192, 0) == _abi.ERR_INVALID
+    assert lib.splitzip_ceiling_order(2, 0, 0x1000, 0x2000, 0x3000, 0x4000, 8192, 0) == _abi.ERR_INVALID
 
 
 def test_struct_layout_matches_header():

@@ -87,6 +87,23 @@ def test_batch_equals_single_calls():
         assert torch.equal(pay[: m.comp_bytes], b.payloads[k][: m.comp_bytes])
 
 
+def test_large_launch_tile_order():
+    """A launch of at least 32,768 tiles takes its tiles in runs of 64 per
+    XCD, and its last (G mod 512) workgroups in the plain order: 32,821
+    encode and decode tiles over items with ragged last tiles, each item
+    equal to the oracle and decoded exactly."""
+    xs = [W.gaussian_weight((1 << 27) + 12_345, seed=70),
+          W.log_uniform_stress(8192 * 37 + 5, seed=71),
+          W.gaussian_weight((1 << 27) - 1, seed=72),
+          W.gaussian_weight(100_003, seed=73)]
+    tiles = sum((x.numel() + 8191) // 8192 for x in xs)
+    assert tiles == 32_821 and tiles % 512 == 53
+    b, st = run_batch(xs)
+    assert st == 0
+    for k, x in enumerate(xs):
+        check_item(b, k, x)
+
+
 def test_batch_of_forty_needs_two_launches():
     xs = [W.gaussian_weight(20_000 + 517 * k, seed=60 + k) if k % 3 else
           W.log_uniform_stress(9_000 + 77 * k, seed=60 + k) for k in range(40)]

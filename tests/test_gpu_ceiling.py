@@ -149,3 +149,28 @@ def test_fused_arrival_fence_atomics_and_launch_probes():
     assert int(sink[0].item()) == 2
     assert lib.splitzip_ceiling_launch(0, 2000, sink.data_ptr(), sh) == _abi.ERR_INVALID
     assert lib.splitzip_ceiling_atomics(ac.data_ptr(), 1, 0, 1, sh) == _abi.ERR_INVALID
+
+
+@pytest.mark.parametrize("run", [0, 1, 8, 64])
+def test_tile_orders_cover_every_tile_once(run):
+    """The order probe in any order writes what the plain-order shapes write
+    (every tile exactly once), 1,100 tiles: with run 64 the first 1,024
+    workgroups take runs of 64 tiles per XCD and the last 76 the plain
+    order."""
+    lib = _abi.ceiling_lib()
+    n = 8192 * 1100
+    _say("tile order run=%d n=%d" % (run, n))
+    g = torch.Generator().manual_seed(90 + run)
+    x = torch.randint(-(1 << 15), 1 << 15, (n,), generator=g, dtype=torch.int32).to(torch.int16).to(DEV)
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    pk0 = torch.zeros(n // 2, dtype=torch.uint8, device=DEV)
+    sm0 = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    out0 = torch.zeros(n, dtype=torch.int16, device=DEV)
+    assert lib.splitzip_ceiling_encode_shape(x.data_ptr(), n, pk0.data_ptr(), sm0.data_ptr(), sh) == 0
+    assert lib.splitzip_ceiling_decode_shape(pk0.data_ptr(), sm0.data_ptr(), out0.data_ptr(), n, sh) == 0
+    pk, sm = torch.zeros_like(pk0), torch.zeros_like(sm0)
+    out = torch.zeros_like(out0)
+    assert lib.splitzip_ceiling_order(0, run, x.data_ptr(), pk.data_ptr(), sm.data_ptr(), 0, n, sh) == 0
+    assert lib.splitzip_ceiling_order(1, run, 0, pk.data_ptr(), sm.data_ptr(), out.data_ptr(), n, sh) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(pk, pk0) and torch.equal(sm, sm0) and torch.equal(out, out0)
