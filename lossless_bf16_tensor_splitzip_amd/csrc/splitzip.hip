@@ -1154,14 +1154,14 @@ constexpr uint32_t kOrderSlots = 65536;
 __device__ __align__(256) uint64_t g_order_sync[kOrderSlots];
 
 // Metadata must describe exactly the layout of (n, n_esc) and fit the buffer.
-__device__ inline bool meta_ok(const DecItem &I, Layout &L) {
-    const splitzip_meta *m = I.meta;
-    if (m->n != I.n || !chunk_ok(I.n, m->chunk_size) || m->n_esc > I.n) return false;
-    L = layout_of(I.n, m->n_esc);
-    return m->n_pairs == L.n_pairs && m->offsets[0] == 0 && m->offsets[1] == L.off_sm &&
-           m->offsets[2] == L.off_cid && m->offsets[3] == L.off_lpos &&
-           m->offsets[4] == L.off_ev && m->comp_bytes == L.total && L.total <= I.payload_bytes;
+__device__ inline bool meta_ok(const DecItem &I, const splitzip_meta &m, Layout &L) {
+    if (m.n != I.n || !chunk_ok(I.n, m.chunk_size) || m.n_esc > I.n) return false;
+    L = layout_of(I.n, m.n_esc);
+    return m.n_pairs == L.n_pairs && m.offsets[0] == 0 && m.offsets[1] == L.off_sm &&
+           m.offsets[2] == L.off_cid && m.offsets[3] == L.off_lpos && m.offsets[4] == L.off_ev &&
+           m.comp_bytes == L.total && L.total <= I.payload_bytes;
 }
+__device__ inline bool meta_ok(const DecItem &I, Layout &L) { return meta_ok(I, *I.meta, L); }
 
 enum DecMode { kPlain = 0, kSlotStage = 1, kSlotFinish = 2 };
 
@@ -1259,14 +1259,20 @@ __device__ void order_pass(const DecArgs &a, const DecItem &I, uint32_t item, co
     }
 }
 
+// Workgroup barrier that orders LDS only: the waves' global loads and stores
+// stay in flight across it (a full __syncthreads waits for all of them).
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int kTh, int kUnits, int kMode>
 __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     constexpr int kDecTile = kTh * kUnit * kUnits;
     __shared__ uint32_t pair_lut[256];      // pk byte -> (even exponent, odd exponent << 16)
     __shared__ uint64_t range[2];
     __shared__ uint32_t last_arrival;
-    __shared__ uint32_t plist[64];          // a sparse tile's escapes: position | exponent << 16, or ~0
-    __shared__ uint32_t plist_n;            // their number, or kNoList
     // Output tile of a tensor with dense escapes, or the sm bytes of a tile
     // with many escapes in an otherwise sparse tensor.
     __shared__ uint32_t tile_buf[kDecTile / 2];
@@ -1296,9 +1302,17 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
             smw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4 *>(sm + i0));
         }
     }
-    const uint32_t lut_entry = tid < 256 ? ((uint32_t)I.dec_lut[(tid >> 4) & 15] | ((uint32_t)I.dec_lut[tid & 15] << 16)) : 0u;
+    // Then the metadata, as one copy: the compiler reads it with scalar
+    // loads, whose wait leaves the stream loads in flight (reading fields
+    // through the pointer took vector loads, and vector loads complete in
+    // order, so their wait was a wait for the whole tile), and the table's two
+    // bytes, loaded by every lane (no branch around the loads) and combined
+    // where the table is written.
+    const splitzip_meta M = *I.meta;
+    const uint32_t lut_lo = I.dec_lut[(tid >> 4) & 15];   // (every lane: no branch around
+    const uint32_t lut_hi = I.dec_lut[tid & 15];          // the loads)
     Layout L;
-    if (!meta_ok(I, L) || (kMode != kPlain && L.total > I.other_bytes)) {
+    if (!meta_ok(I, M, L) || (kMode != kPlain && L.total > I.other_bytes)) {
         // nothing is written for inconsistent metadata
         if (kMode != kSlotFinish && gt == a.tile_start[item] && tid == 0 && a.status)
             atomicOr(a.status, 1);
@@ -1337,7 +1351,7 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
             }
         } else {
             if (tile >= t_split) {   // decoded by the first pass
-                if (I.meta->n_esc && !(I.meta->flags & SPLITZIP_META_ASCENDING))
+                if (M.n_esc && !(M.flags & SPLITZIP_META_ASCENDING))
                     order_pass<true>(a, I, item, L, &last_arrival);
                 return;
             }
@@ -1351,13 +1365,12 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
             }
         }
     }
-    const uint64_t e = I.meta->n_esc;
+    const uint64_t e = M.n_esc;
     const int32_t *cid = reinterpret_cast<const int32_t *>(I.payload + L.off_cid);
     const uint16_t *lpos = reinterpret_cast<const uint16_t *>(I.payload + L.off_lpos);
     const uint8_t *ev = I.payload + L.off_ev;
 
     static_assert(kTh >= 256, "one pair-table entry per thread");
-    if (tid < 256) pair_lut[tid] = lut_entry;
     // A tensor whose escapes average more than 512 per tile is decoded tile
     // by tile in LDS (dense values, the patch, then one coalesced store):
     // scattering thousands of 2-byte stores per tile to memory costs more
@@ -1365,43 +1378,11 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     // An escape stream not known to be ascending cannot be searched per
     // tile: after the dense part the last workgroup of the tensor applies
     // every escape.
-    const bool ascending = (I.meta->flags & SPLITZIP_META_ASCENDING) != 0;
+    const bool ascending = (M.flags & SPLITZIP_META_ASCENDING) != 0;
     const bool in_lds = ascending && full && e * (uint64_t)kDecTile > 512 * I.n;
-    const uint32_t chunk = (uint32_t)I.meta->chunk_size;
-    // The tile's elements lie in chunks [c0, c1), so its escapes are among
-    // those with chunk ids in [c0, c1) of the sorted stream (exactly those
-    // when tiles and chunks align).  For a sparse stream one wave loads the
-    // 64 entries around the interpolated position of c0 now, so that their
-    // round trip overlaps the dense part; they usually hold every escape of
-    // the tile.
-    const bool windowed = full && e && ascending && !in_lds;
-    uint64_t c0 = 0, c1 = 0, wlo = 0;
-    double per_chunk = 0.0;
-    int64_t wc = INT64_MAX;   // (beyond the stream: above every key)
-    uint32_t wl = 0, we = 0;
-    if (tid < 64 && e && ascending) {
-        uint64_t nchunks;
-        uint32_t p0, p1, pn;
-        chunk_split(base, chunk, c0, p0);
-        chunk_split(base + kDecTile - 1, chunk, c1, p1);
-        chunk_split(I.n - 1, chunk, nchunks, pn);
-        ++c1;
-        ++nchunks;
-        if (c1 > nchunks) c1 = nchunks;
-        per_chunk = (double)e / (double)nchunks;
-        if (windowed) {
-            const uint64_t g = (uint64_t)(per_chunk * (double)c0);
-            wlo = g > 32 ? g - 32 : 0;
-            if (wlo + 64 > e) wlo = e > 64 ? e - 64 : 0;
-            const uint64_t r = wlo + lane;
-            if (r < e) {
-                wc = cid[r];
-                wl = lpos[r];
-                we = ev[r];
-            }
-        }
-    }
-    __syncthreads();
+    const uint32_t chunk = (uint32_t)M.chunk_size;
+    if (tid < 256) pair_lut[tid] = lut_lo | (lut_hi << 16);
+    lds_barrier();   // the pair table; the stream loads may still be in flight
 
     // Dense part first: every element through the pair table, 16-byte stores.
     if (full) {
@@ -1433,65 +1414,34 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
         return;
     }
 
-    // Escape patch: the tile's entries [r0, r1) of the stream, from the
-    // window when it brackets them, else found by a search (by one wave while
-    // the dense stores drain); applied after the workgroup barrier, which
-    // orders them after the dense stores of every wave of the workgroup.
-    constexpr uint32_t kNoList = ~0u;
+    // Escape patch: the tile's escapes are among those with chunk ids in
+    // [c0, c1) of the sorted stream (exactly those when tiles and chunks
+    // align), found by one wave while the dense stores drain; they are
+    // applied after the workgroup barrier, which orders them after the dense
+    // stores of every wave of the workgroup.
     if (tid < 64) {
-        uint64_t r0 = 0, r1 = 0;
-        uint32_t listed = kNoList;
-        bool found = false;
-        if (windowed) {
-            const uint64_t b0 = __ballot(wc < (int64_t)c0);
-            const uint64_t b1 = __ballot(wc < (int64_t)c1);
-            const uint32_t k0 = __popcll(b0), k1 = __popcll(b1);
-            // brackets [r0, r1): nothing before the window reaches c0, and
-            // the window holds an entry at or above c1 or the stream's end
-            if ((wlo == 0 || (b0 & 1u)) && (k1 < 64 || wlo + 64 >= e)) {
-                found = true;
-                r0 = wlo + k0;
-                r1 = wlo + k1;
-                listed = k1 - k0;
-                if ((uint32_t)lane >= k0 && (uint32_t)lane < k1) {
-                    const int64_t pos = wc * (int64_t)chunk + (int64_t)wl - (int64_t)base;
-                    plist[lane - k0] = pos >= 0 && pos < kDecTile ? (uint32_t)pos | (we << 16) : kNoList;
-                }
-            }
-        }
-        if (!found) {
-            // interpolated guesses (hints only: the search is exact for any guess)
-            r0 = lower_bound_wave(cid, 0, e, (int64_t)c0, (uint64_t)(per_chunk * (double)c0), lane);
-            r1 = lower_bound_wave(cid, r0, e, (int64_t)c1, r0 + (uint64_t)(per_chunk * (double)(c1 - c0)),
-                                  lane);
-        }
+        // chunks that hold the tile's elements: [c0, c1)
+        uint64_t c0, c1, nchunks;
+        uint32_t p0, p1, pn;
+        chunk_split(base, chunk, c0, p0);
+        chunk_split(base + kDecTile - 1, chunk, c1, p1);
+        chunk_split(I.n - 1, chunk, nchunks, pn);
+        ++c1;
+        ++nchunks;
+        if (c1 > nchunks) c1 = nchunks;
+        // interpolated guesses (hints only: the search is exact for any guess)
+        const double per_chunk = (double)e / (double)nchunks;
+        const uint64_t r0 =
+            lower_bound_wave(cid, 0, e, (int64_t)c0, (uint64_t)(per_chunk * (double)c0), lane);
+        const uint64_t r1 = lower_bound_wave(cid, r0, e, (int64_t)c1,
+                                             r0 + (uint64_t)(per_chunk * (double)(c1 - c0)), lane);
         if (lane == 0) {
             range[0] = r0;
             range[1] = r1;
-            plist_n = listed;
         }
     }
     __syncthreads();
     const uint64_t r0 = range[0], r1 = range[1];
-    if (plist_n != kNoList) {
-        // The window's entries, patched by the thread that decoded the
-        // element, with the sign/mantissa byte it still holds.
-        const uint32_t cnt = plist_n;
-        for (uint32_t q = 0; q < cnt; ++q) {
-            const uint32_t ent = plist[q];
-            if (ent == kNoList) continue;
-            const uint32_t pos = ent & 0xFFFFu;
-            const uint32_t rem = pos % (kTh * kUnit);
-            if (rem / kUnit != (uint32_t)tid) continue;
-            const uint32_t u = pos / (kTh * kUnit), k = rem % kUnit;
-            uint32_t w = 0;
-#pragma unroll
-            for (int uu = 0; uu < kUnits; ++uu)
-                if ((uint32_t)uu == u) w = k < 4 ? smw[uu].x : smw[uu].y;
-            I.out[base + pos] = (uint16_t)join16((w >> (8 * (k & 3))) & 0xFFu, ent >> 16);
-        }
-        return;
-    }
     if (in_lds) {
         // the decoded value already holds the sign and mantissa
         uint16_t *t16 = reinterpret_cast<uint16_t *>(tile_buf);

@@ -238,13 +238,11 @@ def test_staging_cap_edges(counts):
 
 
 def test_decode_patch_paths():
-    """Each way the decode applies escapes, byte for byte: from the window of
-    the stream loaded before the dense part (tiles with few escapes near
-    their interpolated position), scattered after a search (a tile with 100,
-    and a tile with few whose position the interpolation misses by far),
-    through the tile's sign/mantissa bytes staged in LDS (a tile with more
-    than 512 while the tensor averages fewer), and with the whole tile built
-    in LDS (more than 512 per tile on average)."""
+    """Each way the decode applies escapes, byte for byte: scattered from
+    registers (a tile with few, and a tile whose position the interpolation
+    misses by far), through the tile's sign/mantissa bytes staged in LDS (a
+    tile with more than 512 while the tensor averages fewer), and with the
+    whole tile built in LDS (more than 512 per tile on average)."""
     src = torch.ones(8, dtype=torch.bfloat16)          # codes exponent 127 only
     n = 6 * 8192 + 100
     b = np.full(n, 0x3F80, np.uint16)
@@ -269,12 +267,11 @@ def test_decode_patch_paths():
 
 
 @pytest.mark.parametrize("per_tile", [1, 31, 32, 33, 63, 64, 65])
-def test_decode_escape_window(per_tile):
-    """Tiles with the same number of escapes each, so that the interpolated
-    position of a tile's first escape is exact: the 64-entry window loaded
-    before the dense part settles tiles with up to about 32 escapes (their
-    bytes patched from registers), and a tile with more falls back to the
-    search and the memory patch; a ragged last tile takes the element path."""
+def test_decode_escapes_per_tile(per_tile):
+    """Tiles with the same number of escapes each, around the search's 64-entry
+    window (so that the interpolated rank of a tile's first escape is close:
+    the window settles it, or its 64 samples do), and a ragged last tile
+    that takes the element path."""
     src = torch.ones(8, dtype=torch.bfloat16)          # codes exponent 127 only
     n = 9 * 8192 + 1234
     b = np.full(n, 0x3F80, np.uint16)
@@ -285,7 +282,7 @@ def test_decode_escape_window(per_tile):
         j = np.arange(len(pos))
         b[pos] = (((j + t) & 1) << 15) | (((j * 5 + t) % 120 + 1) << 7) | ((j * 3 + t) & 0x7F)
     x = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
-    _, om = full_parity(x, cb_source=src, name="escape window %d" % per_tile)
+    _, om = full_parity(x, cb_source=src, name="escapes per tile %d" % per_tile)
     assert om.n_esc >= 9 * per_tile
 
 
