@@ -236,7 +236,8 @@ def design_probes(S, dev):
     res["tile_order"] = {}
     for name, dec_side in (("encode", 0), ("decode", 1)):
         res["tile_order"][name] = {}
-        for n, runs in ((big, (0, 8, 64, 512, big // 8192 // 8)), (one, (0, 8, 64, 512))):
+        for n, runs in ((big, (0, 8, 16, 32, 64, 128, 256, 512, big // 8192 // 8)),
+                        (one, (0, 8, 16, 32, 64, 128, 256, 512))):
             key = "per_2^30_launch" if n == big else "per_2^25_call"
             row = {}
             for run in runs:
