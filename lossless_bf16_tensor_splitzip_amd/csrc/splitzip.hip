@@ -1138,7 +1138,7 @@ struct DecArgs {
     int32_t *status;
     uint64_t *order_sync;                 // this device's arrival counters (below)
     uint64_t order_ticket;                // this call's first counter, and its tag
-    uint64_t *hold_block;                 // one-kernel in-place decode: the call's barrier block,
+    uint64_t *hold_block;                 // resident in-place decode: the call's barrier block,
     uint32_t hold_tag;                    // its tag,
     uint32_t wait_ticks;                  // and the barrier's bounded wait (10 ns ticks)
 };
@@ -1531,8 +1531,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_slot_finish(DecArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// In-place decode in one cooperative launch (page 1, decode_slot_into; page
-// "SplitZip in DDO -- VMM routes", the CUDA route's expansion in place)
+// In-place decode, resident form (page 1, decode_slot_into; page "SplitZip in
+// DDO -- VMM routes", the CUDA route's expansion in place)
 // ---------------------------------------------------------------------------
 //
 // Tile t writes slot bytes [2tT, 2(t+1)T) (T = 8192 elements); the tiles from
@@ -1552,10 +1552,13 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_slot_finish(DecArgs a) {
 //
 // An ordinary launch does not promise that the whole grid is resident (other
 // work may hold part of the GPU), so the barrier's wait is bounded: a
-// workgroup that has waited wait_ticks (10 ns each) marks the round aborted
+// workgroup that has waited kStartWaitTicks while part of the grid has not
+// started, or wait_ticks (10 ns each) in any case, marks the round aborted
 // unless its last arrival has already come, and that arrival's atomic on the
 // top counter decides: go unless a mark came first.  An abort is sticky for
-// the rest of the launch (the grid stayed partly absent).  On an abort every
+// the rest of the launch (the grid stayed partly absent).  (The same kernels
+// may also be launched cooperatively; then the runtime places the grid
+// whole and no barrier gives up.)  On an abort every
 // workgroup stashes its held tiles' inputs (and its share of the escape
 // sections) and leaves the slot to k_decode_slot_defer, launched after this
 // kernel, which decodes the stashed tiles as the two-launch form's second
@@ -1576,7 +1579,7 @@ struct CoopLds {
     uint64_t dr0, dr1;                     // escape ranks of a direct tile
 };
 
-// Grid barrier of the one-kernel in-place decode.  Same-address atomics
+// Grid barrier of the resident in-place decode.  Same-address atomics
 // serialise at the memory side, so the grid arrives in two levels:
 // workgroups on the counter of their group of kCoopGroup, the last of each
 // group on the top counter, whose arrival tells it whether the round is
@@ -2398,7 +2401,7 @@ bool cu_count(int &cus) {
     return true;
 }
 
-// Workgroups of the one-kernel slot decode that the current device keeps
+// Workgroups of the resident slot decode that the current device keeps
 // resident at once (0: none), and whether it has cooperative launches,
 // cached per device (-1: not known yet).
 std::atomic<int> g_coop_grid[kMaxDevices];
@@ -2478,7 +2481,7 @@ bool order_counters(DecArgs &a, uint32_t count) {
     return true;
 }
 
-// The barrier block of a one-kernel slot decode.  Calls on one stream run
+// The barrier block of a resident slot decode.  Calls on one stream run
 // one after another and share a block (each claims it with its own tag);
 // each stream keeps its block while it is among the kCoopBlocks streams of
 // the device that used one last, so two calls that run at the same time

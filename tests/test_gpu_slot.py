@@ -160,7 +160,7 @@ def test_slot_matches_gpu_encode_and_plain_decode(form):
 @pytest.mark.parametrize("make,n,seed", [(W.gaussian_weight, 40 * 2**20 + 5, 1),
                                          (W.log_uniform_stress, 40 * 2**20 + 3, 2)])
 def test_slot_beyond_register_reach(make, n, seed, form):
-    """More tiles overlap the payload than the one-kernel form's grid holds in
+    """More tiles overlap the payload than the resident form's grid holds in
     registers (3 per workgroup): the rest, and the partial last tile, go
     through the stash; stress data also gives held tiles with more escapes
     than their LDS list takes.  GPU encode, then the in-place decode with the
@@ -386,3 +386,35 @@ def test_slot_groups_on_concurrent_streams(form):
                 assert np.array_equal(host_bits(out.cpu()), c[0])
         for out, c in zip(pouts, plain):
             assert np.array_equal(host_bits(out.cpu()), c[0])
+
+
+def test_resident_blocks_across_many_streams():
+    """The resident form's barrier blocks belong to the streams that used one
+    last (64 per device): resident decodes on 70 streams in turn (blocks
+    handed from stream to stream), then on 8 streams at once, every slot
+    exact."""
+    n = 3 * TILE + 4099
+    x = W.gaussian_weight(n, seed=950)
+    xs_h, ocb, opay, om = oracle_case(x)
+    lut = torch.tensor(np.asarray(ocb.dec_lut, np.uint8)).to(DEV)
+    meta = meta_to_device(om, True)
+    streams = [torch.cuda.Stream() for _ in range(70)]
+    _say("resident decodes on 70 streams in turn")
+    for k, st in enumerate(streams):
+        slot = slot_for(opay, n)
+        stash = stash_for(om.comp_bytes)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            out = S.decode_slot(slot, meta, lut, n, stash, stream=st, resident=True)
+        st.synchronize()
+        assert np.array_equal(host_bits(out.cpu()), xs_h), k
+    _say("resident decodes on 8 streams at once")
+    bufs = [(slot_for(opay, n), stash_for(om.comp_bytes)) for _ in range(8)]
+    torch.cuda.synchronize()
+    outs = []
+    for (slot, stash), st in zip(bufs, streams[:8]):
+        with torch.cuda.stream(st):
+            outs.append(S.decode_slot(slot, meta, lut, n, stash, stream=st, resident=True))
+    torch.cuda.synchronize()
+    for k, out in enumerate(outs):
+        assert np.array_equal(host_bits(out.cpu()), xs_h), k
