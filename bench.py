@@ -146,7 +146,9 @@ def design_probes(S, dev):
       plain order of tiles (TB/s);
     * device-scope atomics: dependent adds by one thread (latency), one add
       by each of 8,192 workgroups on one address against 64 spread ones;
-    * 64 launches of an almost empty kernel, ordinary and cooperative."""
+    * 64 launches of an almost empty kernel, ordinary and cooperative;
+    * the in-place decode's forms alone and beside a long kernel on another
+      stream (slot_contention)."""
     import torch
 
     lib = S._abi.ceiling_lib()
@@ -267,6 +269,68 @@ def design_probes(S, dev):
     for coop in (0, 1):
         ms = timed(lambda: ok(lib.splitzip_ceiling_launch(coop, 64, sink.data_ptr(), sh)), 64)
         res["launch"]["cooperative" if coop else "ordinary"] = {"us_per_launch": round(ms * 1e3, 2)}
+    res["slot_contention"] = slot_contention(S, dev)
+    return res
+
+
+def slot_contention(S, dev):
+    """In-place decode of one KV-stream tensor (33,554,432 elements) on its
+    own and while a long elementwise kernel (a multiply over 2^28 floats,
+    small workgroups) runs on another stream, in the two-launch form (the
+    default) and the resident form (ordinary and cooperative launch).  The
+    multiply is enqueued first and a 200,000-cycle spin on the decode's
+    stream lets it take the GPU before the decode starts; HIP events on the
+    decode's stream, median of 5 after one untimed call."""
+    import os
+    import statistics
+
+    import torch
+    import workloads as W
+
+    x = W.kv_cache_tensor(0, 0, device=dev).reshape(-1)
+    n = x.numel()
+    ws = S.Workspace(n, dev)
+    cb = S.calibrate(x, ws)
+    payload, meta = S.encode(x, cb, ws)
+    comp = S.read_meta(meta).comp_bytes
+    pay = payload[:comp].clone()
+    del payload
+    slot = torch.empty(2 * n, dtype=torch.uint8, device=dev)
+    stash = torch.empty(comp, dtype=torch.uint8, device=dev)
+    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sa, sb = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    res = {}
+    old = os.environ.pop("SPLITZIP_SLOT_LAUNCH", None)
+    try:
+        for form in ("two_launch", "resident", "resident_cooperative"):
+            if form == "resident_cooperative":
+                os.environ["SPLITZIP_SLOT_LAUNCH"] = "coop"
+            row = {}
+            for contend in (False, True):
+                ts = []
+                for k in range(6):
+                    slot[:comp].copy_(pay)
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    if contend:
+                        with torch.cuda.stream(sb):
+                            big.mul_(1.0000001)
+                    with torch.cuda.stream(sa):
+                        if contend:
+                            torch.cuda._sleep(200_000)
+                        e0.record(sa)
+                        S.decode_slot(slot, meta, cb, n, stash, stream=sa, resident=form != "two_launch")
+                        e1.record(sa)
+                    torch.cuda.synchronize()
+                    if k:
+                        ts.append(e0.elapsed_time(e1))
+                assert torch.equal(slot.view(torch.int16), x.view(torch.int16)), form
+                row["beside_multiply_ms" if contend else "alone_ms"] = round(statistics.median(ts), 4)
+            res[form] = row
+    finally:
+        os.environ.pop("SPLITZIP_SLOT_LAUNCH", None)
+        if old is not None:
+            os.environ["SPLITZIP_SLOT_LAUNCH"] = old
     return res
 
 def small_configs(S, W, dev, stream, host_inputs=None, only=None):
