@@ -90,3 +90,49 @@ def test_two_streams_own_workspaces():
             assert torch.equal(cb, ref_cb) and torch.equal(meta, ref_meta), (rep, k)
             assert torch.equal(payload[: ref_pay.numel()], ref_pay), (rep, k)
             assert torch.equal(out.view(torch.int16), xs[k].view(torch.int16)), (rep, k)
+
+
+@pytest.mark.parametrize("resident", [False, True])
+def test_graph_replays_slot_decode(resident):
+    """A group of two in-place decodes captured in a graph (two-launch or
+    resident form: the resident barrier's counters are put back by each
+    launch, so every replay starts clean), replayed six times over three
+    different payloads copied into the slot heads between the replays."""
+    n = 5 * 8192 + 777
+    _say("graph slot decode resident=%s" % resident)
+    inputs = [W.gaussian_weight(n, seed=820, device=DEV), W.log_uniform_stress(n, seed=821, device=DEV),
+              W.gaussian_weight(n, seed=822, device=DEV)]
+    ws = S.Workspace(n, DEV)
+    refs = [eager(x, ws) for x in inputs]     # (cb, payload, meta, out)
+    comp_max = max(r[1].numel() for r in refs)
+    slots = [torch.empty(max(2 * n, comp_max), dtype=torch.uint8, device=DEV) for _ in range(2)]
+    stashes = [torch.empty(comp_max, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    cbs = [torch.empty_like(refs[0][0]) for _ in range(2)]
+    metas = [torch.empty_like(refs[0][2]) for _ in range(2)]
+
+    def load(j, k):
+        """payload k into slot j (the rest of the slot scrambled), with its
+        codebook and metadata"""
+        slots[j].fill_(0xA5)
+        slots[j][: refs[k][1].numel()].copy_(refs[k][1])
+        cbs[j].copy_(refs[k][0])
+        metas[j].copy_(refs[k][2])
+
+    # one eager call first (the library caches its device queries)
+    load(0, 0)
+    load(1, 1)
+    S.decode_slots(slots, metas, cbs, [n, n], stashes, resident=resident)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        S.decode_slots(slots, metas, cbs, [n, n], stashes, resident=resident)
+    for rep in range(6):
+        ks = (rep % 3, (rep + 1) % 3)
+        load(0, ks[0])
+        load(1, ks[1])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for j, k in enumerate(ks):
+            got = slots[j][: 2 * n].view(torch.bfloat16)
+            assert torch.equal(got.view(torch.int16), inputs[k].reshape(-1).view(torch.int16)), (rep, j)
