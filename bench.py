@@ -276,7 +276,7 @@ def design_probes(S, dev):
 def slot_contention(S, dev):
     """In-place decode of one KV-stream tensor (33,554,432 elements) on its
     own and while a long elementwise kernel (a multiply over 2^28 floats,
-    small workgroups) runs on another stream, in the two-launch form (the
+    small workgroups) runs on another stream, in the multi-pass form (the
     default) and the resident form (ordinary and cooperative launch).  The
     multiply is enqueued first and a 200,000-cycle spin on the decode's
     stream lets it take the GPU before the decode starts; HIP events on the
@@ -302,7 +302,7 @@ def slot_contention(S, dev):
     res = {}
     old = os.environ.pop("SPLITZIP_SLOT_LAUNCH", None)
     try:
-        for form in ("two_launch", "resident", "resident_cooperative"):
+        for form in ("multi_pass", "resident", "resident_cooperative"):
             if form == "resident_cooperative":
                 os.environ["SPLITZIP_SLOT_LAUNCH"] = "coop"
             row = {}
@@ -319,7 +319,7 @@ def slot_contention(S, dev):
                         if contend:
                             torch.cuda._sleep(200_000)
                         e0.record(sa)
-                        S.decode_slot(slot, meta, cb, n, stash, stream=sa, resident=form != "two_launch")
+                        S.decode_slot(slot, meta, cb, n, stash, stream=sa, resident=form != "multi_pass")
                         e1.record(sa)
                     torch.cuda.synchronize()
                     if k:
@@ -458,10 +458,11 @@ def slot_decode_phase(S, batch, metas_h, x_all, stream, passes):
     are timed with HIP events on the stream they run on (the GPU kept busy
     while the host enqueues them, so the host's marshalling is not timed):
     one call per tensor, then all 64 as one group (32 per launch), in the
-    library's default two-launch form; the same in the resident form (the
-    GPU has nothing else to run here); and groups in the resident form with
-    its first kernel launched cooperatively.  Copies and sleep on the same
-    stream; `torch.cuda._sleep` spins 10M cycles."""
+    library's default multi-pass form (as many passes as still fill the
+    GPU: two per call, six per group of 32 here); the same in the resident
+    form (the GPU has nothing else to run here); and groups in the resident
+    form with its first kernel launched cooperatively.  Copies and sleep on
+    the same stream; `torch.cuda._sleep` spins 10M cycles."""
     import os
     import torch
 
@@ -514,9 +515,9 @@ def slot_decode_phase(S, batch, metas_h, x_all, stream, passes):
         else:
             os.environ["SPLITZIP_SLOT_LAUNCH"] = old
     del stashes
-    return dict(rec(ms), calls=T, form="two-launch form (two kernels per call)",
+    return dict(rec(ms), calls=T, form="multi-pass form (two kernels per call)",
                 batched=dict(rec(ms_b), launches=(T + 31) // 32,
-                             form="two-launch form, two kernels per 32 slots"),
+                             form="multi-pass form, six kernels per 32 slots"),
                 resident=dict(rec(msr), form="resident form, ordinary launch (+ a finishing "
                                              "kernel) per call"),
                 batched_resident=dict(rec(msr_b), form="resident form, one ordinary launch per "
@@ -524,8 +525,10 @@ def slot_decode_phase(S, batch, metas_h, x_all, stream, passes):
                 batched_cooperative=rec(msc_b),
                 note="payload at the head of the output buffer; resident form: the inputs of "
                      "the tiles whose output overlaps it wait in registers across a grid "
-                     "barrier; two-launch form: they are stashed first, i.e. written and read "
-                     "once more")
+                     "barrier; multi-pass form: the packed nibbles of those tiles, and the "
+                     "sign/mantissa bytes of the last pass's tiles, are stashed first (written "
+                     "and read once more), the other tiles decoded in passes ordered so that no "
+                     "output overwrites an input still to be read")
 
 
 def h2d_pipeline(S, batch, metas_h, x_all, dev, count):

@@ -142,6 +142,22 @@ const char *splitzip_status_string(int status);
  * layout rule above).  splitzip_payload_size(n, n) bounds every payload. */
 uint64_t splitzip_payload_size(uint64_t n, uint64_t n_esc);
 
+/* Pass schedule of the in-place decode of n elements (splitzip_decode_slot;
+ * host only, no GPU work), for inspection and tests.  The slot holds the
+ * payload (layout rule above) and receives 2n output bytes; 8192-element
+ * tile t writes bytes [16384 t, 16384 t + 2 len_t).  *t_min receives the
+ * first tile whose output starts at or past the dense sections' end.  Tiles
+ * whose output starts at or past comp_bytes run in pass 1; the tiles from
+ * *t_min up to those run in the last pass; a tile w below *t_min runs in
+ * pass p(w), where p(w) >= k exactly when lo[k] <= w < hi[k] (k = 2 ..
+ * used passes; lo[2] = 0, hi[2] = *t_min).  lo and hi are host arrays of
+ * passes + 1 entries; the entries of levels above the passes used, and [0]
+ * and [1], are set to 0.  Returns the number of passes used (`passes`, or 2
+ * should the schedule not apply), or 0 for passes outside [2, 8], n above
+ * SPLITZIP_MAX_N or a NULL pointer. */
+uint32_t splitzip_slot_schedule(uint64_t n, uint32_t passes, uint64_t *t_min, uint64_t *lo,
+                                uint64_t *hi);
+
 /* Bytes of device workspace needed by calibrate and encode for tensors of up
  * to n elements (host function): about n/4 bytes plus a fixed ~1.2 MB.  Encode
  * keeps one escape count per 8192-element tile and stages up to 512 escapes
@@ -269,18 +285,25 @@ int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const spli
  *               after the slot head has been overwritten (see below)
  *   d_status    optional, as for splitzip_decode (escapes are re-applied from
  *               the decoded sign and mantissa)
- * Two kernels on `stream` (and, with d_status, a validation kernel): the
- * first stashes the inputs of every tile whose output overlaps the payload,
- * and the escape sections, and decodes the other tiles; the second decodes
- * the stashed tiles.  Calls that share a stash must be ordered on one
- * stream.  The kernels' workgroups depend on no other workgroup, so the
- * decode shares the GPU with concurrent work as any kernel does;
+ * Two to six kernels on `stream` (and, with d_status, a validation
+ * kernel), in passes over 8192-element tiles (splitzip_slot_schedule): the
+ * first decodes the tiles whose output lies past the payload and copies to
+ * the stash the escape sections, the packed nibbles of every other tile and
+ * the sign/mantissa bytes of the tiles the last pass decodes; each later
+ * pass decodes the tiles whose output covers only bytes that no tile of the
+ * same or a later pass still reads from the slot, the last pass the rest
+ * from the stash.  Calls that share a stash must be ordered on one stream.
+ * The kernels' workgroups depend on no other workgroup, so the decode
+ * shares the GPU with concurrent work as any kernel does;
  * splitzip_decode_slot_batch_resident is faster on a GPU the decode has to
  * itself.  The environment variable SPLITZIP_SLOT_LAUNCH selects a form for
  * every slot decode of the process: "two" (this one), "one" (the resident
  * form) or "coop" (the resident form, its first kernel launched
- * cooperatively); SPLITZIP_SLOT_WAIT_US sets the resident form's bounded
- * wait in microseconds (0: nearly every barrier gives up).
+ * cooperatively); SPLITZIP_SLOT_PASSES (2..8) fixes this form's number of
+ * passes (2: every overlapping tile's inputs stashed, one pass decoding them
+ * all), which is otherwise chosen per launch (up to 6, fewer when the last
+ * pass would not fill the GPU); SPLITZIP_SLOT_WAIT_US sets the resident form's
+ * bounded wait in microseconds (0: nearly every barrier gives up).
  * Synchronous errors: INVALID (also for overlapping slot and stash), HIP. */
 int splitzip_decode_slot(uint8_t *d_slot, uint64_t slot_bytes, const splitzip_meta *d_meta,
                          const uint8_t *d_dec_lut, uint64_t n, uint8_t *d_stash,
@@ -290,7 +313,7 @@ int splitzip_decode_slot(uint8_t *d_slot, uint64_t slot_bytes, const splitzip_me
  * "Route B (fallback)": the staging route expands the slots of an execution
  * group after their upload, on the upload stream): the
  * same result as splitzip_decode_slot on every item in order, up to 32
- * items sharing each launch of its two kernels.  Each item needs its own
+ * items sharing each launch of its kernels.  Each item needs its own
  * stash; no slot or stash may overlap another item's buffers.  d_status
  * (optional) collects the status bits of all items.
  * Synchronous errors: INVALID (any item; nothing is enqueued), HIP. */

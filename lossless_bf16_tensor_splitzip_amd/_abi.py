@@ -102,6 +102,8 @@ SIGNATURES = {
     "splitzip_struct_sizes": (None, [ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
     "splitzip_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "splitzip_payload_size": (_U64, [_U64, _U64]),
+    "splitzip_slot_schedule": (ctypes.c_uint32, [_U64, ctypes.c_uint32, ctypes.POINTER(_U64),
+                                                ctypes.POINTER(_U64), ctypes.POINTER(_U64)]),
     "splitzip_workspace_size": (_SZ, [_U64]),
     "splitzip_workspace_init": (ctypes.c_int, [_P, _SZ, _P]),
     "splitzip_calibrate": (ctypes.c_int, [_P, _U64, _P, _P, _SZ, _P]),
@@ -204,6 +206,18 @@ def splitzip_abi_version() -> int:
 
 def splitzip_payload_size(n: int, n_esc: int) -> int:
     return lib().splitzip_payload_size(n, n_esc)
+
+
+def splitzip_slot_schedule(n: int, passes: int):
+    """(passes used, t_min, lo, hi) of the in-place decode's pass schedule;
+    lo and hi are lists of passes + 1 entries.  None for invalid arguments."""
+    t_min = ctypes.c_uint64()
+    lo = (ctypes.c_uint64 * (passes + 1))()
+    hi = (ctypes.c_uint64 * (passes + 1))()
+    used = lib().splitzip_slot_schedule(n, passes, ctypes.byref(t_min), lo, hi)
+    if used == 0:
+        return None
+    return used, t_min.value, list(lo), list(hi)
 
 
 def splitzip_workspace_size(n: int) -> int:

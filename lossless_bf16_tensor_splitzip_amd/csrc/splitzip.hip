@@ -1124,17 +1124,34 @@ struct DecItem {
     uint16_t *out;
     uint64_t n;
     // In-place (slot) decode: the payload sits at the head of the output
-    // buffer.  Pass 1 stashes the inputs of the tiles whose output overlaps
-    // the payload into `stash` (same offsets as in the payload) and decodes
-    // the other tiles directly; pass 2 decodes the stashed tiles.
+    // buffer.  Pass 1 copies into `stash` (same offsets as in the payload)
+    // what later passes read after the slot head has been overwritten, and
+    // decodes the tiles whose output lies past the payload; the later passes
+    // decode the rest (see the schedule above k_decode_slot_stage).
     uint8_t *stash;         // pass 1 only
     uint64_t other_bytes;   // size of the buffer the pass does not read from
 };
 
+// One tensor's share of a pass of the multi-pass in-place decode (tile
+// indices; see the schedule above k_decode_slot_stage).  Pass 1: the tiles
+// [a0, a1) also copy their sm bytes to the stash.  Later passes: the
+// launch's workgroups for this tensor decode the tiles [a0, a1) then
+// [b0, b1).  In the tensor's last pass (last != 0) they read their sm bytes
+// from the stash, and `extra` workgroups come before them, one for each tile
+// from t_min on whose output may overlap the payload (the host bounds the
+// payload by the slot and the stash); every workgroup of the last pass then
+// applies an escape stream not marked ascending.
+struct SlotPass {
+    uint32_t t_min;   // first tile whose output starts at or past the dense sections' end
+    uint32_t a0, a1, b0, b1;
+    uint32_t last, extra;
+};
+
 struct DecArgs {
     uint32_t count;
-    uint64_t tile_start[kMaxBatch + 1];   // first decode tile of each tensor
+    uint64_t tile_start[kMaxBatch + 1];   // first decode tile (slot passes: workgroup) of each tensor
     DecItem it[kMaxBatch];
+    SlotPass pass[kMaxBatch];             // multi-pass in-place decode only
     int32_t *status;
     uint64_t *order_sync;                 // this device's arrival counters (below)
     uint64_t order_ticket;                // this call's first counter, and its tag
@@ -1142,6 +1159,7 @@ struct DecArgs {
     uint32_t hold_tag;                    // its tag,
     uint32_t wait_ticks;                  // and the barrier's bounded wait (10 ns ticks)
 };
+static_assert(sizeof(DecArgs) <= 4096, "kernel arguments");
 
 // Arrival counters of the order-independent escape pass (streams not marked
 // ascending): tensor k of a call uses counter (ticket + k) mod kOrderSlots,
@@ -1163,7 +1181,7 @@ __device__ inline bool meta_ok(const DecItem &I, const splitzip_meta &m, Layout 
 }
 __device__ inline bool meta_ok(const DecItem &I, Layout &L) { return meta_ok(I, *I.meta, L); }
 
-enum DecMode { kPlain = 0, kSlotStage = 1, kSlotFinish = 2 };
+enum DecMode { kPlain = 0, kSlotStage = 1, kSlotLevel = 2 };
 
 // Slot decode: first tile whose output lies wholly beyond the payload.
 __device__ inline uint64_t slot_split(uint64_t comp_bytes, uint64_t tiles, uint64_t tile) {
@@ -1267,122 +1285,31 @@ __device__ inline void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int kTh, int kUnits, int kMode>
-__device__ __forceinline__ void decode_tile(const DecArgs &a) {
+// Dense decode and escape patch of one tile.  A full tile's pk and sm words
+// are in registers; pk and sm point at the sections that a partial tile and
+// the patch read, the escape sections are at I.payload, and the pair table
+// is in LDS.
+template <int kTh, int kUnits>
+__device__ __forceinline__ void decode_body(const DecItem &I, const splitzip_meta &M, const Layout &L,
+                                            uint64_t base, bool full, const uint8_t *pk,
+                                            const uint8_t *sm, const uint32_t (&pkw)[kUnits],
+                                            const u32x2 (&smw)[kUnits], const uint32_t *pair_lut,
+                                            uint64_t *range, uint32_t *tile_buf) {
     constexpr int kDecTile = kTh * kUnit * kUnits;
-    __shared__ uint32_t pair_lut[256];      // pk byte -> (even exponent, odd exponent << 16)
-    __shared__ uint64_t range[2];
-    __shared__ uint32_t last_arrival;
-    // Output tile of a tensor with dense escapes, or the sm bytes of a tile
-    // with many escapes in an otherwise sparse tensor.
-    __shared__ uint32_t tile_buf[kDecTile / 2];
-    const uint64_t gt = launch_tile(blockIdx.x, gridDim.x);
-    const uint32_t item = find_item(a.tile_start, a.count, gt);
-    const DecItem I = a.it[item];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const uint64_t tile = gt - a.tile_start[item];
-    const uint64_t base = tile * kDecTile;
-    const bool full = base + kDecTile <= I.n;
-    // The dense sections depend on n alone (the host checked that the buffer
-    // holds them), so their loads go out before the metadata arrives; in the
-    // second slot pass only for tiles that are certain to be stashed.
-    const Layout L0 = layout_of(I.n, 0);
-    const uint8_t *pk = I.payload;
-    const uint8_t *sm = I.payload + L0.off_sm;
-    uint32_t pkw[kUnits];
-    u32x2 smw[kUnits];
-    // second slot pass: tiles before the dense sections' end are certainly stashed
-    const bool early = full && (kMode != kSlotFinish || tile < L0.total / (2 * kDecTile));
-    if (early) {
-#pragma unroll
-        for (int u = 0; u < kUnits; ++u) {
-            const uint64_t i0 = base + (uint64_t)u * (kTh * kUnit) + tid * kUnit;
-            pkw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(pk + i0 / 2));
-            smw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4 *>(sm + i0));
-        }
-    }
-    // Then the metadata, as one copy: the compiler reads it with scalar
-    // loads, whose wait leaves the stream loads in flight (reading fields
-    // through the pointer took vector loads, and vector loads complete in
-    // order, so their wait was a wait for the whole tile), and the table's two
-    // bytes, loaded by every lane (no branch around the loads) and combined
-    // where the table is written.
-    const splitzip_meta M = *I.meta;
-    const uint32_t lut_lo = I.dec_lut[(tid >> 4) & 15];   // (every lane: no branch around
-    const uint32_t lut_hi = I.dec_lut[tid & 15];          // the loads)
-    Layout L;
-    if (!meta_ok(I, M, L) || (kMode != kPlain && L.total > I.other_bytes)) {
-        // nothing is written for inconsistent metadata
-        if (kMode != kSlotFinish && gt == a.tile_start[item] && tid == 0 && a.status)
-            atomicOr(a.status, 1);
-        return;
-    }
-    if (kMode != kPlain) {
-        const uint64_t tiles = (I.n + kDecTile - 1) / kDecTile;
-        const uint64_t t_split = slot_split(L.total, tiles, kDecTile);
-        if (kMode == kSlotStage) {
-            // Every workgroup of the tensor copies its share of the escape
-            // sections.
-            const uint64_t esc_bytes = L.total - L.off_cid;
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(I.payload + L.off_cid);
-            uint32_t *dst = reinterpret_cast<uint32_t *>(I.stash + L.off_cid);
-            const uint64_t stride = tiles * kTh;
-            for (uint64_t w = tile * kTh + tid; w < esc_bytes / 4; w += stride) dst[w] = src[w];
-            if (tile == 0 && tid < (int)(esc_bytes & 3)) {
-                const uint64_t b = L.off_cid + (esc_bytes & ~uint64_t(3)) + tid;
-                I.stash[b] = I.payload[b];
-            }
-            if (tile < t_split) {   // output overlaps the payload: stash the inputs
-                if (full) {
-#pragma unroll
-                    for (int u = 0; u < kUnits; ++u) {
-                        const uint64_t i0 = base + (uint64_t)u * (kTh * kUnit) + tid * kUnit;
-                        *reinterpret_cast<uint32_t *>(I.stash + i0 / 2) = pkw[u];
-                        *reinterpret_cast<u32x2_a4 *>(I.stash + L0.off_sm + i0) = smw[u];
-                    }
-                } else {
-                    for (uint64_t b = base / 2 + tid; b < L0.n_pairs; b += kTh)
-                        I.stash[b] = pk[b];
-                    for (uint64_t i = base + tid; i < I.n; i += kTh)
-                        I.stash[L0.off_sm + i] = sm[i];
-                }
-                return;
-            }
-        } else {
-            if (tile >= t_split) {   // decoded by the first pass
-                if (M.n_esc && !(M.flags & SPLITZIP_META_ASCENDING))
-                    order_pass<true>(a, I, item, L, &last_arrival);
-                return;
-            }
-            if (full && !early) {
-#pragma unroll
-                for (int u = 0; u < kUnits; ++u) {
-                    const uint64_t i0 = base + (uint64_t)u * (kTh * kUnit) + tid * kUnit;
-                    pkw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(pk + i0 / 2));
-                    smw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4 *>(sm + i0));
-                }
-            }
-        }
-    }
     const uint64_t e = M.n_esc;
     const int32_t *cid = reinterpret_cast<const int32_t *>(I.payload + L.off_cid);
     const uint16_t *lpos = reinterpret_cast<const uint16_t *>(I.payload + L.off_lpos);
     const uint8_t *ev = I.payload + L.off_ev;
 
-    static_assert(kTh >= 256, "one pair-table entry per thread");
     // A tensor whose escapes average more than 512 per tile is decoded tile
     // by tile in LDS (dense values, the patch, then one coalesced store):
     // scattering thousands of 2-byte stores per tile to memory costs more
     // than writing the tile twice.
-    // An escape stream not known to be ascending cannot be searched per
-    // tile: after the dense part the last workgroup of the tensor applies
-    // every escape.
     const bool ascending = (M.flags & SPLITZIP_META_ASCENDING) != 0;
     const bool in_lds = ascending && full && e * (uint64_t)kDecTile > 512 * I.n;
     const uint32_t chunk = (uint32_t)M.chunk_size;
-    if (tid < 256) pair_lut[tid] = lut_lo | (lut_hi << 16);
-    lds_barrier();   // the pair table; the stream loads may still be in flight
 
     // Dense part first: every element through the pair table, 16-byte stores.
     if (full) {
@@ -1408,11 +1335,9 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
             I.out[i] = (uint16_t)join16(sm[i], pair_lut[code << 4] & 0xFFu);
         }
     }
-    if (e == 0) return;
-    if (!ascending) {
-        if (kMode != kSlotStage) order_pass<kMode == kSlotFinish>(a, I, item, L, &last_arrival);
-        return;
-    }
+    // An escape stream not known to be ascending cannot be searched per
+    // tile: it is applied by index after the dense part of every tile.
+    if (e == 0 || !ascending) return;
 
     // Escape patch: the tile's escapes are among those with chunk ids in
     // [c0, c1) of the sorted stream (exactly those when tiles and chunks
@@ -1517,17 +1442,181 @@ __device__ __forceinline__ void decode_tile(const DecArgs &a) {
     }
 }
 
+template <int kTh, int kUnits, int kMode>
+__device__ __forceinline__ void decode_tile(const DecArgs &a) {
+    constexpr int kDecTile = kTh * kUnit * kUnits;
+    static_assert(kTh >= 256, "one pair-table entry per thread");
+    __shared__ uint32_t pair_lut[256];      // pk byte -> (even exponent, odd exponent << 16)
+    __shared__ uint64_t range[2];
+    __shared__ uint32_t last_arrival;
+    // Output tile of a tensor with dense escapes, or the sm bytes of a tile
+    // with many escapes in an otherwise sparse tensor.
+    __shared__ uint32_t tile_buf[kDecTile / 2];
+    const uint64_t gt = launch_tile(blockIdx.x, gridDim.x);
+    const uint32_t item = find_item(a.tile_start, a.count, gt);
+    const DecItem I = a.it[item];
+    const int tid = threadIdx.x;
+    const Layout L0 = layout_of(I.n, 0);
+    uint64_t tile = gt - a.tile_start[item];
+    // Slot passes: the tile this workgroup decodes, and where its sm bytes
+    // are (the slot in passes before the tensor's last one, else the stash).
+    const uint8_t *sm_src = I.payload;
+    bool sm_copy = false;   // pass 1: this tile's sm bytes go to the stash
+    bool has_tile = true;   // last pass: false for the workgroups placed before the others
+    if (kMode == kSlotLevel) {
+        const SlotPass Q = a.pass[item];
+        uint64_t j = tile;
+        if (Q.last) {
+            has_tile = j >= Q.extra;
+            j = has_tile ? j - Q.extra : 0;
+        }
+        const uint64_t la = Q.a1 - Q.a0;
+        tile = j < la ? Q.a0 + j : Q.b0 + (j - la);
+        if (!Q.last) sm_src = reinterpret_cast<const uint8_t *>(I.out);
+    } else if (kMode == kSlotStage) {
+        const SlotPass Q = a.pass[item];
+        sm_copy = tile >= Q.t_min || (tile >= Q.a0 && tile < Q.a1);
+    }
+    const uint64_t base = tile * kDecTile;
+    const bool full = has_tile && base + kDecTile <= I.n;
+    // The dense sections depend on n alone (the host checked that the buffers
+    // hold them), so their loads go out before the metadata arrives; in pass
+    // 1 the sm bytes only of the tiles that need them.
+    const uint8_t *pk = I.payload;
+    const uint8_t *sm = sm_src + L0.off_sm;
+    uint32_t pkw[kUnits];
+    u32x2 smw[kUnits];
+    if (full) {
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u) {
+            const uint64_t i0 = base + (uint64_t)u * (kTh * kUnit) + tid * kUnit;
+            pkw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(pk + i0 / 2));
+            if (kMode != kSlotStage || sm_copy)
+                smw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4 *>(sm + i0));
+        }
+    }
+    // Then the metadata, as one copy: the compiler reads it with scalar
+    // loads, whose wait leaves the stream loads in flight (reading fields
+    // through the pointer took vector loads, and vector loads complete in
+    // order, so their wait was a wait for the whole tile), and the table's two
+    // bytes, loaded by every lane (no branch around the loads) and combined
+    // where the table is written.
+    const splitzip_meta M = *I.meta;
+    const uint32_t lut_lo = I.dec_lut[(tid >> 4) & 15];
+    const uint32_t lut_hi = I.dec_lut[tid & 15];
+    Layout L;
+    if (!meta_ok(I, M, L) || (kMode != kPlain && L.total > I.other_bytes)) {
+        // nothing is written for inconsistent metadata
+        if (kMode != kSlotLevel && gt == a.tile_start[item] && tid == 0 && a.status)
+            atomicOr(a.status, 1);
+        return;
+    }
+    const uint64_t tiles = (I.n + kDecTile - 1) / kDecTile;
+    const uint64_t t_split = kMode == kPlain ? tiles : slot_split(L.total, tiles, kDecTile);
+    if (kMode == kSlotStage) {
+        // Every workgroup of the tensor copies its share of the escape
+        // sections.
+        const uint64_t esc_bytes = L.total - L.off_cid;
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(I.payload + L.off_cid);
+        uint32_t *dst = reinterpret_cast<uint32_t *>(I.stash + L.off_cid);
+        const uint64_t stride = tiles * kTh;
+        for (uint64_t w = tile * kTh + tid; w < esc_bytes / 4; w += stride) dst[w] = src[w];
+        if (tile == 0 && tid < (int)(esc_bytes & 3)) {
+            const uint64_t b = L.off_cid + (esc_bytes & ~uint64_t(3)) + tid;
+            I.stash[b] = I.payload[b];
+        }
+        if (tile < t_split) {   // output overlaps the payload: copy the inputs a later pass reads
+            if (full) {
+#pragma unroll
+                for (int u = 0; u < kUnits; ++u) {
+                    const uint64_t i0 = base + (uint64_t)u * (kTh * kUnit) + tid * kUnit;
+                    *reinterpret_cast<uint32_t *>(I.stash + i0 / 2) = pkw[u];
+                    if (sm_copy) *reinterpret_cast<u32x2_a4 *>(I.stash + L0.off_sm + i0) = smw[u];
+                }
+            } else {
+                for (uint64_t b = base / 2 + tid; b < L0.n_pairs; b += kTh) I.stash[b] = pk[b];
+                if (sm_copy)
+                    for (uint64_t i = base + tid; i < I.n; i += kTh) I.stash[L0.off_sm + i] = sm[i];
+            }
+            return;
+        }
+    }
+    if (tid < 256) pair_lut[tid] = lut_lo | (lut_hi << 16);
+    lds_barrier();   // the pair table; the stream loads may still be in flight
+    const bool ordered = M.n_esc && !(M.flags & SPLITZIP_META_ASCENDING);
+    if (kMode != kSlotLevel) {
+        decode_body<kTh, kUnits>(I, M, L, base, full, pk, sm, pkw, smw, pair_lut, range, tile_buf);
+        if (kMode == kPlain && ordered) order_pass<false>(a, I, item, L, &last_arrival);
+        return;
+    }
+    // Slot pass: one tile per workgroup (a second tile's code in the same
+    // kernel, as a loop or a second copy, doubled its registers and cost the
+    // pass occupancy).  In the tensor's last pass workgroup m < extra takes
+    // tile t_min + m, whose output overlaps the payload past the dense
+    // sections (it covers the escape sections), every input from the stash;
+    // nothing when that tile's output lies past the payload.
+    const SlotPass Q = a.pass[item];
+    if (has_tile)
+        decode_body<kTh, kUnits>(I, M, L, base, full, pk, sm, pkw, smw, pair_lut, range, tile_buf);
+    else if (Q.t_min + (gt - a.tile_start[item]) < t_split) {
+        const uint64_t bt = (Q.t_min + (gt - a.tile_start[item])) * kDecTile;
+        const bool ft = bt + kDecTile <= I.n;
+        const uint8_t *sms = I.payload + L0.off_sm;
+        if (ft) {
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) {
+                const uint64_t i0 = bt + (uint64_t)u * (kTh * kUnit) + tid * kUnit;
+                pkw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(pk + i0 / 2));
+                smw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4 *>(sms + i0));
+            }
+        }
+        decode_body<kTh, kUnits>(I, M, L, bt, ft, pk, sms, pkw, smw, pair_lut, range, tile_buf);
+    }
+    if (Q.last && ordered) order_pass<true>(a, I, item, L, &last_arrival);
+}
+
 template <int kUnits>
 __global__ __launch_bounds__(kDecThreads) void k_decode(DecArgs a) {
     decode_tile<kDecThreads, kUnits, kPlain>(a);
 }
 
+// ---------------------------------------------------------------------------
+// In-place decode, multi-pass form (page 1, decode_slot_into; page "SplitZip
+// in DDO -- VMM routes", the CUDA route's expansion in place)
+// ---------------------------------------------------------------------------
+//
+// Tile t (T = 8192 elements, len_t of them) reads pk bytes [tT/2, ...), sm
+// bytes [S + tT, S + tT + len_t) (S = the sm section's offset) and the
+// escape sections, and writes slot bytes [2tT, 2tT + 2len_t).  Pass 1
+// (k_decode_slot_stage) decodes the tiles whose output starts at or past
+// comp_bytes (t >= t_split) and copies to the stash the escape sections, the
+// pk bytes of every other tile, and the sm bytes of the tiles named below.
+// From pass 2 on (k_decode_slot_level) every tile reads its pk bytes and
+// the escapes from the stash, so the one hazard left is a tile w whose
+// output covers the sm bytes of another tile t that reads them from the
+// slot: t must run in an earlier pass than w.  For the tiles below t_min
+// (output starting before the dense sections' end), with readers(w) the
+// tiles below t_min whose sm bytes meet w's output:
+//   depth(w) = 0 without readers, 1 + max depth(readers) otherwise, and
+//              unbounded when w is among its own readers;
+//   pass(w)  = min(K, 2 + depth(w)).
+// Tiles at pass K, and the tiles from t_min to t_split (their outputs cover
+// the escape sections), read their sm bytes from the stash as well; pass K
+// decodes both.  A tile's readers lie all below it or all above it (a range
+// around 2w - S/T), depth grows toward the tile(s) that overlap their own
+// sm bytes, so each pass's tiles form one range on each side of those and
+// the host finds the ranges by bisection.  With K passes the stash carries
+// the pk bytes (a quarter of the tensor's raw bytes) plus the sm bytes of
+// the pass-K tiles (about 3/2^(K+1) of the tiles) instead of every
+// overlapping tile's inputs, so the slot decode moves about 1.32x its
+// algorithmic bytes at K = 4 against 1.65x at K = 2 (every overlapping tile
+// stashed, pass 2 decoding them all).
 __global__ __launch_bounds__(kDecThreads) void k_decode_slot_stage(DecArgs a) {
     decode_tile<kDecThreads, kDecUnits, kSlotStage>(a);
 }
 
-__global__ __launch_bounds__(kDecThreads) void k_decode_slot_finish(DecArgs a) {
-    decode_tile<kDecThreads, kDecUnits, kSlotFinish>(a);
+__global__ __launch_bounds__(kDecThreads) void k_decode_slot_level(DecArgs a) {
+    decode_tile<kDecThreads, kDecUnits, kSlotLevel>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -2680,10 +2769,116 @@ int launch_decode(const DecItem *items, uint32_t count, int32_t *status, hipStre
     return launched();
 }
 
+// Multi-pass in-place decode schedule (see the comment above
+// k_decode_slot_stage): tile w < t_min runs in pass p(w) in [2, passes];
+// p(w) >= k exactly when lo[k] <= w < hi[k] (k >= 2; lo[2] = 0, hi[2] =
+// t_min).
+constexpr uint32_t kSlotMaxPasses = 8;
+// Passes chosen per launch: the most, up to kSlotAutoPasses, whose last pass
+// still has kSlotMinFinal workgroups over the launch's tensors.  Measured on
+// 64 KV tensors of 2^25 elements (4,096 tiles each): groups of 32 slots take
+// 2.02 / 1.73 / 1.59 ms for 2 / 3 / 6 passes (6,144 workgroups in the last of
+// six); one slot per call 2.60 / 2.73 ms for 2 / 3 passes (1,536 workgroups
+// in the last of three), a launch that does not fill the GPU costing more
+// than the stash bytes it saves.
+constexpr uint32_t kSlotAutoPasses = 6;
+constexpr uint64_t kSlotMinFinal = 4096;
+struct SlotPlan {
+    uint32_t passes;
+    uint64_t t_min;
+    uint64_t lo[kSlotMaxPasses + 1], hi[kSlotMaxPasses + 1];
+};
+
+struct SlotGeom {
+    uint64_t n, tiles, t_min, s0;
+};
+
+// Tiles below t_min whose sm bytes meet tile w's output: [ta, tb]; false when none.
+bool slot_readers(const SlotGeom &G, uint64_t w, uint64_t &ta, uint64_t &tb) {
+    constexpr uint64_t T = kCoopTile;
+    const uint64_t len = G.n - w * T < T ? G.n - w * T : T;
+    const uint64_t o0 = 2 * w * T, o1 = o0 + 2 * len;
+    if (o1 <= G.s0 || o0 >= G.s0 + G.n) return false;
+    ta = o0 > G.s0 ? (o0 - G.s0) / T : 0;
+    tb = (o1 - 1 - G.s0) / T;
+    if (tb > G.t_min - 1) tb = G.t_min - 1;
+    return ta <= tb;
+}
+
+// min(passes, 2 + depth(w)), following the reader nearest the
+// self-overlapping tiles (the deepest one).
+uint32_t slot_pass_of(const SlotGeom &G, uint64_t w, uint32_t passes) {
+    uint32_t d = 2;
+    while (d < passes) {
+        uint64_t ta, tb;
+        if (!slot_readers(G, w, ta, tb)) return d;
+        if (ta <= w && w <= tb) return passes;
+        w = tb < w ? tb : ta;
+        ++d;
+    }
+    return d;
+}
+
+SlotPlan slot_plan(uint64_t n, uint32_t passes) {
+    constexpr uint64_t T = kCoopTile;
+    SlotPlan P{};
+    const Layout L0 = layout_of(n, 0);
+    const uint64_t tiles = (n + T - 1) / T;
+    uint64_t t_min = (L0.off_cid + 2 * T - 1) / (2 * T);
+    if (t_min > tiles) t_min = tiles;
+    P.t_min = t_min;
+    P.passes = 2;
+    P.lo[2] = 0;
+    P.hi[2] = t_min;
+    if (t_min == 0 || passes <= 2) return P;
+    const SlotGeom G{n, tiles, t_min, L0.off_sm};
+    // a tile that overlaps its own sm bytes: the one holding the section's first byte
+    uint64_t wz = L0.off_sm / T;
+    if (wz > t_min - 1) wz = t_min - 1;
+    if (slot_pass_of(G, wz, passes) != passes) return P;   // not expected; two passes are always valid
+    for (uint32_t k = 3; k <= passes; ++k) {
+        // pass is nondecreasing on [0, wz] and nonincreasing on [wz, t_min)
+        uint64_t lo = 0, hi = wz;   // first w in [0, wz] with pass >= k
+        while (lo < hi) {
+            const uint64_t mid = lo + (hi - lo) / 2;
+            if (slot_pass_of(G, mid, passes) >= k) hi = mid; else lo = mid + 1;
+        }
+        P.lo[k] = lo;
+        lo = wz + 1;
+        hi = t_min;   // first w in (wz, t_min) with pass < k, else t_min
+        while (lo < hi) {
+            const uint64_t mid = lo + (hi - lo) / 2;
+            if (slot_pass_of(G, mid, passes) < k) hi = mid; else lo = mid + 1;
+        }
+        P.hi[k] = lo;
+    }
+    P.passes = passes;
+    return P;
+}
+
+// Number of passes for a launch of `count` slots (SPLITZIP_SLOT_PASSES, 2..8,
+// fixes it for every launch).
+uint32_t slot_passes(const splitzip_slot_item *items, uint32_t count) {
+    if (const char *v = getenv("SPLITZIP_SLOT_PASSES")) {
+        const unsigned long k = strtoul(v, nullptr, 10);
+        return k < 2 ? 2u : (k > kSlotMaxPasses ? kSlotMaxPasses : (uint32_t)k);
+    }
+    for (uint32_t k = kSlotAutoPasses; k > 2; --k) {
+        uint64_t last = 0;
+        for (uint32_t i = 0; i < count; ++i) {
+            const SlotPlan P = slot_plan(items[i].n, k);
+            if (P.passes == k) last += P.hi[k] - P.lo[k];
+        }
+        if (last >= kSlotMinFinal) return k;
+    }
+    return 2;
+}
+
 // In-place decode of up to kMaxBatch payloads, each at the head of its own
-// output buffer (a slot): pass 1 stashes the inputs of the tiles whose
-// output overlaps the payload and decodes the rest, pass 2 decodes the
-// stashed tiles over the payload.
+// output buffer (a slot): the resident form, or the multi-pass form (pass 1
+// copies to the stash what later passes read after the slot head has been
+// overwritten and decodes the tiles past the payload, later passes decode
+// the rest).
 int launch_decode_slot(const splitzip_slot_item *items, uint32_t count, int32_t *status, bool resident,
                        hipStream_t s) {
     constexpr uint64_t kTile = (uint64_t)kDecUnits * kDecThreads * kUnit;
@@ -2738,7 +2933,18 @@ int launch_decode_slot(const splitzip_slot_item *items, uint32_t count, int32_t 
         k_decode_slot_defer<<<(unsigned)(cus < (int)kCoopMaxGrid ? cus : (int)kCoopMaxGrid), kDecThreads,
                               0, s>>>(a);
         if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
-    } else {
+    }
+    SlotPlan plan[kMaxBatch];
+    uint32_t most = 2;
+    if (!grid) {
+        const uint32_t passes = slot_passes(items, count);
+        for (uint32_t k = 0; k < count; ++k) {
+            plan[k] = slot_plan(items[k].n, passes);
+            const SlotPlan &P = plan[k];
+            a.pass[k] = SlotPass{(uint32_t)P.t_min, (uint32_t)P.lo[P.passes], (uint32_t)P.hi[P.passes],
+                                 0, 0, 0, 0};
+            if (P.passes > most) most = P.passes;
+        }
         k_decode_slot_stage<<<(unsigned)tiles, kDecThreads, 0, s>>>(a);
         if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     }
@@ -2748,8 +2954,38 @@ int launch_decode_slot(const splitzip_slot_item *items, uint32_t count, int32_t 
         a.it[k].stash = nullptr;
         a.it[k].other_bytes = items[k].slot_bytes;
     }
-    if (!grid) {
-        k_decode_slot_finish<<<(unsigned)tiles, kDecThreads, 0, s>>>(a);
+    for (uint32_t p = 2; !grid && p <= most; ++p) {
+        // pass p: per tensor the tiles [lo[p], lo[p+1]) and [hi[p+1], hi[p]),
+        // or in its last pass [lo[p], hi[p])
+        uint64_t wgs = 0;
+        for (uint32_t k = 0; k < count; ++k) {
+            const SlotPlan &P = plan[k];
+            SlotPass Q{(uint32_t)P.t_min, 0, 0, 0, 0, 0, 0};
+            if (items[k].n && p < P.passes) {
+                Q.a0 = (uint32_t)P.lo[p];
+                Q.a1 = (uint32_t)P.lo[p + 1];
+                Q.b0 = (uint32_t)P.hi[p + 1];
+                Q.b1 = (uint32_t)P.hi[p];
+            } else if (items[k].n && p == P.passes) {
+                Q.a0 = (uint32_t)P.lo[p];
+                Q.a1 = (uint32_t)P.hi[p];
+                Q.last = 1;
+                // one workgroup per tile from t_min on whose output may
+                // overlap the payload: it fits both the slot and the stash
+                const uint64_t room = items[k].slot_bytes < items[k].stash_bytes
+                                          ? items[k].slot_bytes : items[k].stash_bytes;
+                uint64_t reach = ceil_div(room, 2 * kTile);
+                const uint64_t tiles_k = ceil_div(items[k].n, kTile);
+                if (reach > tiles_k) reach = tiles_k;
+                Q.extra = (uint32_t)(reach > P.t_min ? reach - P.t_min : 0);
+            }
+            a.pass[k] = Q;
+            a.tile_start[k] = wgs;
+            wgs += (uint64_t)(Q.a1 - Q.a0) + (Q.b1 - Q.b0) + Q.extra;
+        }
+        a.tile_start[count] = wgs;
+        if (wgs == 0) continue;
+        k_decode_slot_level<<<(unsigned)wgs, kDecThreads, 0, s>>>(a);
         if (hipGetLastError() != hipSuccess) return SPLITZIP_ERR_HIP;
     }
     if (status) {
@@ -2799,6 +3035,18 @@ const char *splitzip_status_string(int status) {
 }
 
 uint64_t splitzip_payload_size(uint64_t n, uint64_t n_esc) { return layout_of(n, n_esc).total; }
+
+uint32_t splitzip_slot_schedule(uint64_t n, uint32_t passes, uint64_t *t_min, uint64_t *lo,
+                                uint64_t *hi) {
+    if (n > SPLITZIP_MAX_N || passes < 2 || passes > kSlotMaxPasses || !t_min || !lo || !hi) return 0;
+    const SlotPlan P = slot_plan(n, passes);
+    *t_min = P.t_min;
+    for (uint32_t k = 0; k <= passes; ++k) {
+        lo[k] = k >= 2 && k <= P.passes ? P.lo[k] : 0;
+        hi[k] = k >= 2 && k <= P.passes ? P.hi[k] : 0;
+    }
+    return P.passes;
+}
 
 size_t splitzip_workspace_size(uint64_t n) {
     uint64_t t = enc_tiles(n);

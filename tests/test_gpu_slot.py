@@ -26,22 +26,27 @@ def setup_module(module):
     S.lib()
 
 
-@pytest.fixture(params=["two", "resident", "resident_abort", "coop"])
+@pytest.fixture(params=["two", "passes2", "passes3", "passes8", "resident", "resident_abort",
+                        "coop"])
 def form(request, monkeypatch):
-    """Form of the in-place decode: the library's two-launch form (the
-    default entry points), the resident form (the resident entry point;
-    one grid barrier per slot, in an ordinary launch), the same with a zero
-    barrier wait, so that nearly every barrier gives up and the slot is
-    finished by the deferral kernel (the path taken when concurrent work
-    keeps the grid from being placed), or the resident form launched
-    cooperatively (forced for every call)."""
+    """Form of the in-place decode: the library's multi-pass form (the
+    default entry points; its default number of passes, or 2, 3 or 8
+    passes), the resident form (the resident entry point; one grid barrier
+    per slot, in an ordinary launch), the same with a zero barrier wait, so
+    that nearly every barrier gives up and the slot is finished by the
+    deferral kernel (the path taken when concurrent work keeps the grid
+    from being placed), or the resident form launched cooperatively (forced
+    for every call)."""
     monkeypatch.delenv("SPLITZIP_SLOT_WAIT_US", raising=False)
     monkeypatch.delenv("SPLITZIP_SLOT_LAUNCH", raising=False)
+    monkeypatch.delenv("SPLITZIP_SLOT_PASSES", raising=False)
     if request.param == "resident_abort":
         monkeypatch.setenv("SPLITZIP_SLOT_WAIT_US", "0")
     elif request.param == "coop":
         monkeypatch.setenv("SPLITZIP_SLOT_LAUNCH", "coop")
-    _RESIDENT[0] = request.param != "two"
+    elif request.param.startswith("passes"):
+        monkeypatch.setenv("SPLITZIP_SLOT_PASSES", request.param[len("passes"):])
+    _RESIDENT[0] = request.param in ("resident", "resident_abort", "coop")
     yield request.param
     _RESIDENT[0] = False
 
