@@ -294,9 +294,9 @@ int splitzip_decode(const uint8_t *d_payload, uint64_t payload_bytes, const spli
  * same or a later pass still reads from the slot, the last pass the rest
  * from the stash.  Calls that share a stash must be ordered on one stream.
  * The kernels' workgroups depend on no other workgroup, so the decode
- * shares the GPU with concurrent work as any kernel does;
- * splitzip_decode_slot_batch_resident is faster on a GPU the decode has to
- * itself.  The environment variable SPLITZIP_SLOT_LAUNCH selects a form for
+ * shares the GPU with concurrent work as any kernel does (on a GPU the
+ * decode has to itself, splitzip_decode_slot_batch_resident is faster for
+ * single slots and slower for groups).  The environment variable SPLITZIP_SLOT_LAUNCH selects a form for
  * every slot decode of the process: "two" (this one), "one" (the resident
  * form) or "coop" (the resident form, its first kernel launched
  * cooperatively); SPLITZIP_SLOT_PASSES (2..8) fixes this form's number of
@@ -322,8 +322,8 @@ int splitzip_decode_slot_batch(const splitzip_slot_item *items, uint32_t count, 
 
 /* In-place decode of a group of slots (page "SplitZip in DDO -- VMM routes",
  * as splitzip_decode_slot_batch): the same result, in a form that needs the
- * whole grid resident at once and pays off on a GPU that the decode has to
- * itself (e.g. a bulk restore between compute phases).  Two kernels per 32
+ * whole grid resident at once and pays off for single slots on a GPU that the
+ * decode has to itself (e.g. a bulk restore between compute phases).  Two kernels per 32
  * items on `stream`.  The first is an ordinary launch of as many workgroups
  * as the GPU keeps resident at once: each decodes its tiles whose output
  * lies past the payload, loads the inputs of up to three whole tiles whose

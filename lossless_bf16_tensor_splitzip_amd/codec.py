@@ -212,7 +212,7 @@ def decode_slots(slots, metas, cbs_or_luts, ns, stashes, status: torch.Tensor | 
     ``resident`` the library's resident form runs (one grid barrier per
     slot, overlapping tiles held in registers; it gives up and finishes the
     slots later when concurrent work keeps its grid from being placed), else
-    the two-launch form, which shares the GPU with concurrent work."""
+    the multi-pass form, which shares the GPU with concurrent work."""
     count = len(slots)
     if not (len(metas) == len(cbs_or_luts) == len(ns) == len(stashes) == count):
         raise ValueError("one meta, codebook, size and stash per slot")

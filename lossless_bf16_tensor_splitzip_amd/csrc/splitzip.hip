@@ -47,11 +47,12 @@
 //   k_decode_check  after every decode: applies the escapes of streams not
 //                 marked ascending by scatter, in any order; with a status
 //                 word it validates every escape and re-applies it.
-//   k_decode_slot_stage / k_decode_slot_finish  in-place decode of payloads
-//                 that sit at the head of their own output buffers: the first
-//                 pass stashes the inputs of the tiles whose output overlaps
-//                 the payload and decodes the others, the second decodes the
-//                 stashed tiles.
+//   k_decode_slot_stage / k_decode_slot_level  in-place decode of payloads
+//                 that sit at the head of their own output buffers, in
+//                 passes: the first decodes the tiles past the payload and
+//                 stashes what later passes read after the slot head has been
+//                 overwritten; each later pass decodes the tiles whose output
+//                 no tile of that or a later pass still reads.
 
 #include <hip/hip_runtime.h>
 
@@ -1635,7 +1636,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_slot_level(DecArgs a) {
 // itself, so the barrier needs no cache flush: it only has to order the held
 // tiles' stores after every load of the first phase.  Overlapping tiles
 // beyond the registers' reach (more than kHold * G of them), and a partial
-// last one, go through the stash as in the two-launch form.  A group of
+// last one, go through the stash as in the multi-pass form.  A group of
 // slots takes one barrier per slot, the stores of one slot overlapping the
 // loads of the next.
 //
@@ -1650,8 +1651,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_slot_level(DecArgs a) {
 // whole and no barrier gives up.)  On an abort every
 // workgroup stashes its held tiles' inputs (and its share of the escape
 // sections) and leaves the slot to k_decode_slot_defer, launched after this
-// kernel, which decodes the stashed tiles as the two-launch form's second
-// kernel does.  A stream not marked ascending is always left to it (its
+// kernel, which decodes the stashed tiles as the multi-pass form's last
+// pass does.  A stream not marked ascending is always left to it (its
 // escapes are applied by index once every tile is decoded).  Neither outcome
 // depends on which workgroups were resident.
 constexpr int kHold = 3;                   // held tiles per workgroup and tensor
@@ -2329,7 +2330,7 @@ __global__ __launch_bounds__(kDecThreads, 5) void k_decode_slot_hold(DecArgs a) 
 // The slots k_decode_slot_hold left: those whose barrier aborted and those
 // with an unmarked escape stream.  Their tiles below t_split are decoded
 // from the stash (the inputs and escape sections the first kernel put
-// there) as the two-launch form's second kernel does; an unmarked stream's
+// there) as the multi-pass form's last pass does; an unmarked stream's
 // escapes are then applied at their indices by the last workgroup to finish
 // the tensor.  The last workgroup of the grid puts the barrier block back.
 __global__ __launch_bounds__(kDecThreads) void k_decode_slot_defer(DecArgs a) {
@@ -2897,10 +2898,11 @@ int launch_decode_slot(const splitzip_slot_item *items, uint32_t count, int32_t 
     a.tile_start[count] = tiles;
     if (tiles == 0) return SPLITZIP_OK;
     // The resident form (k_decode_slot_hold, then k_decode_slot_defer for
-    // what it left) in an ordinary launch, or the two-launch form
-    // (k_decode_slot_stage, k_decode_slot_finish).  The environment variable
-    // SPLITZIP_SLOT_LAUNCH selects a form for every call: "one" (resident),
-    // "coop" (resident, the first kernel launched cooperatively) or "two";
+    // what it left) in an ordinary launch, or the multi-pass form
+    // (k_decode_slot_stage, then k_decode_slot_level once per later pass).
+    // The environment variable SPLITZIP_SLOT_LAUNCH selects a form for every
+    // call: "one" (resident), "coop" (resident, the first kernel launched
+    // cooperatively) or "two" (multi-pass);
     // SPLITZIP_SLOT_WAIT_US sets the resident form's bounded barrier wait
     // (default kHoldWaitUs; 0 makes nearly every barrier give up, which
     // exercises the path taken when the grid is not resident).

@@ -94,7 +94,7 @@ def test_two_streams_own_workspaces():
 
 @pytest.mark.parametrize("resident", [False, True])
 def test_graph_replays_slot_decode(resident):
-    """A group of two in-place decodes captured in a graph (two-launch or
+    """A group of two in-place decodes captured in a graph (multi-pass or
     resident form: the resident barrier's counters are put back by each
     launch, so every replay starts clean), replayed six times over three
     different payloads copied into the slot heads between the replays."""

@@ -226,3 +226,31 @@ def test_schedule_argument_errors():
     assert _abi.splitzip_slot_schedule(100, 9) is None
     assert _abi.splitzip_slot_schedule((1 << 36) + 1, 4) is None
     assert _abi.splitzip_slot_schedule(0, 4)[1] == 0
+
+
+@pytest.mark.parametrize("mistake", ["lo3+1", "lo3-1", "hi3+1", "hi3-1", "loK+1", "hiK-1",
+                                     "last pass reads sm from the slot"])
+def test_checker_catches_planted_schedule_mistakes(mistake, monkeypatch):
+    """The byte-level check fails for a schedule with one range bound moved
+    by a tile, or with the last pass's sm bytes left in the slot."""
+    n = 1 << 22
+    comp = _abi.splitzip_payload_size(n, 4000)
+    orig = _abi.splitzip_slot_schedule
+    if mistake.startswith(("lo", "hi")):
+        def planted(n_, passes):
+            used, t_min, lo, hi = orig(n_, passes)
+            arr = lo if mistake.startswith("lo") else hi
+            k = used if mistake[2] == "K" else 3
+            arr[k] += 1 if mistake.endswith("+1") else -1
+            return used, t_min, lo, hi
+        monkeypatch.setattr(_abi, "splitzip_slot_schedule", planted)
+    else:
+        orig_assign = assignment
+
+        def planted_assignment(n_, comp_, passes):
+            used, t_min, p, pk_st, sm_st = orig_assign(n_, comp_, passes)
+            sm_st = sm_st & ~((p == used) & (np.arange(len(p)) < t_min))
+            return used, t_min, p, pk_st, sm_st
+        monkeypatch.setitem(globals(), "assignment", planted_assignment)
+    with pytest.raises(AssertionError):
+        simulate(n, comp, 4)
