@@ -93,14 +93,14 @@ def run_slot(opay, om, dec_lut, validate=True, extra=0, stash_extra=0, ascending
     return slot, host_bits(out), (int(st.item()) if validate else 0)
 
 
-def check_slot(x_cpu, name, extra=0):
+def check_slot(x_cpu, name, extra=0, stash_extra=0):
     xs, ocb, opay, om = oracle_case(x_cpu)
     n = om.n
     _say("slot case %s n=%d e=%d comp=%d" % (name, n, om.n_esc, om.comp_bytes))
     # the oracle's escapes are ascending: decoded with and without the flag
     # that says so (per-tile patch, or the order-independent pass)
     for validate, ascending in ((False, True), (False, False), (True, True)):
-        slot, out, st = run_slot(opay, om, ocb.dec_lut, validate, extra, ascending=ascending)
+        slot, out, st = run_slot(opay, om, ocb.dec_lut, validate, extra, stash_extra, ascending=ascending)
         assert st == 0
         assert np.array_equal(out, xs), name
         # bytes past the decoded tensor and past the payload are left alone
@@ -134,6 +134,16 @@ def test_slot_split_positions(n, esc_every, form):
     b[k] = ((k & 1) << 15) | ((150 + (k // esc_every) % 40) << 7) | (k & 0x7F)
     x = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
     check_slot(x, "esc every %d" % esc_every, extra=12345)
+
+
+@pytest.mark.parametrize("n", [3 * TILE + 77, 40 * TILE, 1_000_003])
+def test_slot_buffers_larger_than_the_payload(n, form):
+    """Slot and stash much longer than the payload: the last pass of the
+    multi-pass form then runs workgroups for tiles past the payload's end
+    that find nothing to do (their count is bounded by the buffers, not by
+    the payload the kernels read)."""
+    check_slot(W.gaussian_weight(n, seed=400 + n % 83), "large buffers",
+               extra=7 * 2 * TILE + 5, stash_extra=5 * 2 * TILE + 13)
 
 
 def test_slot_matches_gpu_encode_and_plain_decode(form):
