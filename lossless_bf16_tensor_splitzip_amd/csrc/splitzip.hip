@@ -965,7 +965,9 @@ __device__ void rederive_tile(const EncItem &I, const Layout &L, bool fits, cons
 // chunk-local position and raw exponent: copied from the staging area, or
 // for a tile above the staging cap derived from the input again.  The
 // tensor's first tail workgroup writes the padding and the metadata.
-__global__ __launch_bounds__(kTailThreads) void k_encode_tail(EncArgs a) {
+// (at most 128 VGPRs: four waves per SIMD, so a single tensor's 1,024
+// workgroups are all resident at once)
+__global__ __launch_bounds__(kTailThreads, 4) void k_encode_tail(EncArgs a) {
     __shared__ uint64_t red[2][kTailThreads / 64];
     __shared__ uint32_t waves[kTailThreads / 64];
     __shared__ uint32_t scan[kTailMaxTiles + 1];
@@ -986,9 +988,24 @@ __global__ __launch_bounds__(kTailThreads) void k_encode_tail(EncArgs a) {
     const uint64_t t0 = (uint64_t)blk * tt;
     const uint64_t t1 = t0 + tt < ntiles ? t0 + tt : ntiles;
 
-    // this block's own tile counts (issued first, used after the sweep)
+    // this block's own tile counts (issued first, used after the sweep), and
+    // with them the first S = kTailThreads / tt staged escapes of each of its
+    // tiles, one per thread: a sparse tensor's tiles stage at most that many,
+    // so the escapes are at hand when the ranks are known (no second round
+    // trip); entries past a tile's count are read but not used
     const uint64_t mine_t = t0 + tid;
     const uint32_t mine_c = ((uint32_t)tid < tt && mine_t < t1) ? counts[mine_t] : 0u;
+    const uint32_t spt = kTailThreads / tt;   // tt: a power of two up to kTailMaxTiles
+    const uint32_t sj = (uint32_t)tid / spt, si = (uint32_t)tid % spt;
+    const uint32_t spec = t0 + sj < t1 ? a.stage[(tfirst + t0 + sj) * kStageCap + si] : 0u;
+    // the codebook's coverage for the metadata, loaded now (by the whole
+    // workgroup that writes the metadata: a uniform load, kept in scalar
+    // registers)
+    uint64_t cb_cov = 0, cb_tot = 0;
+    if (blk == 0) {
+        cb_cov = I.cb->covered;
+        cb_tot = I.cb->total;
+    }
     uint64_t before = 0, all = 0;
     if (a.sup_sum) {
         // superblocks before this one and in total, then the blocks of this
@@ -1012,7 +1029,8 @@ __global__ __launch_bounds__(kTailThreads) void k_encode_tail(EncArgs a) {
     if ((uint32_t)tid < tt) scan[tid + 1] = incl;
     if (tid == 0) scan[0] = 0;
     // a tile above the staging cap has to be derived from the input again
-    const bool rederive = __syncthreads_or(mine_c > kStageCap) != 0;
+    const bool beyond = __syncthreads_or(mine_c > spt) != 0;   // some tile stages more than S
+    const bool rederive = beyond && __syncthreads_or(mine_c > kStageCap) != 0;
     uint64_t P = 0, e = 0;
 #pragma unroll
     for (int w = 0; w < kTailThreads / 64; ++w) {
@@ -1024,7 +1042,11 @@ __global__ __launch_bounds__(kTailThreads) void k_encode_tail(EncArgs a) {
 
     const uint32_t nt = (uint32_t)(t1 - t0);
     const uint32_t total = scan[nt];
-    if (!rederive && total <= 8 * kTailThreads) {
+    if (!beyond) {
+        // every tile's escapes came with the counts
+        if (sj < nt && si < scan[sj + 1] - scan[sj])
+            place_escape(I, L, fits, (t0 + sj) * kEncTile, spec, P + scan[sj] + si);
+    } else if (!rederive && total <= 8 * kTailThreads) {
         // few escapes: one pass over all of them, the tile of escape k found
         // in the block's scan, 8 staged loads in flight
         uint32_t w8[8], j8[8];
@@ -1106,8 +1128,8 @@ __global__ __launch_bounds__(kTailThreads) void k_encode_tail(EncArgs a) {
         m->offsets[2] = L.off_cid;
         m->offsets[3] = L.off_lpos;
         m->offsets[4] = L.off_ev;
-        m->covered = I.cb->covered;
-        m->total = I.cb->total;
+        m->covered = cb_cov;
+        m->total = cb_tot;
         m->status = fits ? SPLITZIP_OK : SPLITZIP_ERR_CAPACITY;
         m->flags = SPLITZIP_META_ASCENDING;   // ranks follow element order
     }
