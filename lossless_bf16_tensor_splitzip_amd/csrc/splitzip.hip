@@ -1264,42 +1264,6 @@ __device__ inline uint64_t lower_bound_wave(const int32_t *cid, uint64_t lo, uin
     return lo + __popcll(__ballot(v < key));
 }
 
-// The escapes [r0, r1) of chunk ids in [c0, c1) of a sorted stream of e, by
-// one wave.  Both ends are first looked for in the 64-entry windows at their
-// interpolated guesses, loaded together, so the common case (each end inside
-// its window) costs one memory round trip instead of two searches in turn;
-// an end its window does not settle goes through lower_bound_wave.
-__device__ inline uint64_t window_at(uint64_t guess, uint64_t e) {
-    const uint64_t w = guess > 32 ? guess - 32 : 0;
-    return w > e - 64 ? e - 64 : w;   // e > 64
-}
-// lower_bound of key from the window [w, w + 64) of a stream of e: true when
-// the window decides it.
-__device__ inline bool window_settles(int64_t v, int64_t key, uint64_t w, uint64_t e, uint64_t &r) {
-    const uint64_t below = __ballot(v < key);
-    const uint32_t k = __popcll(below);
-    r = w + k;
-    const bool left_ok = w == 0 || (below & 1ull);      // nothing before the window is >= key
-    const bool right_ok = k < 64 || w + 64 == e;         // the first >= key is in it, or none is
-    return left_ok && right_ok;
-}
-__device__ inline void range_wave(const int32_t *cid, uint64_t e, int64_t c0, int64_t c1, uint64_t g0,
-                                  uint64_t g1, int lane, uint64_t &r0, uint64_t &r1) {
-    if (e <= 64) {
-        const int64_t v = (uint64_t)lane < e ? (int64_t)cid[lane] : INT64_MAX;
-        r0 = __popcll(__ballot(v < c0));
-        r1 = __popcll(__ballot(v < c1));
-        return;
-    }
-    const uint64_t w0 = window_at(g0, e), w1 = window_at(g1, e);
-    const int64_t v0 = cid[w0 + lane];
-    const int64_t v1 = cid[w1 + lane];
-    const bool ok0 = window_settles(v0, c0, w0, e, r0);
-    const bool ok1 = window_settles(v1, c1, w1, e, r1);
-    if (!ok0) r0 = lower_bound_wave(cid, 0, e, c0, g0, lane);
-    if (!ok1) r1 = lower_bound_wave(cid, r0, e, c1, g1 > r0 ? g1 : r0, lane);
-}
-
 // Order-independent escape pass (page 1, decode_torch applies the escapes
 // by index, in any order) for a tensor whose stream is not marked ascending:
 // every workgroup of the tensor releases its dense stores and arrives; the
@@ -1415,9 +1379,10 @@ __device__ __forceinline__ void decode_body(const DecItem &I, const splitzip_met
         if (c1 > nchunks) c1 = nchunks;
         // interpolated guesses (hints only: the search is exact for any guess)
         const double per_chunk = (double)e / (double)nchunks;
-        uint64_t r0, r1;
-        range_wave(cid, e, (int64_t)c0, (int64_t)c1, (uint64_t)(per_chunk * (double)c0),
-                   (uint64_t)(per_chunk * (double)c1), lane, r0, r1);
+        const uint64_t r0 =
+            lower_bound_wave(cid, 0, e, (int64_t)c0, (uint64_t)(per_chunk * (double)c0), lane);
+        const uint64_t r1 = lower_bound_wave(cid, r0, e, (int64_t)c1,
+                                             r0 + (uint64_t)(per_chunk * (double)(c1 - c0)), lane);
         if (lane == 0) {
             range[0] = r0;
             range[1] = r1;
@@ -2046,8 +2011,8 @@ __device__ inline void tile_escape_range(const int32_t *cid, uint64_t e, uint64_
     ++nchunks;
     if (c1 > nchunks) c1 = nchunks;
     const double per_chunk = (double)e / (double)nchunks;
-    range_wave(cid, e, (int64_t)c0, (int64_t)c1, (uint64_t)(per_chunk * (double)c0),
-               (uint64_t)(per_chunk * (double)c1), lane, r0, r1);
+    r0 = lower_bound_wave(cid, 0, e, (int64_t)c0, (uint64_t)(per_chunk * (double)c0), lane);
+    r1 = lower_bound_wave(cid, r0, e, (int64_t)c1, r0 + (uint64_t)(per_chunk * (double)(c1 - c0)), lane);
 }
 
 // Applies the escapes of ranks [r0, r1) that fall in the LDS tile at element base.
