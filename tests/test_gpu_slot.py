@@ -146,6 +146,28 @@ def test_slot_buffers_larger_than_the_payload(n, form):
                extra=7 * 2 * TILE + 5, stash_extra=5 * 2 * TILE + 13)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_slot_random_sizes_densities_and_passes(seed, monkeypatch):
+    """Seeded random sizes (1 .. 3M elements), escape densities (none to
+    about half the elements) and pass counts of the multi-pass form: every
+    in-place decode equals the input bit for bit, and the slot's bytes past
+    the output are left alone."""
+    rnd = np.random.default_rng(5000 + seed)
+    n = int(rnd.integers(1, 3_000_000))
+    passes = int(rnd.integers(2, 9))
+    every = int(rnd.choice([0, 997, 61, 7, 2]))
+    monkeypatch.setenv("SPLITZIP_SLOT_PASSES", str(passes))
+    monkeypatch.delenv("SPLITZIP_SLOT_LAUNCH", raising=False)
+    b = host_bits(W.gaussian_weight(n, seed=600 + seed)).copy()
+    if every:
+        k = np.arange(0, n, every)
+        b[k] = ((k & 1) << 15) | ((150 + (k // every) % 40) << 7) | (k & 0x7F)
+    x = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+    _say("random slot case seed=%d n=%d passes=%d every=%d" % (seed, n, passes, every))
+    check_slot(x, "random", extra=int(rnd.integers(0, 3 * 2 * TILE)),
+               stash_extra=int(rnd.integers(0, 3 * 2 * TILE)))
+
+
 def test_slot_matches_gpu_encode_and_plain_decode(form):
     """GPU encode -> payload copied to the slot head -> in-place decode, equal
     to the out-of-place decode, on one 33,554,432-element KV-cache tensor."""
