@@ -76,6 +76,38 @@ int main(void) {
     EXPECT(splitzip_decode_batch(NULL, 2, NULL, NULL) == SPLITZIP_ERR_INVALID);
     splitzip_slot_item slots[1] = {{p, 100, m, p, 100, (uint8_t *)0x8000, 1 << 20}};
     EXPECT(splitzip_decode_slot_batch(slots, 1, NULL, NULL) == SPLITZIP_ERR_INVALID);
+    /* in-place decode schedule: argument errors, then for many sizes and
+       pass counts the ranges the header promises (lo[2] = 0, hi[2] = t_min,
+       nested ranges, t_min = the first tile whose output starts at or past
+       the dense sections' end) */
+    {
+        uint64_t t_min = 0, lo[9], hi[9];
+        EXPECT(splitzip_slot_schedule(100, 1, &t_min, lo, hi) == 0);
+        EXPECT(splitzip_slot_schedule(100, 9, &t_min, lo, hi) == 0);
+        EXPECT(splitzip_slot_schedule(SPLITZIP_MAX_N + 1, 4, &t_min, lo, hi) == 0);
+        EXPECT(splitzip_slot_schedule(100, 4, NULL, lo, hi) == 0);
+        EXPECT(splitzip_slot_schedule(100, 4, &t_min, NULL, hi) == 0);
+        for (uint64_t n = 1; n <= SPLITZIP_MAX_N; n = n * 5 / 2 + 3) {
+            for (uint32_t passes = 2; passes <= 8; ++passes) {
+                for (int k = 0; k < 9; ++k) lo[k] = hi[k] = 0xdead;
+                const uint32_t used = splitzip_slot_schedule(n, passes, &t_min, lo, hi);
+                EXPECT(used == 2 || used == passes);
+                const uint64_t tiles = (n + 8191) / 8192;
+                const uint64_t dense = splitzip_payload_size(n, 0);
+                /* dense sections end at off_cid, the first 4-aligned offset past P' + n */
+                const uint64_t P = (n + 1) / 2, off_cid = ((((P + 3) & ~3ull) + n) + 3) & ~3ull;
+                uint64_t want = (off_cid + 16383) / 16384;
+                if (want > tiles) want = tiles;
+                EXPECT(dense == off_cid && t_min == want);
+                EXPECT(lo[0] == 0 && hi[0] == 0 && lo[1] == 0 && hi[1] == 0);
+                EXPECT(lo[2] == 0 && hi[2] == t_min);
+                for (uint32_t k = 2; k < used; ++k)
+                    EXPECT(lo[k] <= lo[k + 1] && lo[k + 1] <= hi[k + 1] && hi[k + 1] <= hi[k]);
+                if (used == passes && passes > 2) EXPECT(lo[passes] < hi[passes]);   /* last pass holds a tile */
+                for (uint32_t k = used + 1; k <= passes; ++k) EXPECT(lo[k] == 0 && hi[k] == 0);
+            }
+        }
+    }
     printf("%d failures\n", failures);
     return failures ? 1 : 0;
 }
