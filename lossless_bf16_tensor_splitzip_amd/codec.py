@@ -271,6 +271,25 @@ class Batch:
         self.count = len(self.xs)
         self.device = device
 
+    def fit_payloads(self, slack: int = 0):
+        """Size every payload buffer for the payload its tensor has under the
+        codebook the last calibrate wrote: n_esc = total - covered, exact for
+        a codebook calibrated on that tensor (every exponent outside the
+        top 16 escapes; page "splitzip_codec.py -- SplitZip codec adapter
+        for diffusers-dynamic-offloader", calibrate_codebook), instead of the
+        all-escape bound (8.5 bytes per element) the buffers start with.  A
+        codebook whose total is not this tensor's length keeps the bound.
+        Reads the codebooks back, so it synchronises with the device; an
+        encode that would not fit still reports SPLITZIP_ERR_CAPACITY in its
+        metadata."""
+        for k, cb in enumerate(self.cbs):
+            c = read_codebook(cb)
+            n = self.ns[k]
+            e = c.total - c.covered if c.total == n and c.covered <= n else n
+            cap = max(payload_size(n, e) + slack, 16)
+            self.payloads[k] = torch.empty(cap, dtype=torch.uint8, device=self.device)
+            self.items[k].payload, self.items[k].capacity = self.payloads[k].data_ptr(), cap
+
     def calibrate(self, ws: Workspace, stream=None):
         _abi._check("splitzip_calibrate_batch",
                     _abi.splitzip_calibrate_batch(self.items, self.count, ws.ptr(), ws.nbytes,

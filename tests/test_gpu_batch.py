@@ -207,3 +207,32 @@ def test_batch_decode_streams_not_marked_ascending():
         torch.cuda.synchronize()
         for k, x in enumerate(xs):
             assert torch.equal(b.outs[k].view(torch.int16), x.view(torch.int16)), (rep, k)
+
+
+def test_fit_payloads_sizes_each_buffer_exactly():
+    """Batch.fit_payloads after a calibrate: every payload buffer is exactly
+    its payload's length (n_esc = total - covered under the tensor's own
+    codebook), the encode fits with status 0 and the round trip is bit for
+    bit; a codebook calibrated on a tensor of another length keeps the
+    all-escape bound."""
+    xs = [W.gaussian_weight(1_000_003, seed=71, device=DEV),
+          W.log_uniform_stress(77_777, seed=72, device=DEV),
+          W.kv_cache_tensor(3, 1, device=DEV).reshape(-1)[: 3 * 8192 + 5].contiguous()]
+    b = S.Batch(xs, capacities=[16] * len(xs))
+    ws = S.Workspace(max(b.ns), device=DEV, batch_ns=b.ns)
+    b.calibrate(ws)
+    b.fit_payloads()
+    b.encode(ws)
+    b.decode()
+    torch.cuda.synchronize()
+    for k, x in enumerate(xs):
+        m = S.read_meta(b.metas[k])
+        c = S.read_codebook(b.cbs[k])
+        assert m.status == 0
+        assert m.n_esc == c.total - c.covered
+        assert b.payloads[k].numel() == max(m.comp_bytes, 16)
+        assert torch.equal(b.outs[k].view(torch.int16), x.view(torch.int16))
+    # tensor 1 given tensor 0's codebook (another length): the bound stays
+    b.cbs[1].copy_(b.cbs[0])
+    b.fit_payloads()
+    assert b.payloads[1].numel() == S.payload_size(b.ns[1], b.ns[1])
