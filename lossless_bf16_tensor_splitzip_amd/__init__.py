@@ -13,8 +13,8 @@ diffusers-dynamic-offloader" and page "SplitZip in DDO -- VMM routes".
 from ._abi import CHUNK, Codebook, Meta, SplitZipError, lib  # noqa: F401
 from . import persist  # noqa: F401
 from .codec import (Batch, Workspace, calibrate, decode, decode_slot, decode_slots,  # noqa: F401
-                    encode, payload_size, read_codebook, read_meta)
+                    encode, payload_for, payload_size, read_codebook, read_meta)
 
 __all__ = ["CHUNK", "Batch", "Codebook", "Meta", "SplitZipError", "Workspace", "calibrate", "encode",
-           "decode", "decode_slot", "decode_slots", "payload_size", "read_codebook", "read_meta",
+           "decode", "decode_slot", "decode_slots", "payload_for", "payload_size", "read_codebook", "read_meta",
            "lib", "persist"]

@@ -77,12 +77,24 @@ def calibrate(x: torch.Tensor, ws: Workspace, cb: torch.Tensor | None = None,
     return cb
 
 
+def payload_for(cb: torch.Tensor, n: int) -> torch.Tensor:
+    """A payload buffer for an n-element tensor encoded with ``cb``: exactly
+    its payload's length when ``cb`` was calibrated on that tensor (n_esc =
+    total - covered), else the all-escape bound.  Reads the codebook back,
+    so it synchronises with the device."""
+    c = read_codebook(cb)
+    e = c.total - c.covered if c.total == n and c.covered <= n else n
+    return torch.empty(max(payload_size(n, e), 16), dtype=torch.uint8, device=cb.device)
+
+
 def encode(x: torch.Tensor, cb: torch.Tensor, ws: Workspace, payload: torch.Tensor | None = None,
            meta: torch.Tensor | None = None, stream=None, chunk_size: int = CHUNK):
-    """Encode into ``payload`` (allocated for the worst case when None).
-    Returns (payload, meta) as uint8 tensors; the payload occupies the first
-    meta.comp_bytes bytes.  ``payload`` may be pinned host memory: the kernels
-    then write it over the host link (an offload without a separate copy)."""
+    """Encode into ``payload`` (allocated for the all-escape bound, 8.5 bytes
+    per element, when None; ``payload_for`` gives one of the payload's own
+    length).  Returns (payload, meta) as uint8 tensors; the payload occupies
+    the first meta.comp_bytes bytes.  ``payload`` may be pinned host memory:
+    the kernels then write it over the host link (an offload without a
+    separate copy)."""
     xb = _bits(x)
     n = xb.numel()
     if payload is None:

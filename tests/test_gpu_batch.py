@@ -236,3 +236,18 @@ def test_fit_payloads_sizes_each_buffer_exactly():
     b.cbs[1].copy_(b.cbs[0])
     b.fit_payloads()
     assert b.payloads[1].numel() == S.payload_size(b.ns[1], b.ns[1])
+
+
+def test_payload_for_is_the_payload_length():
+    """payload_for after a calibrate on the same tensor: the encode fits a
+    buffer of exactly comp_bytes and decodes bit for bit."""
+    x = W.kv_cache_tensor(5, 0, device=DEV).reshape(-1)[: 40 * 8192 + 3].contiguous()
+    ws = S.Workspace(x.numel(), device=DEV)
+    cb = S.calibrate(x, ws)
+    buf = S.payload_for(cb, x.numel())
+    pay, meta = S.encode(x, cb, ws, payload=buf)
+    m = S.read_meta(meta)
+    assert m.status == 0 and buf.numel() == max(m.comp_bytes, 16)
+    out = S.decode(pay, meta, cb, x.numel())
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), x.view(torch.int16))
