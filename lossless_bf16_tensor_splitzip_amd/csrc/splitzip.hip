@@ -314,6 +314,7 @@ __global__ __launch_bounds__(kCalThreads, 8) void k_calibrate(CalArgs a) {
     __shared__ uint32_t hist[256 * 64];   // [exponent][lane]
     __shared__ uint32_t part[4 * 256];
     __shared__ __attribute__((aligned(16))) uint64_t key[256];
+    __shared__ __attribute__((aligned(16))) uint64_t cand[64];
     __shared__ uint64_t wcov[4];
     __shared__ uint32_t wdist[4];
     __shared__ uint32_t proceed;
@@ -462,20 +463,47 @@ __global__ __launch_bounds__(kCalThreads, 8) void k_calibrate(CalArgs a) {
         key[tid] = c ? ((c << 8) | (uint64_t)(255 - tid)) : 0;
     }
     __syncthreads();
-    {   // rank = number of larger keys; 4 threads per exponent, 64 keys
-        // each, 16 keys loaded at a time
+    // Rank = number of larger keys, needed exactly only below 16.  First
+    // each key's rank inside its group of 64 (4 threads per key, 16 keys
+    // each): a key with 16 larger ones in its group has a rank of 16 or more,
+    // so the candidates are the nonzero keys that rank below 16 in their
+    // group (at most 64).  Every key larger than a key of global rank below
+    // 16 is a candidate, and every key that is not one has at least the 16
+    // candidates of its group above it, so a key's rank among the candidates
+    // is its rank when that is below 16, and 16 or more otherwise.
+    {
         const int bin = tid & 255, quarter = tid >> 8;
         const uint64_t own = key[bin];
-        const u64x2 *kv = reinterpret_cast<const u64x2 *>(key + quarter * 64);
+        const u64x2 *kv = reinterpret_cast<const u64x2 *>(key + (bin & ~63) + quarter * 16);
+        u64x2 kk[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kk[j] = kv[j];
         uint32_t r = 0;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            u64x2 kk[8];
+        for (int j = 0; j < 8; ++j) r += (kk[j].x > own ? 1u : 0u) + (kk[j].y > own ? 1u : 0u);
+        part[tid] = r;
+    }
+    __syncthreads();
+    if (tid < 256) {
+        const uint32_t group_rank = part[tid] + part[256 + tid] + part[512 + tid] + part[768 + tid];
+        const uint64_t own = key[tid];
+        const bool keep = own != 0 && group_rank < 16;
+        const uint64_t m = __ballot(keep);
+        uint64_t *slots = cand + (tid >> 6) * 16;
+        if (keep) slots[lanes_below(m)] = own;
+        if (lane < 16 && (uint32_t)lane >= (uint32_t)__popcll(m)) slots[lane] = 0;
+    }
+    __syncthreads();
+    {
+        const int bin = tid & 255, quarter = tid >> 8;
+        const uint64_t own = key[bin];
+        const u64x2 *kv = reinterpret_cast<const u64x2 *>(cand + quarter * 16);
+        u64x2 kk[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) kk[j] = kv[b * 8 + j];
+        for (int j = 0; j < 8; ++j) kk[j] = kv[j];
+        uint32_t r = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) r += (kk[j].x > own ? 1u : 0u) + (kk[j].y > own ? 1u : 0u);
-        }
+        for (int j = 0; j < 8; ++j) r += (kk[j].x > own ? 1u : 0u) + (kk[j].y > own ? 1u : 0u);
         part[tid] = r;
     }
     __syncthreads();
