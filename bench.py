@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--small-only", metavar="WORKLOAD", nargs="?", const="all",
                     help="instead of the benchmark, run the smaller single-tensor workloads only "
                          "(or the one named) and print them as one JSON line")
+    ap.add_argument("--sizes", action="store_true",
+                    help="instead of the benchmark, time single-tensor calls of N(0, 0.02) values "
+                         "at 2^16, 2^18, ..., 2^30 elements and print them as one JSON line")
     ap.add_argument("--probes", action="store_true",
                     help="instead of the benchmark, run the probes of the part's costs that the "
                          "design rests on (reference-stream library) and print them as one JSON line")
@@ -332,6 +335,51 @@ def slot_contention(S, dev):
         if old is not None:
             os.environ["SPLITZIP_SLOT_LAUNCH"] = old
     return res
+
+def single_call_sizes(S, W, dev, stream):
+    """Single-tensor calls by size: one N(0, 0.02) tensor of 2^k elements
+    (k = 16, 18, ..., 30), median event time of 10 calls per phase after 3
+    warm-up calls (calibrate, encode into a payload of the tensor's own
+    size, decode into one output buffer), round trip checked."""
+    import statistics
+
+    import torch
+
+    out = {}
+    ws = S.Workspace(1 << 30, device=dev)
+    for k in range(16, 31, 2):
+        n = 1 << k
+        x = W.gaussian_weight(n, seed=7, device=dev)
+        cb = S.calibrate(x, ws)
+        payload = S.payload_for(cb, n)
+        meta = S.codec.new_meta(dev)
+        dst = torch.empty(n, dtype=torch.bfloat16, device=dev)
+
+        def med(fn):
+            for _ in range(3):
+                fn()
+            ts = []
+            for _ in range(10):
+                torch.cuda._sleep(100_000)      # keep the GPU busy while the call is enqueued
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            return statistics.median(ts)
+
+        us = {"calibrate": med(lambda: S.calibrate(x, ws, cb=cb)),
+              "encode": med(lambda: S.encode(x, cb, ws, payload=payload, meta=meta)),
+              "decode": med(lambda: S.decode(payload, meta, cb, n, out=dst))}
+        if S.read_meta(meta).status != 0 or not torch.equal(dst.view(torch.int16),
+                                                            x.view(torch.int16)):
+            raise AssertionError("round trip failed at 2^%d elements" % k)
+        out["2^%d" % k] = {ph: {"us": round(v, 1), "raw_GBps": round(2 * n / v / 1e3, 1)}
+                          for ph, v in us.items()}
+        del x, payload, dst
+    return out
+
 
 def small_configs(S, W, dev, stream, host_inputs=None, only=None):
     """The smaller single-tensor workloads: one call per phase, median GPU
@@ -668,6 +716,9 @@ def main():
     sh = int(stream.cuda_stream)
     if args.probes:
         print(json.dumps({"probes": design_probes(S, dev), "device": torch.cuda.get_device_name(dev)}))
+        return
+    if args.sizes:
+        print(json.dumps({"single_call_sizes": single_call_sizes(S, W, dev, stream)}))
         return
     if args.small_only:
         only = None if args.small_only == "all" else args.small_only
